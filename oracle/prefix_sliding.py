@@ -1,0 +1,250 @@
+"""Float64 CPU oracle for Prefix Sliding attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library path may import or call this
+module: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it.  It shares no code with the HIP kernels.
+
+What it computes, and where each rule comes from (page titles as printed on
+the pages; no page is quoted):
+
+* Visibility.  Blog "Prefix Sliding 完全拆解" (pinghaoyang.com.cn), section
+  "核心机制：注意力掩码上的两个区间", definition of the allowed set A(i): a query
+  sees the prefix and the last W tokens up to itself; every other score is set
+  to -inf before the softmax.  The same rule is restated in the Polish notes
+  "Prefix Sliding. Myślenie może być długie, pamięć nie", section "Intuicja".
+  Readings (the pages are 1-indexed and loose at the edges):
+    - positions are 0-indexed absolute positions p, j of one sequence;
+    - the prefix is [0, L); the window is (p - W, p], i.e. W tokens counting
+      the query itself -- this is what makes "100-token prefix + 4096 window
+      holds at most 4196 tokens" (agihunt.info summary; ainews.surl.tw
+      article) come out exactly;
+    - attention is always causal (j <= p), also inside the prefix: during
+      warm-up the method behaves exactly like the unmodified model (same blog
+      section, warm-up paragraph);
+    - prefix and window are a set union: no key is counted twice.
+* Eviction and Continue PE.  Same blog, the mask section (hidden tokens'
+  K/V are not kept) and section "位置编码：Reset PE 还是 Continue PE？": every
+  token keeps its absolute position; cached keys are rotated once and reused.
+  Because a hidden key only ever contributes a -inf score, the method's result
+  is exactly plain masked softmax attention over the *full, un-evicted*
+  history, which is what this oracle evaluates.
+* Rotary embedding.  The pages name RoPE without fixing a variant.  Reading:
+  rotate-half pairing (i, i + D/2) with inverse frequencies theta^(-2i/D),
+  theta = 10000, evaluated exactly in float64 at the absolute position.
+* GQA.  Query head h uses KV head floor(h / (Hq/Hkv)) (the blog's memory
+  formula counts KV heads separately from query heads).
+* Prefill key set (truncated backprop, blog section
+  "超长 rollouts 的反向传播：截断回传"): keys are the prefix followed by a chunk
+  of consecutive positions starting at ``kv_start``; queries are the last T
+  keys; nothing before the chunk other than the prefix exists.
+* Tile plan (blog section "Kernel 实现：两层级过滤"): tiles with no visible pair
+  are skipped, tiles whose every pair is visible need no element mask, the
+  rest are partial.  The oracle decides this by enumerating every element.
+* Ring slot of position n (the pages only say hidden tokens are not kept):
+  n for n < L, else L + ((n - L) mod W).
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+against closed forms, reductions to torch's CPU attention with independently
+built masks, the pages' printed numbers (tests/golden/) and brute force.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+KIND_FULL = 1
+KIND_PARTIAL = 2
+
+
+# --------------------------------------------------------------------------
+# visibility (blog "Prefix Sliding 完全拆解", mask section: the set A(i))
+# --------------------------------------------------------------------------
+def visible(pq, pk, prefix_len: int, window: int):
+    """Element-wise: may a query at absolute position ``pq`` see the key at ``pk``?
+
+    Causal, plus (key in the pinned prefix [0, L) or key in the window (pq-W, pq]).
+    Works on scalars and broadcasting numpy arrays."""
+    pq = np.asarray(pq, dtype=np.int64)
+    pk = np.asarray(pk, dtype=np.int64)
+    return (pk <= pq) & ((pk < prefix_len) | (pk > pq - window))
+
+
+def visible_positions(p: int, prefix_len: int, window: int) -> np.ndarray:
+    """All history positions a decode query at ``p`` sees, found by testing
+    every j in [0, p]."""
+    j = np.arange(p + 1, dtype=np.int64)
+    return j[visible(p, j, prefix_len, window)]
+
+
+def visible_count(p: int, prefix_len: int, window: int) -> int:
+    """Number of keys a decode query at ``p`` sees (enumeration, not a formula)."""
+    return int(visible_positions(p, prefix_len, window).size)
+
+
+# --------------------------------------------------------------------------
+# ring slots (bounded cache of L + W entries per sequence)
+# --------------------------------------------------------------------------
+def slot_of(n: int, prefix_len: int, window: int) -> int:
+    """Ring slot that holds position ``n``: prefix positions sit in their own
+    slot, window positions cycle through the W slots after the prefix."""
+    if n < prefix_len:
+        return int(n)
+    return int(prefix_len + (n - prefix_len) % window)
+
+
+def simulate_ring(positions: Sequence[int], prefix_len: int, window: int, capacity: int) -> np.ndarray:
+    """Append ``positions`` in order into an empty ring; return, for every slot,
+    the position it holds last (-1 when never written)."""
+    ring = np.full(capacity, -1, dtype=np.int64)
+    for n in positions:
+        ring[slot_of(int(n), prefix_len, window)] = int(n)
+    return ring
+
+
+# --------------------------------------------------------------------------
+# rotary embedding at the absolute position (Continue PE)
+# --------------------------------------------------------------------------
+def rope(x: np.ndarray, pos, theta: float) -> np.ndarray:
+    """Rotate-half RoPE in float64.  ``x`` is [..., D]; ``pos`` broadcasts
+    against x.shape[:-1].  theta == 0 means "already rotated": identity."""
+    x = np.asarray(x, dtype=np.float64)
+    if not theta:
+        return x.copy()
+    d = x.shape[-1]
+    half = d // 2
+    inv_freq = float(theta) ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+def _masked_softmax_rows(scores: np.ndarray, mask: np.ndarray):
+    s = np.where(mask, scores, -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=-1, keepdims=True)
+    return e / z, (m + np.log(z))[..., 0]
+
+
+def decode_attention(q: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray, p: int,
+                     prefix_len: int, window: int, scale: float, theta: float) -> np.ndarray:
+    """One decode query at absolute position ``p`` over the full history.
+
+    q: raw query [Hq, D]; k_hist, v_hist: raw keys/values [>= p+1, Hkv, D] for
+    positions 0..p (hidden positions included; the mask removes them).
+    Returns [Hq, D] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    hq, d = q.shape
+    hkv = k_hist.shape[1]
+    g = hq // hkv
+    n = p + 1
+    pos = np.arange(n, dtype=np.int64)
+    qr = rope(q, p, theta)
+    kr = rope(np.asarray(k_hist[:n], dtype=np.float64), pos[:, None], theta)
+    v = np.asarray(v_hist[:n], dtype=np.float64)
+    mask = visible(p, pos, prefix_len, window)
+    out = np.empty((hq, d), dtype=np.float64)
+    for h in range(hq):
+        kv = h // g
+        s = scale * (kr[:, kv, :] @ qr[h])
+        w, _ = _masked_softmax_rows(s[None, :], mask[None, :])
+        out[h] = w[0] @ v[:, kv, :]
+    return out
+
+
+def decode_from_slots(q: np.ndarray, p: int, k_rot: np.ndarray, v: np.ndarray, scale: float,
+                      theta: float) -> np.ndarray:
+    """Attention of a query at ``p`` over an explicit set of cached keys that are
+    already rotated at their own positions (the ring's contents, in any
+    order).  No mask: the cache holds exactly the visible keys."""
+    q = np.asarray(q, dtype=np.float64)
+    hq, d = q.shape
+    hkv = k_rot.shape[1]
+    g = hq // hkv
+    qr = rope(q, p, theta)
+    out = np.empty((hq, d), dtype=np.float64)
+    for h in range(hq):
+        kv = h // g
+        s = scale * (np.asarray(k_rot[:, kv, :], dtype=np.float64) @ qr[h])
+        e = np.exp(s - s.max())
+        out[h] = (e @ np.asarray(v[:, kv, :], dtype=np.float64)) / e.sum()
+    return out
+
+
+def key_positions(nk: int, prefix_len: int, kv_start: int) -> np.ndarray:
+    """Absolute positions of a prefill key array: [prefix 0..L-1][chunk from kv_start]."""
+    k = np.arange(nk, dtype=np.int64)
+    return np.where(k < prefix_len, k, kv_start + (k - prefix_len))
+
+
+def prefill_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, prefix_len: int, window: int,
+                      kv_start: int, scale: float, theta: float, rows=None):
+    """Masked attention of a prefill chunk.
+
+    q: raw [T, Hq, D]; k, v: raw [Nk, Hkv, D] with key positions from
+    ``key_positions``; query t is key Nk - T + t.  ``rows`` optionally limits
+    the evaluation to some query indices.  Returns (out [R, Hq, D],
+    lse [R, Hq]) with lse the natural-log sum of exp of the scaled, masked
+    scores."""
+    q = np.asarray(q, dtype=np.float64)
+    t_all, hq, d = q.shape
+    nk, hkv, _ = k.shape
+    g = hq // hkv
+    posk = key_positions(nk, prefix_len, kv_start)
+    posq_all = posk[nk - t_all:]
+    rows = np.arange(t_all) if rows is None else np.asarray(rows, dtype=np.int64)
+    posq = posq_all[rows]
+    qr = rope(q[rows], posq[:, None], theta)
+    kr = rope(np.asarray(k, dtype=np.float64), posk[:, None], theta)
+    v = np.asarray(v, dtype=np.float64)
+    mask = visible(posq[:, None], posk[None, :], prefix_len, window)
+    out = np.empty((rows.size, hq, d), dtype=np.float64)
+    lse = np.empty((rows.size, hq), dtype=np.float64)
+    for h in range(hq):
+        kv = h // g
+        s = scale * (qr[:, h, :] @ kr[:, kv, :].T)
+        w, l = _masked_softmax_rows(s, mask)
+        out[:, h, :] = w @ v[:, kv, :]
+        lse[:, h] = l
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# prefill tile plan by element enumeration
+# --------------------------------------------------------------------------
+def tile_plan(t_q: int, nk: int, prefix_len: int, window: int, kv_start: int, bm: int, bn: int
+              ) -> List[Tuple[int, int, int]]:
+    """Every (q_tile, k_tile) of the BM x BN grid that holds at least one
+    visible in-range (query, key) pair, in (q_tile, k_tile) order, with kind
+    KIND_FULL when all BM*BN pairs exist and are visible, else KIND_PARTIAL."""
+    posk = key_positions(nk, prefix_len, kv_start)
+    posq = posk[nk - t_q:]
+    n_qt = -(-t_q // bm)
+    n_kt = -(-nk // bn)
+    plan = []
+    for qt in range(n_qt):
+        q0, q1 = qt * bm, min(t_q, (qt + 1) * bm)
+        vis = visible(posq[q0:q1, None], posk[None, :], prefix_len, window)  # [rows, nk]
+        for kt in range(n_kt):
+            k0, k1 = kt * bn, min(nk, (kt + 1) * bn)
+            cnt = int(vis[:, k0:k1].sum())
+            if cnt == 0:
+                continue
+            plan.append((qt, kt, KIND_FULL if cnt == bm * bn else KIND_PARTIAL))
+    return plan
+
+
+def visible_pairs(t_q: int, nk: int, prefix_len: int, window: int, kv_start: int) -> int:
+    """Total visible (query, key) pairs of a prefill, by enumeration."""
+    posk = key_positions(nk, prefix_len, kv_start)
+    posq = posk[nk - t_q:]
+    total = 0
+    for s in range(0, t_q, 1024):
+        total += int(visible(posq[s:s + 1024, None], posk[None, :], prefix_len, window).sum())
+    return total

@@ -1,0 +1,99 @@
+"""Plants plausible mistakes in the oracle (on the CPU, through monkeypatching)
+and checks that the pins catch each one."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.prefix_sliding as ops
+from tests import test_oracle_pins as pins
+
+PIN_CHECKS = [
+    lambda: pins.test_visible_count_closed_form(3, 2),
+    lambda: pins.test_visible_count_closed_form(16, 64),
+    lambda: pins.test_pages_max_resident_tokens(),
+    lambda: pins.test_prefill_reduces_to_reference_attention(40, 3, "full-prefix"),
+    lambda: pins.test_prefill_reduces_to_reference_attention(3, 6, "ps"),
+    lambda: pins.test_decode_reduces_to_reference_attention(4, 9),
+    lambda: pins.test_decode_with_rope_matches_reference_on_complex_rotation(),
+    lambda: pins.test_gqa_head_map_is_consecutive(),
+    lambda: pins.test_rope_two_dims_is_plane_rotation(),
+    lambda: pins.test_rope_frequencies_and_pairing(),
+    lambda: pins.test_tile_plan_hand_worked_cases(),
+    lambda: pins.test_zero_query_gives_mean_of_visible_values(4, 6),
+]
+
+
+def _window_off_by_one(pq, pk, L, W):
+    pq, pk = np.asarray(pq), np.asarray(pk)
+    return (pk <= pq) & ((pk < L) | (pk >= pq - W))
+
+
+def _prefix_not_causal(pq, pk, L, W):
+    pq, pk = np.asarray(pq), np.asarray(pk)
+    return (pk < L) | ((pk <= pq) & (pk > pq - W))
+
+
+def _prefix_inclusive(pq, pk, L, W):
+    pq, pk = np.asarray(pq), np.asarray(pk)
+    return (pk <= pq) & ((pk <= L) | (pk > pq - W))
+
+
+def _rope_sign_flip(x, pos, theta):
+    x = np.asarray(x, dtype=np.float64)
+    if not theta:
+        return x.copy()
+    d = x.shape[-1]
+    h = d // 2
+    f = float(theta) ** (-2.0 * np.arange(h) / d)
+    a = np.asarray(pos, dtype=np.float64)[..., None] * f
+    c, s = np.cos(a), np.sin(a)
+    return np.concatenate([x[..., :h] * c + x[..., h:] * s, x[..., h:] * c - x[..., :h] * s], axis=-1)
+
+
+def _rope_wrong_freq(x, pos, theta):
+    x = np.asarray(x, dtype=np.float64)
+    if not theta:
+        return x.copy()
+    d = x.shape[-1]
+    h = d // 2
+    f = float(theta) ** (-1.0 * np.arange(h) / d)
+    a = np.asarray(pos, dtype=np.float64)[..., None] * f
+    c, s = np.cos(a), np.sin(a)
+    return np.concatenate([x[..., :h] * c - x[..., h:] * s, x[..., h:] * c + x[..., :h] * s], axis=-1)
+
+
+def _decode_interleaved_gqa(q, k_hist, v_hist, p, L, W, scale, theta):
+    # maps query head h to KV head h % Hkv instead of h // G
+    hkv = k_hist.shape[1]
+    out = np.empty_like(np.asarray(q, dtype=np.float64))
+    for h in range(q.shape[0]):
+        kk = k_hist[:, [h % hkv], :]
+        vv = v_hist[:, [h % hkv], :]
+        out[h] = ORIG_DECODE(q[[h]], kk, vv, p, L, W, scale, theta)[0]
+    return out
+
+
+ORIG_DECODE = ops.decode_attention
+
+MUTANTS = {
+    "window-off-by-one": ("visible", _window_off_by_one),
+    "prefix-not-causal": ("visible", _prefix_not_causal),
+    "prefix-inclusive": ("visible", _prefix_inclusive),
+    "rope-sign-flip": ("rope", _rope_sign_flip),
+    "rope-wrong-frequency": ("rope", _rope_wrong_freq),
+    "gqa-interleaved": ("decode_attention", _decode_interleaved_gqa),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(ops, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    caught = 0
+    for check in PIN_CHECKS:
+        try:
+            check()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin caught mutant {name}"

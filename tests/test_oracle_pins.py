@@ -1,0 +1,323 @@
+"""Pins for the float64 oracle: each test checks it against something other than
+itself -- numbers the pages print, closed forms, torch's CPU attention with a
+mask built independently, the textbook definitions of a rotation, and hand-worked
+tile plans.  The cases are picked so that a plausible slip in the oracle (an
+off-by-one window edge, a non-causal prefix, a swapped GQA map, a sign flip in
+the rotation, a transposed operand) fails at least one of them."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- visible set
+@pytest.mark.parametrize("L,W", [(0, 1), (0, 5), (1, 1), (3, 2), (16, 64), (100, 7), (7, 100)])
+def test_visible_count_closed_form(L, W):
+    # warm-up: all n = p+1 tokens; afterwards exactly L + W (blog mask section: L_total = L_prefix + W)
+    for p in list(range(0, 3 * (L + W) + 5)) + [10 * (L + W) + 3]:
+        assert oracle.visible_count(p, L, W) == min(p + 1, L + W), (p, L, W)
+
+
+def test_pages_max_resident_tokens():
+    g = _golden("pages_numbers.json")["max_resident_tokens"]
+    for p in (4195, 4196, 10_000, 100_000, 262_143):
+        assert oracle.visible_count(p, g["prefix_len"], g["window"]) == g["value"]
+    # and the cap is reached exactly when the sequence has L + W tokens
+    assert oracle.visible_count(g["value"] - 2, g["prefix_len"], g["window"]) == g["value"] - 1
+
+
+def test_visible_set_closed_form_membership():
+    # prefix [0, min(L, p+1)) union window (max(p-W, L-1), p]
+    for L, W, p in itertools.product((0, 1, 4, 9), (1, 2, 3, 8), range(0, 40)):
+        want = set(range(min(L, p + 1))) | set(range(max(p - W, L - 1) + 1, p + 1))
+        assert set(oracle.visible_positions(p, L, W).tolist()) == want
+
+
+# ---------------------------------------------------------------- ring / slots
+@pytest.mark.parametrize("L,W", [(0, 1), (0, 4), (3, 1), (16, 64), (5, 7)])
+def test_slot_map_bijection_and_eviction(L, W):
+    cap = L + W
+    for p in range(0, 4 * cap + 3):
+        ring = oracle.simulate_ring(range(p + 1), L, W, cap)
+        held = set(int(x) for x in ring if x >= 0)
+        assert held == set(oracle.visible_positions(p, L, W).tolist())
+        if p >= cap - 1:
+            slots = sorted(oracle.slot_of(j, L, W) for j in oracle.visible_positions(p, L, W))
+            assert slots == list(range(cap))
+        if p - W >= L:
+            assert oracle.slot_of(p, L, W) == oracle.slot_of(p - W, L, W)
+
+
+def test_ring_permutation_invariance():
+    rs = np.random.default_rng(3)
+    L, W, p, hq, hkv, d = 5, 11, 57, 4, 2, 8
+    k = rs.standard_normal((p + 1, hkv, d))
+    v = rs.standard_normal((p + 1, hkv, d))
+    q = rs.standard_normal((hq, d))
+    full = oracle.decode_attention(q, k, v, p, L, W, 0.3, 10000.0)
+    ring = oracle.simulate_ring(range(p + 1), L, W, L + W)
+    pos = ring[ring >= 0]
+    k_rot = oracle.rope(k[pos], pos[:, None], 10000.0)
+    for _ in range(5):
+        perm = rs.permutation(pos.size)
+        got = oracle.decode_from_slots(q, p, k_rot[perm], v[pos][perm], 0.3, 10000.0)
+        np.testing.assert_allclose(got, full, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- reductions to torch's attention
+def _sdpa(q, k, v, mask, scale):
+    """torch CPU attention in float64; q [T,Hq,D], k/v [N,Hkv,D] with KV heads
+    expanded by repeat_interleave (consecutive query heads share a KV head)."""
+    hq, hkv = q.shape[1], k.shape[1]
+    kk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+    vv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+    qq = torch.from_numpy(q).permute(1, 0, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=torch.from_numpy(mask),
+                                                         scale=scale)
+    return o.permute(1, 0, 2).numpy()
+
+
+def _band_mask(n, L, W):
+    """Causal band with W keys (self included) plus pinned columns [0, L), built
+    from torch's triangular helpers."""
+    ones = torch.ones(n, n, dtype=torch.bool)
+    band = ones.tril() & ~ones.tril(-W)
+    pinned = torch.zeros(n, n, dtype=torch.bool)
+    pinned[:, :L] = True
+    return (band | (pinned & ones.tril())).numpy()
+
+
+@pytest.mark.parametrize("L,W,kind", [(0, 1 << 20, "full"), (5, 1 << 20, "full"), (40, 3, "full-prefix"),
+                                      (0, 6, "swa"), (0, 1, "swa"), (3, 6, "ps")])
+def test_prefill_reduces_to_reference_attention(L, W, kind):
+    rs = np.random.default_rng(7)
+    n, hq, hkv, d = 37, 6, 2, 16
+    q = rs.standard_normal((n, hq, d))
+    k = rs.standard_normal((n, hkv, d))
+    v = rs.standard_normal((n, hkv, d))
+    scale = 1 / math.sqrt(d)
+    got, _ = oracle.prefill_attention(q, k, v, min(L, n), W, min(L, n), scale, 0.0)
+    if kind.startswith("full"):
+        mask = np.tril(np.ones((n, n), dtype=bool))       # L >= n or W >= n: plain causal attention
+    else:
+        mask = _band_mask(n, L, W)
+    want = _sdpa(q, k, v, mask, scale)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("L,W", [(0, 1 << 20), (0, 9), (4, 9), (64, 2)])
+def test_decode_reduces_to_reference_attention(L, W):
+    rs = np.random.default_rng(11)
+    hq, hkv, d = 8, 2, 16
+    k = rs.standard_normal((60, hkv, d))
+    v = rs.standard_normal((60, hkv, d))
+    for p in (0, 1, 8, 13, 59):
+        q = rs.standard_normal((hq, d))
+        got = oracle.decode_attention(q, k, v, p, L, W, 0.25, 0.0)
+        mask = _band_mask(p + 1, min(L, p + 1), W)[-1:]
+        want = _sdpa(q[None], k[:p + 1], v[:p + 1], mask, 0.25)[0]
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_decode_with_rope_matches_reference_on_complex_rotation():
+    # rotate with the complex-number form of RoPE (x_lo + i x_hi) * exp(i pos f), then plain attention
+    rs = np.random.default_rng(5)
+    L, W, p, hq, hkv, d, theta = 3, 10, 40, 4, 1, 8, 10000.0
+    k = rs.standard_normal((p + 1, hkv, d))
+    v = rs.standard_normal((p + 1, hkv, d))
+    q = rs.standard_normal((hq, d))
+    f = theta ** (-np.arange(d // 2) * 2.0 / d)
+
+    def crot(x, pos):
+        z = (x[..., : d // 2] + 1j * x[..., d // 2:]) * np.exp(1j * np.multiply.outer(pos, f))
+        return np.concatenate([z.real, z.imag], axis=-1)
+
+    pos = np.arange(p + 1)
+    kr = crot(k, pos[:, None])
+    qr = crot(q, np.full(hq, p))
+    mask = _band_mask(p + 1, L, W)[-1:]
+    want = _sdpa(qr[None], kr, v, mask, 0.2)[0]
+    got = oracle.decode_attention(q, k, v, p, L, W, 0.2, theta)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("L,W", [(0, 5), (4, 6), (10, 3), (2, 100)])
+def test_zero_query_gives_mean_of_visible_values(L, W):
+    # q = 0 -> uniform weights over A(p).  With v_j = (1, j, j^2) the output is
+    # (1, mean j, mean j^2) over A(p), written here with arithmetic-series sums.
+    d = 4
+
+    def s1(a, b):  # sum of j for a <= j < b
+        return (b - a) * (a + b - 1) / 2 if b > a else 0.0
+
+    def s2(a, b):  # sum of j^2 for a <= j < b
+        f = lambda n: (n - 1) * n * (2 * n - 1) / 6  # sum_{j<n} j^2
+        return f(b) - f(a) if b > a else 0.0
+
+    for p in range(0, 60):
+        j = np.arange(p + 1, dtype=np.float64)
+        v = np.zeros((p + 1, 1, d))
+        v[:, 0, 0], v[:, 0, 1], v[:, 0, 2] = 1.0, j, j * j
+        k = np.random.default_rng(p).standard_normal((p + 1, 1, d))
+        got = oracle.decode_attention(np.zeros((2, d)), k, v, p, L, W, 1.0, 10000.0)
+        a = min(L, p + 1)                     # prefix part [0, a)
+        b = max(p - W + 1, a)                 # window part [b, p+1), disjoint from the prefix
+        n = a + (p + 1 - b)
+        assert n == min(p + 1, L + W)
+        want = [1.0, (s1(0, a) + s1(b, p + 1)) / n, (s2(0, a) + s2(b, p + 1)) / n, 0.0]
+        np.testing.assert_allclose(got[0], want, rtol=1e-13)
+        np.testing.assert_allclose(got[1], want, rtol=1e-13)
+
+
+def test_single_visible_key_returns_its_value():
+    rs = np.random.default_rng(1)
+    k = rs.standard_normal((1, 2, 8))
+    v = rs.standard_normal((1, 2, 8))
+    out = oracle.decode_attention(rs.standard_normal((4, 8)), k, v, 0, 0, 1, 1.0, 10000.0)
+    np.testing.assert_allclose(out, np.repeat(v[0], 2, axis=0), rtol=0, atol=0)
+    # W = 1 with no prefix: every query sees only itself
+    k = rs.standard_normal((9, 2, 8))
+    v = rs.standard_normal((9, 2, 8))
+    out = oracle.decode_attention(rs.standard_normal((4, 8)), k, v, 8, 0, 1, 1.0, 10000.0)
+    np.testing.assert_allclose(out, np.repeat(v[8], 2, axis=0), rtol=0, atol=1e-15)
+
+
+def test_gqa_head_map_is_consecutive():
+    # Hq=4, Hkv=2: heads 0,1 -> KV head 0; heads 2,3 -> KV head 1.  With a single
+    # visible key the output is that KV head's value.
+    rs = np.random.default_rng(2)
+    k = rs.standard_normal((1, 2, 8))
+    v = rs.standard_normal((1, 2, 8))
+    out = oracle.decode_attention(rs.standard_normal((4, 8)), k, v, 0, 0, 1, 1.0, 0.0)
+    for h in range(4):
+        np.testing.assert_array_equal(out[h], v[0, h // 2])
+
+
+# ---------------------------------------------------------------- RoPE
+def test_rope_two_dims_is_plane_rotation():
+    x = np.array([[0.3, -1.7]])
+    for pos in (0, 1, 5, 1000, 131072):
+        c, s = math.cos(pos), math.sin(pos)           # D=2: the only frequency is theta^0 = 1
+        want = np.array([[c * 0.3 - s * -1.7, s * 0.3 + c * -1.7]])
+        np.testing.assert_allclose(oracle.rope(x, pos, 10000.0), want, rtol=0, atol=1e-15)
+
+
+def test_rope_frequencies_and_pairing():
+    # unit vector e_i (i < D/2) at position pos rotates into (cos, sin) on dims (i, i + D/2)
+    d, theta = 8, 10000.0
+    for i in range(d // 2):
+        e = np.zeros(d)
+        e[i] = 1.0
+        pos = 37
+        ang = pos * theta ** (-2 * i / d)
+        want = np.zeros(d)
+        want[i], want[i + d // 2] = math.cos(ang), math.sin(ang)
+        np.testing.assert_allclose(oracle.rope(e, pos, theta), want, atol=1e-15)
+
+
+def test_rope_relative_position_and_norm():
+    rs = np.random.default_rng(4)
+    q, k = rs.standard_normal(64), rs.standard_normal(64)
+    base = oracle.rope(q, 100, 10000.0) @ oracle.rope(k, 70, 10000.0)
+    for shift in (1, 17, 4096, 131000):
+        got = oracle.rope(q, 100 + shift, 10000.0) @ oracle.rope(k, 70 + shift, 10000.0)
+        assert abs(got - base) < 1e-9
+    np.testing.assert_allclose(np.linalg.norm(oracle.rope(q, 262143, 10000.0)), np.linalg.norm(q), rtol=1e-14)
+    np.testing.assert_array_equal(oracle.rope(q, 0, 10000.0), q)
+
+
+# ---------------------------------------------------------------- decode == prefill row
+def test_decode_matches_prefill_rows_tiny_config():
+    c = synth.C1_PREFILL
+    n = 200
+    k = synth.history(0, 1, synth.T_K, 0, 0, 0, n, c.hkv, c.dim, 1.0, "f32")
+    v = synth.history(0, 1, synth.T_V, 0, 0, 0, n, c.hkv, c.dim, 1.0, "f32")
+    q = synth.history(0, 1, synth.T_Q, 0, 0, 0, n, c.hq, c.dim, 1.0, "f32")
+    pre, _ = oracle.prefill_attention(q, k, v, c.prefix, c.window, c.prefix, 0.125, 10000.0)
+    for p in (0, 15, 16, 79, 80, 81, 199):
+        dec = oracle.decode_attention(q[p], k, v, p, c.prefix, c.window, 0.125, 10000.0)
+        np.testing.assert_allclose(dec, pre[p], rtol=0, atol=1e-12)
+
+
+def test_prefill_lse_matches_direct_sum():
+    rs = np.random.default_rng(9)
+    q = rs.standard_normal((12, 2, 8))
+    k = rs.standard_normal((15, 1, 8))
+    v = rs.standard_normal((15, 1, 8))
+    _, lse = oracle.prefill_attention(q, k, v, 3, 4, 3, 0.5, 0.0)
+    posk = np.arange(15)
+    for t in range(12):
+        pq = 3 + t
+        vis = [j for j in range(15) if j <= pq and (j < 3 or j > pq - 4)]
+        for h in range(2):
+            want = math.log(sum(math.exp(0.5 * float(q[t, h] @ k[j, 0])) for j in vis))
+            assert abs(lse[t, h] - want) < 1e-12
+
+
+# ---------------------------------------------------------------- tile plan
+def test_tile_plan_hand_worked_cases():
+    for case in _golden("tile_plan_small.json")["cases"]:
+        plan = oracle.tile_plan(case["T"], case["Nk"], case["L"], case["W"], case["kv_start"], case["BM"],
+                                case["BN"])
+        want = [(qt, kt, oracle.KIND_FULL if kind == "F" else oracle.KIND_PARTIAL)
+                for qt, kt, kind, _ in case["tiles"]]
+        assert plan == want, case["name"]
+        assert oracle.visible_pairs(case["T"], case["Nk"], case["L"], case["W"], case["kv_start"]) \
+            == case["total_pairs"]
+
+
+def test_tile_plan_invariants_truncated_backprop_shape():
+    # chunk of 4W tokens behind a 100-token prefix, as in the truncated-backprop example
+    g = _golden("pages_numbers.json")["truncated_backprop_example"]
+    W, T, L, start = g["window"], g["trainer_tokens"], 100, 98304
+    nk = L + T
+    total = oracle.visible_pairs(T, nk, L, W, start)
+    # closed form: every query sees the whole prefix plus min(t+1, W) chunk keys
+    assert total == L * T + sum(min(t + 1, W) for t in range(T)) == 15_500_288
+    plan = oracle.tile_plan(T, nk, L, W, start, 128, 64)
+    full = [p for p in plan if p[2] == oracle.KIND_FULL]
+    # full tiles carry BM*BN pairs each, partial tiles the remainder, and no pair is lost
+    posk = oracle.key_positions(nk, L, start)
+    posq = posk[nk - T:]
+    covered = 0
+    for qt, kt, kind in plan:
+        cnt = int(oracle.visible(posq[qt * 128:(qt + 1) * 128, None], posk[None, kt * 64:(kt + 1) * 64],
+                                 L, W).sum())
+        assert cnt > 0 and (kind == oracle.KIND_PARTIAL or cnt == 128 * 64)
+        covered += cnt
+    assert covered == total and len(full) > 0
+
+
+def test_key_positions_layout():
+    np.testing.assert_array_equal(oracle.key_positions(6, 2, 100), [0, 1, 100, 101, 102, 103])
+    np.testing.assert_array_equal(oracle.key_positions(4, 0, 7), [7, 8, 9, 10])
+
+
+# ---------------------------------------------------------------- byte accounting from the pages
+def test_kv_bytes_per_token_formula():
+    for key in ("kv_bytes_per_token_qwen3_1p7b", "kv_bytes_per_token_7b"):
+        g = _golden("pages_numbers.json")[key]
+        b = 2 * g["layers"] * g["kv_heads"] * g["head_dim"] * g["bytes_per_elem"]
+        assert round(b / 1000) == g["approx_kb"] or round(b / 1024) == g["approx_kb"]
+
+
+# ---------------------------------------------------------------- synthetic input rounding
+def test_bf16_rounding_matches_torch():
+    x = synth.normal((4096,), 0, 99, std=3.0)
+    want = torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(synth.round_to(x, "bf16"), want)
