@@ -1,0 +1,332 @@
+// C-ABI entry points: host-side validation, workspace sizing and launches.
+// Every check the host can make happens before anything is enqueued.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ps_internal.h"
+#include "ps_sched.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ps_status fail(ps_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ps_status fail(ps_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ps_status ok() {
+  g_last_error.clear();
+  return PS_OK;
+}
+
+ps_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PS_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+ps_status check_attn(const ps_attn_desc* a) {
+  if (!a) return fail(PS_INVALID_ARGUMENT, "attention descriptor is NULL");
+  if (a->num_q_heads <= 0 || a->num_kv_heads <= 0)
+    return fail(PS_INVALID_ARGUMENT, "head counts must be positive (Hq=%d, Hkv=%d)", a->num_q_heads, a->num_kv_heads);
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return fail(PS_INVALID_ARGUMENT, "Hq=%d is not a multiple of Hkv=%d", a->num_q_heads, a->num_kv_heads);
+  if (a->num_q_heads / a->num_kv_heads > ps::kMaxGroup)
+    return fail(PS_UNSUPPORTED, "query heads per KV head %d exceeds %d", a->num_q_heads / a->num_kv_heads,
+                ps::kMaxGroup);
+  if (a->head_dim != 64 && a->head_dim != 128) return fail(PS_UNSUPPORTED, "head_dim %d (64 or 128)", a->head_dim);
+  if (a->dtype != PS_BF16 && a->dtype != PS_F32) return fail(PS_UNSUPPORTED, "dtype %d", a->dtype);
+  if (!(a->softmax_scale > 0.f) || !isfinite(a->softmax_scale))
+    return fail(PS_INVALID_ARGUMENT, "softmax_scale must be positive and finite");
+  if (!(a->rope_theta >= 0.0) || !isfinite(a->rope_theta))
+    return fail(PS_INVALID_ARGUMENT, "rope_theta must be >= 0 and finite");
+  if (a->rope_theta > 0.0 && a->rope_theta <= 1.0) return fail(PS_INVALID_ARGUMENT, "rope_theta must exceed 1");
+  return PS_OK;
+}
+
+ps_status check_cache(const ps_cache_desc* c, const int32_t* block_table) {
+  if (!c) return fail(PS_INVALID_ARGUMENT, "cache descriptor is NULL");
+  if (c->window < 1) return fail(PS_INVALID_ARGUMENT, "window W=%d must be >= 1", c->window);
+  if (c->page_size != 0 && c->page_size != 64)
+    return fail(PS_UNSUPPORTED, "page_size %d (0 = contiguous or 64)", c->page_size);
+  if (c->slot_capacity <= 0 || c->slot_capacity % 64 != 0)
+    return fail(PS_INVALID_ARGUMENT, "slot_capacity %d must be a positive multiple of 64", c->slot_capacity);
+  if (c->page_size == 64) {
+    if (!block_table) return fail(PS_INVALID_ARGUMENT, "paged cache needs a block table");
+    if (c->max_pages_per_seq * 64 != c->slot_capacity)
+      return fail(PS_INVALID_ARGUMENT, "max_pages_per_seq*64 (%d) != slot_capacity (%d)", c->max_pages_per_seq * 64,
+                  c->slot_capacity);
+    if (c->num_pages <= 0) return fail(PS_INVALID_ARGUMENT, "paged cache needs num_pages > 0");
+  }
+  return PS_OK;
+}
+
+ps::CacheGeom make_geom(const ps_attn_desc* a, const ps_cache_desc* c) {
+  ps::CacheGeom g;
+  g.paged = c->page_size == 64 ? 1 : 0;
+  g.hkv = a->num_kv_heads;
+  g.head_dim = a->head_dim;
+  g.window = c->window;
+  g.slot_capacity = c->slot_capacity;
+  g.max_pages = c->page_size == 64 ? c->max_pages_per_seq : 0;
+  g.num_pages = c->page_size == 64 ? c->num_pages : 0;
+  return g;
+}
+
+ps::RopeFreq make_rope(const ps_attn_desc* a) {
+  ps::RopeFreq r;
+  r.enabled = a->rope_theta > 0.0 ? 1 : 0;
+  const int half = a->head_dim / 2;
+  for (int i = 0; i < ps::kMaxHalfDim; ++i)
+    r.inv_freq[i] = (r.enabled && i < half) ? pow(a->rope_theta, -2.0 * (double)i / (double)a->head_dim) : 0.0;
+  return r;
+}
+
+int32_t device_cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return cus;
+}
+
+// Split count: enough work items for about two resident decode workgroups per
+// CU, but never splits shorter than 4 chunks per wave.
+int32_t auto_splits(const ps_attn_desc* a, const ps_cache_desc* c, int32_t num_seqs, int32_t cus) {
+  const int64_t streams = (int64_t)num_seqs * a->num_kv_heads;
+  if (streams <= 0) return 1;
+  const int64_t want = (2 * (int64_t)cus + streams - 1) / streams;
+  const int64_t max_by_len = c->slot_capacity / (32 * 4 * 4);
+  int64_t s = want < max_by_len ? want : max_by_len;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return (int32_t)s;
+}
+
+int32_t split_keys_for(const ps_cache_desc* c, int32_t splits) {
+  const int32_t per = (c->slot_capacity + splits - 1) / splits;
+  return (per + 31) / 32 * 32;
+}
+
+size_t decode_ws_bytes(const ps_attn_desc* a, int32_t num_seqs, int32_t splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * a->num_q_heads * splits;
+  return rows * a->head_dim * sizeof(float) + rows * 2 * sizeof(float);
+}
+
+ps_status check_prefill_geom(int32_t window, int32_t prefix_len, int64_t kv_start, int32_t batch, int32_t num_q,
+                             int32_t num_k) {
+  if (window < 1) return fail(PS_INVALID_ARGUMENT, "window W=%d must be >= 1", window);
+  if (prefix_len < 0) return fail(PS_INVALID_ARGUMENT, "prefix_len %d must be >= 0", prefix_len);
+  if (batch < 0 || num_q < 0 || num_k < 0) return fail(PS_INVALID_ARGUMENT, "negative batch/query/key count");
+  if (prefix_len > num_k) return fail(PS_INVALID_ARGUMENT, "prefix_len %d exceeds num_keys %d", prefix_len, num_k);
+  if (kv_start < prefix_len) return fail(PS_INVALID_ARGUMENT, "kv_start %lld < prefix_len %d", (long long)kv_start, prefix_len);
+  if (num_q > num_k) return fail(PS_INVALID_ARGUMENT, "num_queries %d exceeds num_keys %d", num_q, num_k);
+  if (num_q > num_k - prefix_len && kv_start != prefix_len)
+    return fail(PS_INVALID_ARGUMENT, "queries reach into the prefix, so kv_start must equal prefix_len");
+  return PS_OK;
+}
+
+size_t prefill_ws_bytes(const ps_attn_desc* a, int32_t batch, int32_t num_q, int32_t num_k) {
+  int32_t bm, bn;
+  ps::prefill_tile_shape(a->dtype, a->head_dim, &bm, &bn);
+  const size_t elem = a->dtype == PS_BF16 ? 2 : 4;
+  const size_t nkp = ((size_t)num_k + bn - 1) / bn * bn;
+  const size_t kv = 2 * (size_t)batch * a->num_kv_heads * nkp * a->head_dim * elem;
+  const size_t table = (size_t)num_q * (a->head_dim / 2) * 2 * sizeof(float);
+  return ((kv + 255) / 256) * 256 + table;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ps_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ps_abi_version(void) { return PS_ABI_VERSION; }
+
+const char* ps_status_string(ps_status st) {
+  switch (st) {
+    case PS_OK: return "ok";
+    case PS_INVALID_ARGUMENT: return "invalid argument";
+    case PS_UNSUPPORTED: return "unsupported";
+    case PS_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PS_HIP_ERROR: return "HIP error";
+  }
+  return "unknown status";
+}
+
+ps_status ps_kv_append(const ps_attn_desc* attn, const ps_cache_desc* cache, void* k_cache, void* v_cache,
+                       const int32_t* block_table, const int32_t* prefix_len, const int64_t* start_pos,
+                       const int32_t* seq_tokens, int32_t tokens_per_seq, const void* k_new, const void* v_new,
+                       int32_t num_seqs, int32_t* slot_pos, hipStream_t stream) {
+  ps_status st = check_attn(attn);
+  if (st != PS_OK) return st;
+  if ((st = check_cache(cache, block_table)) != PS_OK) return st;
+  if (num_seqs < 0 || tokens_per_seq < 0) return fail(PS_INVALID_ARGUMENT, "negative num_seqs or tokens_per_seq");
+  if (num_seqs == 0 || tokens_per_seq == 0) return ok();
+  if ((int64_t)num_seqs * tokens_per_seq > (int64_t)1 << 26)
+    return fail(PS_INVALID_ARGUMENT, "num_seqs*tokens_per_seq exceeds 2^26 per call");
+  if (!k_cache || !v_cache || !prefix_len || !start_pos || !k_new || !v_new)
+    return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  ps::AppendArgs a;
+  a.geom = make_geom(attn, cache);
+  a.dtype = attn->dtype;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.prefix_len = prefix_len;
+  a.start_pos = start_pos;
+  a.seq_tokens = seq_tokens;
+  a.tokens_per_seq = tokens_per_seq;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.num_seqs = num_seqs;
+  a.slot_pos = slot_pos;
+  a.rope = make_rope(attn);
+  return from_hip(ps::launch_append(a, stream), "ps_kv_append launch");
+}
+
+int32_t ps_decode_num_splits(const ps_attn_desc* attn, const ps_cache_desc* cache, int32_t num_seqs) {
+  if (check_attn(attn) != PS_OK || !cache || cache->slot_capacity <= 0 || num_seqs < 0) return 0;
+  return auto_splits(attn, cache, num_seqs, device_cu_count());
+}
+
+size_t ps_decode_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* cache, int32_t num_seqs,
+                                int32_t num_splits) {
+  if (check_attn(attn) != PS_OK || !cache || cache->slot_capacity <= 0 || num_seqs < 0 || num_splits < 0) return 0;
+  const int32_t s = num_splits > 0 ? num_splits : auto_splits(attn, cache, num_seqs, device_cu_count());
+  return decode_ws_bytes(attn, num_seqs, s);
+}
+
+ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table, const int32_t* prefix_len, const int64_t* pos,
+                         const void* q, void* out, int32_t num_seqs, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  ps_status st = check_attn(attn);
+  if (st != PS_OK) return st;
+  if ((st = check_cache(cache, block_table)) != PS_OK) return st;
+  if (num_seqs < 0) return fail(PS_INVALID_ARGUMENT, "negative num_seqs");
+  if (num_splits < 0) return fail(PS_INVALID_ARGUMENT, "negative num_splits");
+  if (num_seqs == 0) return ok();
+  if (!k_cache || !v_cache || !prefix_len || !pos || !q || !out) return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if ((int64_t)num_seqs * attn->num_kv_heads * 64 > (int64_t)1 << 31)
+    return fail(PS_INVALID_ARGUMENT, "num_seqs too large for one launch");
+  const int32_t splits = num_splits > 0 ? num_splits : auto_splits(attn, cache, num_seqs, device_cu_count());
+  if (splits > 1024 || splits > cache->slot_capacity / 32)
+    return fail(PS_INVALID_ARGUMENT, "num_splits %d too large for slot_capacity %d", splits, cache->slot_capacity);
+  const size_t need = decode_ws_bytes(attn, num_seqs, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PS_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  ps::DecodeArgs a;
+  a.geom = make_geom(attn, cache);
+  a.dtype = attn->dtype;
+  a.hq = attn->num_q_heads;
+  a.group = attn->num_q_heads / attn->num_kv_heads;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.prefix_len = prefix_len;
+  a.pos = pos;
+  a.q = q;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_splits = splits;
+  a.split_keys = split_keys_for(cache, splits);
+  float* ws = static_cast<float*>(workspace);
+  const size_t rows = (size_t)num_seqs * attn->num_q_heads * splits;
+  a.part_o = splits > 1 ? ws : nullptr;
+  a.part_ml = splits > 1 ? ws + rows * attn->head_dim : nullptr;
+  a.scale_log2 = attn->softmax_scale * 1.4426950408889634f;
+  a.rope = make_rope(attn);
+  return from_hip(ps::launch_decode(a, stream), "ps_decode_attn launch");
+}
+
+size_t ps_prefill_workspace_size(const ps_attn_desc* attn, int32_t batch, int32_t num_queries, int32_t num_keys) {
+  if (check_attn(attn) != PS_OK || batch < 0 || num_queries < 0 || num_keys < 0) return 0;
+  return prefill_ws_bytes(attn, batch, num_queries, num_keys);
+}
+
+ps_status ps_prefill_tile_shape(const ps_attn_desc* attn, int32_t* block_m, int32_t* block_n) {
+  ps_status st = check_attn(attn);
+  if (st != PS_OK) return st;
+  if (!block_m || !block_n) return fail(PS_INVALID_ARGUMENT, "NULL output pointer");
+  ps::prefill_tile_shape(attn->dtype, attn->head_dim, block_m, block_n);
+  return ok();
+}
+
+ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t prefix_len, int64_t kv_start,
+                          const void* q, const void* k, const void* v, int32_t batch, int32_t num_queries,
+                          int32_t num_keys, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  ps_status st = check_attn(attn);
+  if (st != PS_OK) return st;
+  if ((st = check_prefill_geom(window, prefix_len, kv_start, batch, num_queries, num_keys)) != PS_OK) return st;
+  if (batch == 0 || num_queries == 0) return ok();
+  if (!q || !k || !v || !out) return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  const size_t need = prefill_ws_bytes(attn, batch, num_queries, num_keys);
+  if (!workspace || workspace_bytes < need)
+    return fail(PS_WORKSPACE_TOO_SMALL, "prefill needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  int32_t bm, bn;
+  ps::prefill_tile_shape(attn->dtype, attn->head_dim, &bm, &bn);
+  if ((int64_t)batch * attn->num_q_heads * ((num_queries + bm - 1) / bm) + 8 > (int64_t)1 << 31)
+    return fail(PS_INVALID_ARGUMENT, "prefill grid too large");
+  ps::PrefillArgs a;
+  a.dtype = attn->dtype;
+  a.hq = attn->num_q_heads;
+  a.hkv = attn->num_kv_heads;
+  a.group = attn->num_q_heads / attn->num_kv_heads;
+  a.head_dim = attn->head_dim;
+  a.window = window;
+  a.prefix_len = prefix_len;
+  a.kv_start = kv_start;
+  a.batch = batch;
+  a.num_q = num_queries;
+  a.num_k = num_keys;
+  a.bm = bm;
+  a.bn = bn;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  const size_t elem = attn->dtype == PS_BF16 ? 2 : 4;
+  const size_t nkp = ((size_t)num_keys + bn - 1) / bn * bn;
+  const size_t kv = 2 * (size_t)batch * attn->num_kv_heads * nkp * attn->head_dim * elem;
+  a.k_rot = workspace;
+  a.rope_cs = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((kv + 255) / 256) * 256);
+  a.scale_log2 = attn->softmax_scale * 1.4426950408889634f;
+  a.rope = make_rope(attn);
+  return from_hip(ps::launch_prefill(a, stream), "ps_prefill_attn launch");
+}
+
+ps_status ps_prefill_plan(const ps_attn_desc* attn, int32_t window, int32_t prefix_len, int64_t kv_start,
+                          int32_t num_queries, int32_t num_keys, int32_t* tiles, int32_t max_tiles,
+                          int32_t* num_tiles, hipStream_t stream) {
+  ps_status st = check_attn(attn);
+  if (st != PS_OK) return st;
+  if ((st = check_prefill_geom(window, prefix_len, kv_start, 1, num_queries, num_keys)) != PS_OK) return st;
+  if (!num_tiles || (max_tiles > 0 && !tiles)) return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if (max_tiles < 0) return fail(PS_INVALID_ARGUMENT, "negative max_tiles");
+  int32_t bm, bn;
+  ps::prefill_tile_shape(attn->dtype, attn->head_dim, &bm, &bn);
+  return from_hip(ps::launch_prefill_plan(num_queries, num_keys, prefix_len, window, kv_start, bm, bn, tiles,
+                                          max_tiles, num_tiles, stream),
+                  "ps_prefill_plan launch");
+}
+
+}  // extern "C"

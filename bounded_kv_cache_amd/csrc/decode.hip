@@ -1,0 +1,458 @@
+// Split-KV decode attention over the bounded ring cache.
+//
+// Blog "Prefix Sliding 完全拆解" (pinghaoyang.com.cn): section
+// "核心机制：注意力掩码上的两个区间" -- a query at position p sees the prefix and
+// the last W tokens, so it reads min(p+1, L+W) keys whatever the trace length --
+// and section "Kernel 实现：两层级过滤" (only prefix and window are read).  Since
+// the ring's first min(p+1, L+W) slots hold exactly that set (keys stored
+// pre-rotated), decode needs no element mask, only a length.
+//
+// Work item: (sequence, KV head, key split).  The G = Hq/Hkv query heads of the
+// KV head are handled together so every K/V byte is read once per item.
+//
+// bf16 path (MFMA).  With G = 8 a key costs 8*D*2*2 flops per 4*D bytes, i.e.
+// 8 flop/byte; fp32 VALU FMAs at the ~5.6 TB/s target would take ~57% of the
+// non-packed vector peak before softmax, conversions and addressing.  The
+// product is a genuine (skinny) contraction, so it goes to the matrix cores:
+//   S^T[16 keys x 16 heads] = K[16 x 32] * Q^T[32 x 16]    (v_mfma_f32_16x16x32_bf16)
+//   O^T[16 dims x 16 heads] += V^T[16 x 32 keys] * P^T[32 keys x 16 heads]
+// Heads are padded to 16 (MFMA headroom is >10x).  Key rows of the two QK tiles
+// of a 32-key chunk are permuted (row m of tile t is key 8*(m/4) + 4t + m%4) so
+// that the S output registers of a lane ARE its P operand for the PV MFMA: lane
+// (g = lane/16, n = lane%16) ends up holding keys 8g..8g+7 of head n, and no
+// cross-lane shuffle is needed between the two products.  The V cache stores
+// each run of 8 slots d-major, so the V^T operand (8 consecutive keys of one
+// dim) is a single 16-byte load.  K operands are 16-byte loads of a key row.
+// Everything goes HBM -> VGPR directly (no reuse to stage through LDS); chunks
+// are double-buffered in registers.  The running max needs a 4-lane max per
+// chunk; running sums stay lane-local until the end.
+#include "ps_internal.h"
+
+namespace ps {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+struct RegionRef {
+  const uint16_t* k;
+  const uint16_t* v;
+};
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA partial kernel
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
+  constexpr int NC = D / 32;   // QK k-steps (32 dims each)
+  constexpr int NDT = D / 16;  // PV d-tiles (16 dims each)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;   // MFMA row/column index
+  const int g = lane >> 4;   // MFMA lane group (k-slot group)
+
+  int bid = blockIdx.x;
+  const int split = bid % a.num_splits;
+  bid /= a.num_splits;
+  const int h = bid % a.geom.hkv;
+  const int s = bid / a.geom.hkv;
+  const CacheGeom& geo = a.geom;
+
+  const int32_t L = a.prefix_len[s];
+  const int64_t pos = a.pos[s];
+  bool bad = L < 0 || (int64_t)L + geo.window > geo.slot_capacity || pos < 0;
+  const int64_t nvis64 = bad ? 0 : (pos + 1 < (int64_t)L + geo.window ? pos + 1 : (int64_t)L + geo.window);
+  const int nvis = (int)nvis64;
+  const int kb = split * a.split_keys;
+  const int ke = kb + a.split_keys < nvis ? kb + a.split_keys : nvis;
+
+  // ---- query operand: rotate at pos, fold in scale*log2(e), round to bf16 ----
+  bf16x8 qop[NC];
+  {
+    const int G = a.group;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)s * a.hq + h * G + (r < G ? r : 0)) * D;
+    float qv[NC][8];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[c][2 * e] = (r < G) ? lo_bf16(ww[e]) : 0.f;
+        qv[c][2 * e + 1] = (r < G) ? hi_bf16(ww[e]) : 0.f;
+      }
+    }
+    if (a.rope.enabled) {
+#pragma unroll
+      for (int c = 0; c < NC / 2; ++c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float cs, sn;
+          rope_cos_sin(pos, a.rope.inv_freq[32 * c + 8 * g + i], cs, sn);
+          const float x1 = qv[c][i], x2 = qv[c + NC / 2][i];
+          qv[c][i] = x1 * cs - x2 * sn;
+          qv[c + NC / 2][i] = x2 * cs + x1 * sn;
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qop[c][i] = (bf16)(qv[c][i] * a.scale_log2);
+  }
+
+  // ---- per-lane load offsets inside a 32-key chunk (elements) ----
+  // K tile t, row r -> key 8*(r/4) + 4t + r%4; k-step c covers dims 32c + 8g .. +8
+  int koff[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) koff[t] = (8 * (r >> 2) + 4 * t + (r & 3)) * D + 8 * g;
+  // V block g (keys 8g..8g+7), d-tile dt, dim 16*dt + r: 8 contiguous bf16
+  const int voff = g * 8 * D + r * 8;
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x4 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+
+  // chunk index list of this wave: first chunk kb/32 + wave, stride NW
+  const int c_end = (ke + 31) >> 5;   // chunks touching [kb, ke)
+  int c = (kb >> 5) + wave;
+
+  uint4 kA[2][NC], vA[NDT], kB[2][NC], vB[NDT];
+
+  auto load_chunk = [&](int ci, uint4 (&kr)[2][NC], uint4 (&vr)[NDT]) {
+    const int key0 = ci << 5;
+    const int64_t base = region_offset(geo, a.block_table, s, h, key0);
+    if (base < 0) {
+      bad = true;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) kr[t][cc] = uint4{0, 0, 0, 0};
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vr[dt] = uint4{0, 0, 0, 0};
+      return;
+    }
+    const int in_reg = (key0 & 63) * D;
+    const uint16_t* kp = kc + base + in_reg;
+    const uint16_t* vp = vc + base + in_reg;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) kr[t][cc] = *reinterpret_cast<const uint4*>(kp + koff[t] + 32 * cc);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vr[dt] = *reinterpret_cast<const uint4*>(vp + voff + dt * 16 * 8);
+  };
+
+  auto compute_chunk = [&](int ci, uint4 (&kr)[2][NC], uint4 (&vr)[NDT]) {
+    f32x4 st0 = f32x4{0.f, 0.f, 0.f, 0.f}, st1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      st0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[0][cc]), qop[cc], st0, 0, 0, 0);
+      st1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[1][cc]), qop[cc], st1, 0, 0, 0);
+    }
+    // lane holds head r, keys 8g + i (i<4 from tile 0, i>=4 from tile 1)
+    float sv[8] = {st0[0], st0[1], st0[2], st0[3], st1[0], st1[1], st1[2], st1[3]};
+    const int key0 = (ci << 5) + 8 * g;
+    const bool tail = ((ci + 1) << 5) > ke || (ci << 5) < kb;
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = key0 + i;
+        if (key >= ke || key < kb) sv[i] = -INFINITY;
+      }
+      // masked keys must contribute exactly zero: clear their V elements too
+      // (slots past the visible length may hold anything, including NaN bits)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        uint32_t w[4] = {vr[dt].x, vr[dt].y, vr[dt].z, vr[dt].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k0 = key0 + 2 * e;
+          if (k0 >= ke || k0 < kb) w[e] &= 0xffff0000u;
+          if (k0 + 1 >= ke || k0 + 1 < kb) w[e] &= 0x0000ffffu;
+        }
+        vr[dt] = uint4{w[0], w[1], w[2], w[3]};
+      }
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float pv[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
+      psum += pv[i];
+    }
+    l_run = l_run * alpha + psum;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+    }
+    bf16x8 pop;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pop[i] = (bf16)pv[i];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vr[dt]), pop, acc[dt], 0, 0, 0);
+  };
+
+  if (c < c_end) load_chunk(c, kA, vA);
+  while (c < c_end) {
+    if (c + NW < c_end) load_chunk(c + NW, kB, vB);
+    compute_chunk(c, kA, vA);
+    c += NW;
+    if (c >= c_end) break;
+    if (c + NW < c_end) load_chunk(c + NW, kA, vA);
+    compute_chunk(c, kB, vB);
+    c += NW;
+  }
+
+  // ---- finish the wave: sum the lane-local partial sums of each head ----
+  l_run += wave_shfl_xor(l_run, 16);
+  l_run += wave_shfl_xor(l_run, 32);
+
+  // ---- merge the NW waves through LDS ----
+  __shared__ float sm_o[NW][D][17];
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  __shared__ int sm_bad;
+  if (threadIdx.x == 0) sm_bad = 0;
+  __syncthreads();
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_o[wave][16 * dt + 4 * g + i][r] = acc[dt][i];
+  if (g == 0) {
+    sm_m[wave][r] = m_run;
+    sm_l[wave][r] = l_run;
+  }
+  if (bad) sm_bad = 1;
+  __syncthreads();
+
+  const int G = a.group;
+  const bool any_bad = sm_bad != 0;
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int n = idx / D;
+    const int d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][n]);
+    float o = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm_m[w][n] - M);
+        o += f * sm_o[w][d][n];
+        l += f * sm_l[w][n];
+      }
+    }
+    const int64_t row = (int64_t)s * a.hq + h * G + n;
+    if (a.num_splits == 1) {
+      const float val = any_bad ? __builtin_nanf("") : o / l;
+      static_cast<uint16_t*>(a.out)[row * D + d] = f32_to_bf16_bits(val);
+    } else {
+      const int64_t prow = row * a.num_splits + split;
+      a.part_o[prow * D + d] = any_bad ? __builtin_nanf("") : o;
+      if (d == 0) {
+        a.part_ml[prow * 2 + 0] = any_bad ? __builtin_nanf("") : M;
+        a.part_ml[prow * 2 + 1] = any_bad ? __builtin_nanf("") : l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 debug partial kernel (plain VALU, LDS-tiled; correctness path)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
+  constexpr int TK = 32;  // keys per tile
+  __shared__ float qs[kMaxGroup][D];
+  __shared__ float ks[TK][D + 1];
+  __shared__ float vs[TK][D + 1];
+  __shared__ float ps_[kMaxGroup][TK];
+  __shared__ float m_s[kMaxGroup], l_s[kMaxGroup], alpha_s[kMaxGroup];
+  __shared__ int bad_s;
+
+  int bid = blockIdx.x;
+  const int split = bid % a.num_splits;
+  bid /= a.num_splits;
+  const int h = bid % a.geom.hkv;
+  const int s = bid / a.geom.hkv;
+  const CacheGeom& geo = a.geom;
+  const int G = a.group;
+  const int tid = threadIdx.x;
+
+  const int32_t L = a.prefix_len[s];
+  const int64_t pos = a.pos[s];
+  const bool seq_bad = L < 0 || (int64_t)L + geo.window > geo.slot_capacity || pos < 0;
+  const int nvis = seq_bad ? 0 : (int)(pos + 1 < (int64_t)L + geo.window ? pos + 1 : (int64_t)L + geo.window);
+  const int kb = split * a.split_keys;
+  const int ke = kb + a.split_keys < nvis ? kb + a.split_keys : nvis;
+
+  const float* q = static_cast<const float*>(a.q);
+  for (int idx = tid; idx < G * (D / 2); idx += 256) {
+    const int n = idx / (D / 2), i = idx % (D / 2);
+    const float* qr = q + ((int64_t)s * a.hq + h * G + n) * D;
+    float x1 = qr[i], x2 = qr[i + D / 2];
+    if (a.rope.enabled) {
+      float c, sn;
+      rope_cos_sin(pos, a.rope.inv_freq[i], c, sn);
+      const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
+      x1 = y1;
+      x2 = y2;
+    }
+    qs[n][i] = x1 * a.scale_log2;
+    qs[n][i + D / 2] = x2 * a.scale_log2;
+  }
+  if (tid < kMaxGroup) {
+    m_s[tid] = -INFINITY;
+    l_s[tid] = 0.f;
+  }
+  if (tid == 0) bad_s = seq_bad ? 1 : 0;
+  constexpr int NOUT = (kMaxGroup * D + 255) / 256;
+  float acc[NOUT];
+#pragma unroll
+  for (int k = 0; k < NOUT; ++k) acc[k] = 0.f;
+  const float* kc = static_cast<const float*>(a.k_cache);
+  const float* vc = static_cast<const float*>(a.v_cache);
+  __syncthreads();
+
+  for (int t0 = kb; t0 < ke; t0 += TK) {
+    const int64_t base = region_offset(geo, a.block_table, s, h, t0);
+    if (base < 0) {
+      if (tid == 0) bad_s = 1;
+      break;
+    }
+    // tiles start at multiples of 32, so a tile never crosses a 64-slot region
+    for (int idx = tid; idx < TK * D; idx += 256) {
+      const int j = idx / D, d = idx % D;
+      const int key = t0 + j;
+      const bool ok = key < ke;
+      ks[j][d] = ok ? kc[base + k_in_region(key, d, D)] : 0.f;
+      vs[j][d] = ok ? vc[base + v_in_region(key, d, D)] : 0.f;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * TK; idx += 256) {
+      const int n = idx / TK, j = idx % TK;
+      float sc = 0.f;
+      for (int d = 0; d < D; ++d) sc += qs[n][d] * ks[j][d];
+      ps_[n][j] = (t0 + j < ke) ? sc : -INFINITY;
+    }
+    __syncthreads();
+    if (tid < G) {
+      float mx = -INFINITY;
+      for (int j = 0; j < TK; ++j) mx = fmaxf(mx, ps_[tid][j]);
+      const float mn = fmaxf(m_s[tid], mx);
+      const float al = __builtin_amdgcn_exp2f(m_s[tid] - mn);
+      float sum = 0.f;
+      for (int j = 0; j < TK; ++j) {
+        const float e = __builtin_amdgcn_exp2f(ps_[tid][j] - mn);
+        ps_[tid][j] = e;
+        sum += e;
+      }
+      l_s[tid] = l_s[tid] * al + sum;
+      m_s[tid] = mn;
+      alpha_s[tid] = al;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NOUT; ++k) {
+      const int idx = tid + 256 * k;
+      if (idx < G * D) {
+        const int n = idx / D, d = idx % D;
+        float o = acc[k] * alpha_s[n];
+        for (int j = 0; j < TK; ++j) o += ps_[n][j] * vs[j][d];
+        acc[k] = o;
+      }
+    }
+    __syncthreads();
+  }
+  __syncthreads();
+  const bool any_bad = bad_s != 0;
+#pragma unroll
+  for (int k = 0; k < NOUT; ++k) {
+    const int idx = tid + 256 * k;
+    if (idx >= G * D) continue;
+    const int n = idx / D, d = idx % D;
+    const int64_t row = (int64_t)s * a.hq + h * G + n;
+    if (a.num_splits == 1) {
+      static_cast<float*>(a.out)[row * D + d] = any_bad ? __builtin_nanf("") : acc[k] / l_s[n];
+    } else {
+      const int64_t prow = row * a.num_splits + split;
+      a.part_o[prow * D + d] = any_bad ? __builtin_nanf("") : acc[k];
+      if (d == 0) {
+        a.part_ml[prow * 2 + 0] = any_bad ? __builtin_nanf("") : m_s[n];
+        a.part_ml[prow * 2 + 1] = any_bad ? __builtin_nanf("") : l_s[n];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine: merge the split partials of each (sequence, query head) in split order
+// ---------------------------------------------------------------------------
+template <typename OutT, int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+  const int64_t row = blockIdx.x;  // s * hq + head
+  const int d = threadIdx.x;
+  const int S = a.num_splits;
+  const float* ml = a.part_ml + row * S * 2;
+  float M = -INFINITY;
+  bool nan = false;
+  for (int i = 0; i < S; ++i) {
+    const float m = ml[2 * i];
+    nan |= (m != m);
+    M = fmaxf(M, m);
+  }
+  float o = 0.f, l = 0.f;
+  for (int i = 0; i < S; ++i) {
+    const float m = ml[2 * i];
+    if (m == -INFINITY) continue;  // empty split
+    const float f = __builtin_amdgcn_exp2f(m - M);
+    o += f * a.part_o[(row * S + i) * D + d];
+    l += f * ml[2 * i + 1];
+  }
+  const float val = nan ? __builtin_nanf("") : o / l;
+  Elem<OutT>::store(static_cast<OutT*>(a.out) + row * D + d, val);
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid((uint32_t)((int64_t)a.num_seqs * a.geom.hkv * a.num_splits));
+  if (a.dtype == PS_BF16) {
+    constexpr int NW = 4;
+    hipLaunchKernelGGL((decode_bf16_kernel<D, NW>), grid, dim3(NW * 64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(256), 0, stream, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_splits == 1) return e;
+  const dim3 cgrid((uint32_t)((int64_t)a.num_seqs * a.hq));
+  if (a.dtype == PS_BF16)
+    hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D>), cgrid, dim3(D), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<float, D>), cgrid, dim3(D), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  return a.geom.head_dim == 64 ? launch_decode_d<64>(a, stream) : launch_decode_d<128>(a, stream);
+}
+
+}  // namespace ps

@@ -1,0 +1,539 @@
+// Masked prefill / training-forward attention with tile skipping.
+//
+// Blog "Prefix Sliding 完全拆解" (pinghaoyang.com.cn): section
+// "Kernel 实现：两层级过滤" (skip tiles with no visible pair; element masks only
+// on partly visible tiles; walk the prefix tiles and the window tiles) and
+// section "超长 rollouts 的反向传播：截断回传" (a chunk of the trace behind
+// the prefix is attended to as a whole).
+//
+// Pipeline of one call:
+//   1. prep kernel: rotate K at its absolute positions into a per-(batch, KV
+//      head) contiguous copy, write V transposed ([D][keys], keys padded to BN
+//      with zeros) and a cos/sin table for the query positions.
+//   2. attention kernel: one workgroup per (batch, query head, BM-query tile),
+//      walking the scheduled key tiles (ps_sched.h).
+// The bf16 kernel is an MFMA kernel (v_mfma_f32_32x32x16_bf16): it computes
+// S^T = K Q^T so each lane owns one query column and the softmax reductions are
+// in-lane plus one cross-half exchange; the S^T registers feed the PV product
+// O^T += V^T P^T directly as its B operand, with V^T staged through LDS.
+#include "ps_internal.h"
+#include "ps_sched.h"
+
+namespace ps {
+namespace {
+
+constexpr float kLn2 = 0.69314718055994531f;
+
+template <typename T>
+struct PfTraits;
+template <>
+struct PfTraits<uint16_t> {
+  static constexpr int BM = 128, BN = 64;
+};
+template <>
+struct PfTraits<float> {
+  static constexpr int BM = 64, BN = 64;
+};
+
+__host__ __device__ inline int32_t nk_padded(int32_t nk, int32_t bn) { return (nk + bn - 1) / bn * bn; }
+
+// ---------------------------------------------------------------------------
+// 1. prep: rotated K [b][hkv][nkp][D], V^T [b][hkv][D][nkp], query cos/sin table
+// ---------------------------------------------------------------------------
+// One workgroup per (batch, 64-key tile): the tile's cos/sin are formed once in
+// LDS and reused for every KV head; V is transposed through LDS so that both
+// the reads and the V^T writes are row-contiguous.  Keys past num_k are zero.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
+  constexpr int TK = 64;
+  constexpr int HALF = D / 2;
+  __shared__ float cs_lds[TK][HALF][2];
+  __shared__ T vt_lds[D][TK + 1];
+  PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, a.bm, a.bn};
+  const int32_t nkp = nk_padded(a.num_k, a.bn);
+  const int32_t nkt = nkp / TK;
+  const int tid = threadIdx.x;
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  T* kr = static_cast<T*>(a.k_rot);
+  T* vt = kr + (int64_t)a.batch * a.hkv * nkp * D;
+
+  for (int64_t blk = blockIdx.x; blk < (int64_t)a.batch * nkt; blk += gridDim.x) {
+    const int32_t kt = (int32_t)(blk % nkt);
+    const int32_t b = (int32_t)(blk / nkt);
+    for (int idx = tid; idx < TK * HALF; idx += 256) {
+      const int j = idx / HALF, i = idx % HALF;
+      const int32_t key = kt * TK + j;
+      float c = 1.f, s = 0.f;
+      if (a.rope.enabled && key < a.num_k) rope_cos_sin(pf_key_pos(geo, key), a.rope.inv_freq[i], c, s);
+      cs_lds[j][i][0] = c;
+      cs_lds[j][i][1] = s;
+    }
+    __syncthreads();
+    for (int32_t h = 0; h < a.hkv; ++h) {
+      const int64_t bh = (int64_t)b * a.hkv + h;
+      for (int idx = tid; idx < TK * HALF; idx += 256) {
+        const int j = idx / HALF, i = idx % HALF;
+        const int32_t key = kt * TK + j;
+        float y1 = 0.f, y2 = 0.f;
+        T v1 = T(0), v2 = T(0);
+        if (key < a.num_k) {
+          const int64_t src = (((int64_t)b * a.num_k + key) * a.hkv + h) * D;
+          const float x1 = Elem<T>::load(k + src + i), x2 = Elem<T>::load(k + src + i + HALF);
+          const float c = cs_lds[j][i][0], s = cs_lds[j][i][1];
+          y1 = x1 * c - x2 * s;
+          y2 = x2 * c + x1 * s;
+          v1 = v[src + i];
+          v2 = v[src + i + HALF];
+        }
+        Elem<T>::store(kr + (bh * nkp + key) * D + i, y1);
+        Elem<T>::store(kr + (bh * nkp + key) * D + i + HALF, y2);
+        vt_lds[i][j] = v1;
+        vt_lds[i + HALF][j] = v2;
+      }
+      __syncthreads();
+      for (int idx = tid; idx < D * TK; idx += 256) {
+        const int d = idx / TK, j = idx % TK;
+        vt[(bh * D + d) * nkp + kt * TK + j] = vt_lds[d][j];
+      }
+      __syncthreads();
+    }
+  }
+  // cos/sin of every query position (shared by batch and heads)
+  const int64_t tq = (int64_t)a.num_q * HALF;
+  for (int64_t idx = blockIdx.x * 256ll + tid; idx < tq; idx += (int64_t)gridDim.x * 256) {
+    const int32_t i = (int32_t)(idx % HALF);
+    const int32_t t = (int32_t)(idx / HALF);
+    float c = 1.f, s = 0.f;
+    if (a.rope.enabled) rope_cos_sin(pf_query_pos(geo, t), a.rope.inv_freq[i], c, s);
+    a.rope_cs[idx * 2 + 0] = c;
+    a.rope_cs[idx * 2 + 1] = s;
+  }
+}
+
+// Work-item decode shared by the attention kernels: workgroups are spread so
+// that each XCD (hardware round-robin on blockIdx) gets a contiguous run of
+// items ordered (batch, KV head, q-tile, head-in-group): concurrently running
+// workgroups of one XCD then share the same K/V tiles in that XCD's L2.
+struct Item {
+  int32_t b, hq, qt;
+  bool valid;
+};
+__device__ inline Item decode_item(const PrefillArgs& a, int32_t n_qt) {
+  const int64_t total = (int64_t)a.batch * a.hq * n_qt;
+  const int64_t per = (total + 7) / 8;
+  const int64_t lin = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  Item it;
+  it.valid = lin < total;
+  const int32_t hg = (int32_t)(lin % a.group);
+  int64_t rest = lin / a.group;
+  it.qt = (int32_t)(rest % n_qt);
+  rest /= n_qt;
+  const int32_t kvh = (int32_t)(rest % a.hkv);
+  it.b = (int32_t)(rest / a.hkv);
+  it.hq = kvh * a.group + hg;
+  return it;
+}
+
+// ---------------------------------------------------------------------------
+// 2a. fp32 debug kernel: one thread per query row, LDS-tiled, same schedule
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
+  constexpr int BM = PfTraits<float>::BM, BN = PfTraits<float>::BN;
+  __shared__ float qs[BM][D + 1];
+  __shared__ float ks[BN][D + 1];
+  __shared__ float vs[BN][D + 1];
+  PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, BM, BN};
+  const int32_t n_qt = pf_num_qtiles(geo);
+  const Item it = decode_item(a, n_qt);
+  if (!it.valid) return;
+  const int tid = threadIdx.x;
+  const int32_t t = it.qt * BM + tid;
+  const bool row_ok = t < a.num_q;
+  const int32_t kvh = it.hq / a.group;
+  const int32_t nkp = nk_padded(a.num_k, BN);
+  const float* q = static_cast<const float*>(a.q);
+  const float* kr = static_cast<const float*>(a.k_rot) + ((int64_t)it.b * a.hkv + kvh) * nkp * D;
+  const float* vt = static_cast<const float*>(a.k_rot) + (int64_t)a.batch * a.hkv * nkp * D +
+                    ((int64_t)it.b * a.hkv + kvh) * D * nkp;
+  if (row_ok) {
+    const float* qrow = q + (((int64_t)it.b * a.num_q + t) * a.hq + it.hq) * D;
+    for (int i = 0; i < D / 2; ++i) {
+      const float c = a.rope_cs[((int64_t)t * (D / 2) + i) * 2], s = a.rope_cs[((int64_t)t * (D / 2) + i) * 2 + 1];
+      const float x1 = qrow[i], x2 = qrow[i + D / 2];
+      qs[tid][i] = (x1 * c - x2 * s) * a.scale_log2;
+      qs[tid][i + D / 2] = (x2 * c + x1 * s) * a.scale_log2;
+    }
+  }
+  const int64_t pq = row_ok ? pf_query_pos(geo, t) : 0;
+  float acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const TileRange tr = pf_tile_range(geo, it.qt);
+  const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
+  for (int32_t ci = 0; ci < n_cand; ++ci) {
+    const int32_t kt = ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix);
+    const int kind = pf_classify(geo, it.qt, kt);
+    if (kind == 0) continue;
+    __syncthreads();
+    for (int idx = tid; idx < BN * D; idx += 64) {
+      const int j = idx / D, d = idx % D;
+      ks[j][d] = kr[((int64_t)kt * BN + j) * D + d];
+      vs[j][d] = vt[(int64_t)d * nkp + kt * BN + j];
+    }
+    __syncthreads();
+    if (!row_ok) continue;
+    float sc[BN];
+    float mx = -INFINITY;
+    for (int j = 0; j < BN; ++j) {
+      float s = 0.f;
+      for (int d = 0; d < D; ++d) s += qs[tid][d] * ks[j][d];
+      const int32_t key = kt * BN + j;
+      bool vis = key < a.num_k;
+      if (kind == 2 && vis) {
+        const int64_t pk = pf_key_pos(geo, key);
+        vis = pk <= pq && (pk < a.prefix_len || pk > pq - a.window);
+      }
+      sc[j] = vis ? s : -INFINITY;
+      mx = fmaxf(mx, sc[j]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+    for (int d = 0; d < D; ++d) acc[d] *= alpha;
+    for (int j = 0; j < BN; ++j) {
+      const float p = __builtin_amdgcn_exp2f(sc[j] - m_use);
+      l_run += p;
+      for (int d = 0; d < D; ++d) acc[d] += p * vs[j][d];
+    }
+  }
+  if (!row_ok) return;
+  float* o = static_cast<float*>(a.out) + (((int64_t)it.b * a.num_q + t) * a.hq + it.hq) * D;
+  for (int d = 0; d < D; ++d) o[d] = acc[d] / l_run;
+  if (a.lse) a.lse[((int64_t)it.b * a.hq + it.hq) * a.num_q + t] = (m_run + __log2f(l_run)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// 2b. bf16 MFMA kernel
+// ---------------------------------------------------------------------------
+// Workgroup: 4 waves x 32 query rows = BM 128; key tiles of BN 64.
+// 32x32x16 MFMA lane layout used throughout (lane l, half hf = l/32, col = l%32):
+//   A[m][k]: lane (m + 32*(k/8)) element k%8        B[k][n]: lane (n + 32*(k/8)) element k%8
+//   D[m][n]: lane (n + 32*((m/4)%2)) register 4*(m/8) + m%4
+// The dim <-> k-slot map of QK is shared by both operands (dim 16*ks + 8*hf + e),
+// so it never matters which physical k the hardware pairs.
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr int BM = 128, BN = 64;
+  constexpr int KS = D / 16;        // QK k-steps
+  constexpr int MT = D / 32;        // PV output d-tiles
+  constexpr int KPAD = D + 8;       // K row stride in LDS (bf16 elements)
+  constexpr int VPAD = BN + 4;      // V^T row stride in LDS
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VPAD];
+
+  PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, BM, BN};
+  const int32_t n_qt = pf_num_qtiles(geo);
+  const Item it = decode_item(a, n_qt);
+  if (!it.valid) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int32_t kvh = it.hq / a.group;
+  const int32_t nkp = nk_padded(a.num_k, BN);
+  const uint16_t* kr = static_cast<const uint16_t*>(a.k_rot) + ((int64_t)it.b * a.hkv + kvh) * nkp * D;
+  const uint16_t* vt = static_cast<const uint16_t*>(a.k_rot) + (int64_t)a.batch * a.hkv * nkp * D +
+                       ((int64_t)it.b * a.hkv + kvh) * D * nkp;
+
+  // ---- query operand (B of S^T = K Q^T): query row t, dims 16*ks + 8*hf + e ----
+  const int32_t t = it.qt * BM + wave * 32 + col;
+  const bool row_ok = t < a.num_q;
+  bf16x8 qop[KS];
+  {
+    float qv[KS][8];
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           (((int64_t)it.b * a.num_q + (row_ok ? t : 0)) * a.hq + it.hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hf);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[ks][2 * e] = lo_bf16(ww[e]);
+        qv[ks][2 * e + 1] = hi_bf16(ww[e]);
+      }
+    }
+    const float* cs = a.rope_cs + (int64_t)(row_ok ? t : 0) * (D / 2) * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 16 * ks + 8 * hf + e;
+        const float c = cs[2 * i], s = cs[2 * i + 1];
+        const float x1 = qv[ks][e], x2 = qv[ks + KS / 2][e];
+        qv[ks][e] = x1 * c - x2 * s;
+        qv[ks + KS / 2][e] = x2 * c + x1 * s;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qop[ks][e] = (bf16)(row_ok ? qv[ks][e] * a.scale_log2 : 0.f);
+  }
+  const int64_t pq = row_ok ? pf_query_pos(geo, t) : -1;
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // ---- cooperative tile loads (global -> registers -> LDS) ----
+  // K tile: BN rows x D dims = BN*D/8 16-byte pieces; V^T tile: D rows x BN keys.
+  constexpr int KPIECES = BN * D / 8 / 256;   // per thread
+  constexpr int VPIECES = D * BN / 8 / 256;
+  uint4 kreg[KPIECES], vreg[VPIECES];
+  auto gload = [&](int32_t kt) {
+#pragma unroll
+    for (int p = 0; p < KPIECES; ++p) {
+      const int piece = tid + 256 * p;
+      const int row = piece / (D / 8), c8 = piece % (D / 8);
+      kreg[p] = *reinterpret_cast<const uint4*>(kr + ((int64_t)kt * BN + row) * D + c8 * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < VPIECES; ++p) {
+      const int piece = tid + 256 * p;
+      const int row = piece / (BN / 8), c8 = piece % (BN / 8);
+      vreg[p] = *reinterpret_cast<const uint4*>(vt + (int64_t)row * nkp + (int64_t)kt * BN + c8 * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < KPIECES; ++p) {
+      const int piece = tid + 256 * p;
+      const int row = piece / (D / 8), c8 = piece % (D / 8);
+      *reinterpret_cast<uint4*>(&k_lds[buf][row * KPAD + c8 * 8]) = kreg[p];
+    }
+#pragma unroll
+    for (int p = 0; p < VPIECES; ++p) {
+      const int piece = tid + 256 * p;
+      const int row = piece / (BN / 8), c8 = piece % (BN / 8);
+      uint16_t* dst = &v_lds[buf][row * VPAD + c8 * 8];
+      // VPAD keeps rows 8-byte aligned only: store as two 8-byte halves
+      *reinterpret_cast<uint2*>(dst) = uint2{vreg[p].x, vreg[p].y};
+      *reinterpret_cast<uint2*>(dst + 4) = uint2{vreg[p].z, vreg[p].w};
+    }
+  };
+
+  const TileRange tr = pf_tile_range(geo, it.qt);
+  const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
+  auto cand_tile = [&](int32_t ci) { return ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix); };
+
+  // find the first scheduled tile
+  int32_t ci = 0;
+  int kind = 0;
+  while (ci < n_cand && (kind = pf_classify(geo, it.qt, cand_tile(ci))) == 0) ++ci;
+  if (ci < n_cand) {
+    gload(cand_tile(ci));
+    lstore(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (ci < n_cand) {
+    const int32_t kt = cand_tile(ci);
+    const int cur_kind = kind;
+    // next scheduled tile; its loads are in flight during this tile's math
+    int32_t cn = ci + 1;
+    int nkind = 0;
+    while (cn < n_cand && (nkind = pf_classify(geo, it.qt, cand_tile(cn))) == 0) ++cn;
+    if (cn < n_cand) gload(cand_tile(cn));
+
+    // ---- S^T = K Q^T: two 32-key M-tiles ----
+    f32x16 st[2];
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[m2][i] = 0.f;
+      const uint16_t* krow = &k_lds[buf][(32 * m2 + col) * KPAD + 8 * hf];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
+        st[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], st[m2], 0, 0, 0);
+      }
+    }
+    // key of register i of tile m2: 32*m2 + 8*(i/4) + 4*hf + i%4
+    if (cur_kind == 2) {
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t key = kt * BN + 32 * m2 + 8 * (i >> 2) + 4 * hf + (i & 3);
+          bool vis = row_ok && key < a.num_k;
+          if (vis) {
+            const int64_t pk = pf_key_pos(geo, key);
+            vis = pk <= pq && (pk < a.prefix_len || pk > pq - a.window);
+          }
+          if (!vis) st[m2][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[m2][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    bf16x8 pop[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(st[m2][i] - m_use);
+        psum += p;
+        pop[2 * m2 + (i >> 3)][i & 7] = (bf16)p;
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+
+    // ---- O^T += V^T P^T: PV k-step j covers keys 16j + 8*(e/4) + 4*hf + e%4 ----
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint16_t* vrow = &v_lds[buf][(32 * mt + col) * VPAD + 4 * hf];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * j);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * j + 8);
+        const uint4 w = uint4{lo.x, lo.y, hi.x, hi.y};
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pop[j], acc[mt], 0, 0, 0);
+      }
+    }
+    if (cn < n_cand) lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    ci = cn;
+    kind = nkind;
+  }
+
+  // ---- epilogue: l across the two halves, normalise, store ----
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (!row_ok) return;
+  const float inv = 1.f / l_run;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + (((int64_t)it.b * a.num_q + t) * a.hq + it.hq) * D;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = 32 * mt + 8 * i4 + 4 * hf;
+      const uint2 w = uint2{pack_bf16x2(acc[mt][4 * i4] * inv, acc[mt][4 * i4 + 1] * inv),
+                            pack_bf16x2(acc[mt][4 * i4 + 2] * inv, acc[mt][4 * i4 + 3] * inv)};
+      *reinterpret_cast<uint2*>(orow + d) = w;
+    }
+  if (a.lse && hf == 0) a.lse[((int64_t)it.b * a.hq + it.hq) * a.num_q + t] = (m_run + __log2f(l_run)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// plan export: one workgroup enumerates the same schedule the kernels walk
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 256;
+
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillGeom geo, int32_t* tiles,
+                                                                    int32_t max_tiles, int32_t* num_tiles) {
+  __shared__ int32_t part[kPlanThreads];
+  const int tid = threadIdx.x;
+  const int32_t n_qt = pf_num_qtiles(geo);
+  const int32_t per = (n_qt + kPlanThreads - 1) / kPlanThreads;
+  const int32_t q0 = tid * per, q1 = q0 + per < n_qt ? q0 + per : n_qt;
+  int32_t cnt = 0;
+  for (int32_t qt = q0; qt < q1; ++qt) {
+    const TileRange tr = pf_tile_range(geo, qt);
+    for (int32_t kt = 0; kt < tr.n_prefix; ++kt) cnt += pf_classify(geo, qt, kt) != 0;
+    for (int32_t kt = tr.band_lo; kt <= tr.band_hi; ++kt) cnt += pf_classify(geo, qt, kt) != 0;
+  }
+  part[tid] = cnt;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int i = 0; i < kPlanThreads; ++i) {
+      const int32_t c = part[i];
+      part[i] = run;
+      run += c;
+    }
+    *num_tiles = run;
+  }
+  __syncthreads();
+  int32_t o = part[tid];
+  for (int32_t qt = q0; qt < q1; ++qt) {
+    const TileRange tr = pf_tile_range(geo, qt);
+    const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
+    for (int32_t ci = 0; ci < n_cand; ++ci) {
+      const int32_t kt = ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix);
+      const int kind = pf_classify(geo, qt, kt);
+      if (!kind) continue;
+      if (o < max_tiles) {
+        tiles[3 * (int64_t)o + 0] = qt;
+        tiles[3 * (int64_t)o + 1] = kt;
+        tiles[3 * (int64_t)o + 2] = kind;
+      }
+      ++o;
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+  {
+    int64_t blocks = (int64_t)a.batch * (nk_padded(a.num_k, a.bn) / 64);
+    blocks = blocks < 1 ? 1 : (blocks > 16384 ? 16384 : blocks);
+    hipLaunchKernelGGL((prefill_prep_kernel<T, D>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int32_t n_qt = (a.num_q + a.bm - 1) / a.bm;
+  const int64_t total = (int64_t)a.batch * a.hq * n_qt;
+  const dim3 grid((uint32_t)(((total + 7) / 8) * 8));
+  if (sizeof(T) == 2)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_f32_kernel<D>), grid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void prefill_tile_shape(int32_t dtype, int32_t head_dim, int32_t* bm, int32_t* bn) {
+  (void)head_dim;
+  if (dtype == PS_BF16) {
+    *bm = PfTraits<uint16_t>::BM;
+    *bn = PfTraits<uint16_t>::BN;
+  } else {
+    *bm = PfTraits<float>::BM;
+    *bn = PfTraits<float>::BN;
+  }
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  if (a.batch == 0 || a.num_q == 0) return hipSuccess;
+  if (a.dtype == PS_BF16)
+    return a.head_dim == 64 ? launch_prefill_t<uint16_t, 64>(a, stream) : launch_prefill_t<uint16_t, 128>(a, stream);
+  return a.head_dim == 64 ? launch_prefill_t<float, 64>(a, stream) : launch_prefill_t<float, 128>(a, stream);
+}
+
+hipError_t launch_prefill_plan(int32_t num_q, int32_t num_k, int32_t prefix_len, int32_t window,
+                               int64_t kv_start, int32_t bm, int32_t bn, int32_t* tiles, int32_t max_tiles,
+                               int32_t* num_tiles, hipStream_t stream) {
+  PrefillGeom geo{num_q, num_k, prefix_len, window, kv_start, bm, bn};
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, geo, tiles, max_tiles, num_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace ps

@@ -1,0 +1,77 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ps_common.h"
+
+namespace ps {
+
+struct AppendArgs {
+  CacheGeom geom;
+  int32_t dtype;  // ps_dtype
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const int32_t* prefix_len;
+  const int64_t* start_pos;
+  const int32_t* seq_tokens;
+  int32_t tokens_per_seq;
+  const void* k_new;
+  const void* v_new;
+  int32_t num_seqs;
+  int32_t* slot_pos;
+  RopeFreq rope;
+};
+
+struct DecodeArgs {
+  CacheGeom geom;
+  int32_t dtype;
+  int32_t hq;
+  int32_t group;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* prefix_len;
+  const int64_t* pos;
+  const void* q;
+  void* out;
+  int32_t num_seqs;
+  int32_t num_splits;
+  int32_t split_keys;     // keys per split, multiple of 32
+  float* part_o;          // [num_seqs][hq][num_splits][D] (unnormalised)
+  float* part_ml;         // [num_seqs][hq][num_splits][2]  (running max in log2 units, sum)
+  float scale_log2;       // softmax_scale * log2(e)
+  RopeFreq rope;
+};
+
+struct PrefillArgs {
+  int32_t dtype;
+  int32_t hq, hkv, group, head_dim;
+  int32_t window, prefix_len;
+  int64_t kv_start;
+  int32_t batch, num_q, num_k;
+  int32_t bm, bn;
+  const void* q;
+  const void* k;          // raw keys
+  const void* v;
+  void* out;
+  float* lse;
+  void* k_rot;            // workspace: rotated keys [batch][num_k][hkv][D]
+  float* rope_cs;         // workspace: [num_q][D/2][2] cos/sin of query positions
+  float scale_log2;
+  RopeFreq rope;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_plan(int32_t num_q, int32_t num_k, int32_t prefix_len, int32_t window,
+                               int64_t kv_start, int32_t bm, int32_t bn, int32_t* tiles,
+                               int32_t max_tiles, int32_t* num_tiles, hipStream_t stream);
+
+// Tile shape of the prefill kernels for a dtype / head_dim.
+void prefill_tile_shape(int32_t dtype, int32_t head_dim, int32_t* bm, int32_t* bn);
+
+}  // namespace ps

@@ -1,0 +1,217 @@
+/*
+ * prefix_sliding.h -- C ABI of the Prefix Sliding attention library (gfx950).
+ *
+ * Prefix Sliding: a query at absolute position p attends only to the pinned
+ * prefix [0, L) and to the last W tokens (p-W, p], causally.  Source: blog
+ * "Prefix Sliding 完全拆解" (pinghaoyang.com.cn), section
+ * "核心机制：注意力掩码上的两个区间" (the allowed set A(i), the cap
+ * L_total = L_prefix + W, warm-up, hidden tokens not kept).  Positions here
+ * are 0-indexed; W counts the query itself, so a sequence never holds more
+ * than L + W keys (100 + 4096 -> 4196, as the agihunt.info summary states).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer argument named *_cache, q, k, v, out, lse, workspace,
+ *    block_table, prefix_len, pos, start_pos, seq_tokens, slot_pos, tiles,
+ *    num_tiles is a DEVICE pointer.  Descriptors are HOST pointers, read
+ *    during the call only.
+ *  - The caller owns every buffer and the stream.  The library never
+ *    allocates, frees or synchronises; work is enqueued on `stream` and runs
+ *    asynchronously.  Calls on one stream run in order (append before the
+ *    decode that reads the token).
+ *  - Arguments the host can see are validated before anything is enqueued;
+ *    on failure nothing is launched, the status says why and
+ *    ps_last_error() returns a thread-local message.  Launch failures return
+ *    PS_HIP_ERROR.  Faults in asynchronous work surface at the caller's next
+ *    synchronisation.
+ *  - Per-sequence values that live on the device (prefix_len, pos,
+ *    start_pos, block_table entries) cannot be checked by the host.  A
+ *    sequence whose values are out of range (prefix_len < 0,
+ *    prefix_len + W > slot_capacity, pos < 0, a page id outside
+ *    [0, num_pages)) is never read or written out of bounds: its appends are
+ *    dropped and its decode output rows are set to NaN.
+ *  - The library keeps no mutable global state; calls are reentrant.
+ *
+ * KV cache layout (owned by the caller, defined here)
+ * ---------------------------------------------------
+ * The cache of one layer is a set of 64-slot REGIONS, one per
+ * (page or ring segment, KV head).  A region holds D*64 elements of K and
+ * D*64 elements of V (elements are bf16 or f32, per ps_attn_desc.dtype):
+ *    K region: row-major [64 slots][D]
+ *    V region: 8 blocks of 8 slots, each block d-major: [8][D][8]
+ *              (slot s, dim d at (s/8)*8*D + d*8 + s%8)
+ * V is stored this way so that 8 consecutive slots of one dimension are 16
+ * contiguous bytes: exactly one operand register of a bf16 MFMA that
+ * contracts over keys.
+ *  - Contiguous mode (page_size == 0): sequence s, KV head h, slot j lives in
+ *    region ((s*Hkv + h) * slot_capacity/64 + j/64); i.e. the K cache is
+ *    [num_seqs][Hkv][slot_capacity][D] and V is the same size.
+ *  - Paged mode (page_size == 64): slot j of sequence s lives in page
+ *    block_table[s*max_pages_per_seq + j/64]; page P, KV head h is region
+ *    (P*Hkv + h); i.e. the K pool is [num_pages][Hkv][64][D].
+ * Slots follow the ring map of Continue PE (blog section
+ * "位置编码：Reset PE 还是 Continue PE？": every token keeps its absolute
+ * position, cached keys are rotated once and reused):
+ *    slot(n) = n                         if n < L
+ *            = L + ((n - L) mod W)       otherwise,
+ * so appending position n overwrites position n - W, the token that has just
+ * left the window, and after warm-up slots [0, L+W) hold exactly A(p).  K is
+ * stored already rotated (RoPE at its absolute position); V is not rotated.
+ */
+#ifndef PREFIX_SLIDING_H
+#define PREFIX_SLIDING_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PS_ABI_VERSION 1
+
+typedef enum {
+  PS_OK = 0,
+  PS_INVALID_ARGUMENT = 1,
+  PS_UNSUPPORTED = 2,
+  PS_WORKSPACE_TOO_SMALL = 3,
+  PS_HIP_ERROR = 4
+} ps_status;
+
+typedef enum { PS_BF16 = 0, PS_F32 = 1 } ps_dtype;
+
+/* Attention geometry.
+ * num_q_heads % num_kv_heads == 0; query head h uses KV head
+ * h / (num_q_heads/num_kv_heads) (consecutive heads share a KV head);
+ * the group size must be <= 16.  head_dim is 64 or 128.
+ * rope_theta > 0: rotate-half RoPE with inverse frequencies
+ * rope_theta^(-2i/D), pairing dims (i, i + D/2), applied inside the library at
+ * absolute positions (angle formed in double precision); 0: inputs are already
+ * rotated.  softmax_scale > 0 multiplies q.k before the softmax. */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;            /* ps_dtype: element type of q, k, v, caches, out */
+  double rope_theta;
+  float softmax_scale;
+} ps_attn_desc;
+
+/* Cache geometry.  window = W >= 1.  page_size 0 (contiguous) or 64 (paged).
+ * slot_capacity: slots per (sequence, KV head), a multiple of 64; every
+ * sequence needs prefix_len + W <= slot_capacity.  Paged mode also needs
+ * max_pages_per_seq == slot_capacity/64 (row length of block_table) and
+ * num_pages (pages in the pool, bound for block_table entries). */
+typedef struct {
+  int32_t window;
+  int32_t page_size;
+  int32_t slot_capacity;
+  int32_t max_pages_per_seq;
+  int64_t num_pages;
+} ps_cache_desc;
+
+/* ps_kv_append -- write new tokens' K (rotated at their absolute position) and
+ * V into their ring slots.  Blog "Prefix Sliding 完全拆解", mask section (hidden
+ * tokens are not kept) and the Continue PE section (rotate once, reuse).
+ *   k_new, v_new : [num_seqs][tokens_per_seq][Hkv][D], dtype of attn, raw K.
+ *   start_pos    : [num_seqs] int64, absolute position of token 0.
+ *   seq_tokens   : [num_seqs] int32 tokens actually present per sequence
+ *                  (<= tokens_per_seq), or NULL for tokens_per_seq each.
+ *   prefix_len   : [num_seqs] int32 L of each sequence.
+ *   block_table  : paged mode [num_seqs][max_pages_per_seq] int32, else NULL.
+ *   slot_pos     : NULL, or [num_seqs][slot_capacity] int32 that receives the
+ *                  absolute position written into each slot (for checking).
+ * Within one call a token at position j is written only if j < L or
+ * j > p_last - W (p_last = the sequence's last position in the call): tokens
+ * that the same call would already evict are skipped, so no two writes of a
+ * call hit the same slot.  tokens_per_seq == 0 or num_seqs == 0 is a no-op. */
+ps_status ps_kv_append(const ps_attn_desc* attn, const ps_cache_desc* cache,
+                       void* k_cache, void* v_cache, const int32_t* block_table,
+                       const int32_t* prefix_len, const int64_t* start_pos,
+                       const int32_t* seq_tokens, int32_t tokens_per_seq,
+                       const void* k_new, const void* v_new, int32_t num_seqs,
+                       int32_t* slot_pos, hipStream_t stream);
+
+/* ps_decode_attn -- one decode query per sequence over its bounded cache.
+ * Blog "Prefix Sliding 完全拆解", mask section (A(i); the per-token cost is
+ * constant after warm-up) and section "Kernel 实现：两层级过滤" (only the
+ * prefix and the window are read).
+ *   q   : [num_seqs][Hq][D] raw (un-rotated) queries, dtype of attn.
+ *   pos : [num_seqs] int64 absolute query position p; the cache must already
+ *         hold position p (append first).  The query sees ring slots
+ *         [0, min(p+1, L+W)), which are exactly A(p).
+ *   out : [num_seqs][Hq][D], dtype of attn.
+ *   num_splits : key-range splits per (sequence, KV head); 0 picks one from
+ *         the device's CU count (ps_decode_num_splits).  Partial results are
+ *         merged in a fixed order, so results are bitwise reproducible for a
+ *         given split count.
+ *   workspace : device scratch of at least
+ *         ps_decode_workspace_size(attn, cache, num_seqs, num_splits) bytes. */
+ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache,
+                         const void* k_cache, const void* v_cache, const int32_t* block_table,
+                         const int32_t* prefix_len, const int64_t* pos,
+                         const void* q, void* out, int32_t num_seqs, int32_t num_splits,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Split count ps_decode_attn uses for num_splits == 0 (queries the current
+ * device; assumes 256 CUs when none is visible).  Returns >= 1, or 0 on
+ * invalid arguments. */
+int32_t ps_decode_num_splits(const ps_attn_desc* attn, const ps_cache_desc* cache, int32_t num_seqs);
+
+/* Workspace bytes ps_decode_attn needs (num_splits 0: automatic). */
+size_t ps_decode_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* cache,
+                                int32_t num_seqs, int32_t num_splits);
+
+/* ps_prefill_attn -- masked attention of a chunk of queries (truncated
+ * backprop forward / prefill).  Blog "Prefix Sliding 完全拆解", sections
+ * "Kernel 实现：两层级过滤" (tiles with no visible pair are skipped, element
+ * masks only on tiles that are partly visible) and
+ * "超长 rollouts 的反向传播：截断回传" (the trainer sees a chunk of the
+ * trace behind the prefix).
+ *   k, v : [batch][num_keys][Hkv][D] raw keys/values; key k has absolute
+ *          position k for k < prefix_len and kv_start + (k - prefix_len)
+ *          otherwise (kv_start >= prefix_len).
+ *   q    : [batch][num_queries][Hq][D] raw queries; query t is key
+ *          num_keys - num_queries + t (same position).  If the queries reach
+ *          into the prefix (num_queries > num_keys - prefix_len), kv_start
+ *          must equal prefix_len.
+ *   out  : [batch][num_queries][Hq][D], dtype of attn.
+ *   lse  : NULL or [batch][Hq][num_queries] float, natural-log sum of
+ *          exp(scaled masked scores) per query row.
+ *   workspace : >= ps_prefill_workspace_size(...) bytes (rotated keys and a
+ *          rotation table for the query positions). */
+ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t prefix_len,
+                          int64_t kv_start, const void* q, const void* k, const void* v,
+                          int32_t batch, int32_t num_queries, int32_t num_keys,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+size_t ps_prefill_workspace_size(const ps_attn_desc* attn, int32_t batch, int32_t num_queries,
+                                 int32_t num_keys);
+
+/* Tile shape (BM queries x BN keys) ps_prefill_attn uses for this geometry. */
+ps_status ps_prefill_tile_shape(const ps_attn_desc* attn, int32_t* block_m, int32_t* block_n);
+
+/* ps_prefill_plan -- the tile list ps_prefill_attn executes, for checking.
+ * Every (q_tile, k_tile) of the BM x BN grid holding at least one visible
+ * (query, key) pair, sorted by q_tile then k_tile, as int32 triples
+ * (q_tile, k_tile, kind) with kind 1 = every pair of the full BM x BN tile
+ * exists and is visible (no element mask), 2 = partial (masked).  tiles is
+ * [max_tiles][3]; *num_tiles receives the total count even when it exceeds
+ * max_tiles (then only max_tiles triples are written).  Same geometry rules
+ * as ps_prefill_attn. */
+ps_status ps_prefill_plan(const ps_attn_desc* attn, int32_t window, int32_t prefix_len,
+                          int64_t kv_start, int32_t num_queries, int32_t num_keys,
+                          int32_t* tiles, int32_t max_tiles, int32_t* num_tiles,
+                          hipStream_t stream);
+
+const char* ps_last_error(void);
+const char* ps_status_string(ps_status status);
+int32_t ps_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PREFIX_SLIDING_H */

@@ -1,0 +1,36 @@
+// Host build of the library's prefill tile scheduler (ps_sched.h, compiled with
+// g++), so the CPU tests can compare the closed-form schedule with the oracle's
+// element enumeration without a GPU.
+#include "ps_sched.h"
+
+extern "C" int ps_host_plan(int T, int Nk, int L, int W, long long kv_start, int bm, int bn, int* tiles,
+                            int max_tiles) {
+  ps::PrefillGeom g{T, Nk, L, W, kv_start, bm, bn};
+  int n = 0;
+  const int nqt = ps::pf_num_qtiles(g);
+  for (int qt = 0; qt < nqt; ++qt) {
+    const ps::TileRange r = ps::pf_tile_range(g, qt);
+    const int ncand = r.n_prefix + (r.band_hi >= r.band_lo ? r.band_hi - r.band_lo + 1 : 0);
+    for (int ci = 0; ci < ncand; ++ci) {
+      const int kt = ci < r.n_prefix ? ci : r.band_lo + (ci - r.n_prefix);
+      const int kind = ps::pf_classify(g, qt, kt);
+      if (!kind) continue;
+      if (n < max_tiles) {
+        tiles[3 * n] = qt;
+        tiles[3 * n + 1] = kt;
+        tiles[3 * n + 2] = kind;
+      }
+      ++n;
+    }
+  }
+  return n;
+}
+
+extern "C" int ps_host_classify_all(int T, int Nk, int L, int W, long long kv_start, int bm, int bn, int* kinds) {
+  ps::PrefillGeom g{T, Nk, L, W, kv_start, bm, bn};
+  const int nqt = ps::pf_num_qtiles(g), nkt = ps::pf_num_ktiles(g);
+  for (int qt = 0; qt < nqt; ++qt)
+    for (int kt = 0; kt < nkt; ++kt) kinds[qt * nkt + kt] = ps::pf_classify(g, qt, kt);
+  return nqt * nkt;
+}
+

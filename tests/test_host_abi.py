@@ -1,0 +1,186 @@
+"""CPU tests of the native library's host side: it loads, exports every symbol
+the header declares, validates arguments before launching anything, sizes
+workspaces, and its prefill tile scheduler (compiled for the host) agrees with
+the oracle's element enumeration."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prefix_sliding.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bounded_kv_cache_amd import _lib
+    return _lib.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    text = open(HEADER).read()
+    names = sorted(set(re.findall(r"\b(ps_[a-z_0-9]+)\s*\(", text)))
+    assert "ps_kv_append" in names and "ps_decode_attn" in names and "ps_prefill_attn" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "bounded_kv_cache_amd",
+                                                                      "libprefix_sliding.so")],
+                         capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, re.M), f"{n} not exported with C linkage"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.ps_abi_version() == 1
+    assert lib.ps_status_string(0) == b"ok"
+    assert lib.ps_status_string(3) == b"workspace too small"
+
+
+def _descs(hq=16, hkv=2, d=128, dtype=0, theta=10000.0, scale=0.0884, window=4096, page=0, cap=4224, mp=0, npages=0):
+    from bounded_kv_cache_amd import _lib
+    return (_lib.AttnDesc(hq, hkv, d, dtype, theta, scale), _lib.CacheDesc(window, page, cap, mp, npages))
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("mut,status", [
+    (dict(hq=15), 1), (dict(hkv=0), 1), (dict(hq=34, hkv=2), 2), (dict(d=96), 2), (dict(dtype=7), 2),
+    (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(theta=-1.0), 1), (dict(theta=0.5), 1),
+    (dict(window=0), 1), (dict(page=32), 2), (dict(cap=100), 1), (dict(page=64, cap=4224, mp=10, npages=5), 1),
+    (dict(page=64, cap=4224, mp=66, npages=0), 1),
+])
+def test_decode_validation(lib, mut, status):
+    a, c = _descs(**mut)
+    st = lib.ps_decode_attn(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1,
+                            None, 0, None)
+    assert st == status, lib.ps_last_error()
+    assert lib.ps_last_error()
+
+
+def test_decode_null_pointers_and_workspace(lib):
+    a, c = _descs()
+    assert lib.ps_decode_attn(ctypes.byref(a), ctypes.byref(c), None, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 1,
+                              None, 0, None) == 1
+    # paged mode without a block table
+    a, c = _descs(page=64, mp=66, npages=100)
+    assert lib.ps_decode_attn(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 1,
+                              None, 0, None) == 1
+    a, c = _descs()
+    need = lib.ps_decode_workspace_size(ctypes.byref(a), ctypes.byref(c), 4, 3)
+    assert need == 4 * 16 * 3 * (128 + 2) * 4
+    assert lib.ps_decode_workspace_size(ctypes.byref(a), ctypes.byref(c), 4, 1) == 0
+    assert lib.ps_decode_attn(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 3,
+                              FAKE, need - 1, None) == 3
+    assert "workspace" in lib.ps_last_error().decode()
+    # too many splits for the capacity
+    assert lib.ps_decode_attn(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 500,
+                              FAKE, 1 << 40, None) == 1
+    # no sequences: nothing to do
+    assert lib.ps_decode_attn(ctypes.byref(a), ctypes.byref(c), None, None, None, None, None, None, None, 0, 1,
+                              None, 0, None) == 0
+
+
+def test_append_validation(lib):
+    a, c = _descs()
+    assert lib.ps_kv_append(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, None, -1, FAKE, FAKE,
+                            2, None, None) == 1
+    assert lib.ps_kv_append(ctypes.byref(a), ctypes.byref(c), FAKE, None, None, FAKE, FAKE, None, 1, FAKE, FAKE,
+                            2, None, None) == 1
+    assert lib.ps_kv_append(ctypes.byref(a), ctypes.byref(c), None, None, None, None, None, None, 0, None, None,
+                            2, None, None) == 0
+    a, c = _descs(window=-3)
+    assert lib.ps_kv_append(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, None, 1, FAKE, FAKE,
+                            2, None, None) == 1
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 0, 0, 1, 8, 8), 1),        # window 0
+    ((4, -1, 0, 1, 8, 8), 1),       # negative prefix
+    ((4, 9, 9, 1, 8, 8), 1),        # prefix longer than the key array
+    ((4, 4, 2, 1, 8, 8), 1),        # kv_start before the end of the prefix
+    ((4, 2, 2, 1, 9, 8), 1),        # more queries than keys
+    ((4, 2, 5, 1, 8, 8), 1),        # queries reach into the prefix but positions are not contiguous
+])
+def test_prefill_validation(lib, args, status):
+    a, _ = _descs()
+    w, L, start, b, t, nk = args
+    st = lib.ps_prefill_attn(ctypes.byref(a), w, L, start, FAKE, FAKE, FAKE, b, t, nk, FAKE, None, FAKE, 1 << 40,
+                             None)
+    assert st == status, lib.ps_last_error()
+    st = lib.ps_prefill_plan(ctypes.byref(a), w, L, start, t, nk, FAKE, 10, FAKE, None)
+    assert st == status
+
+
+def test_prefill_workspace_and_tiles(lib):
+    a, _ = _descs(hq=28, hkv=4)
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.ps_prefill_tile_shape(ctypes.byref(a), ctypes.byref(bm), ctypes.byref(bn)) == 0
+    assert (bm.value, bn.value) == (128, 64)
+    need = lib.ps_prefill_workspace_size(ctypes.byref(a), 8, 8192, 8292)
+    nkp = -(-8292 // 64) * 64
+    assert need == (2 * 8 * 4 * nkp * 128 * 2 + 255) // 256 * 256 + 8192 * 64 * 2 * 4
+    assert lib.ps_prefill_attn(ctypes.byref(a), 2048, 100, 98304, FAKE, FAKE, FAKE, 8, 8192, 8292, FAKE, None,
+                               FAKE, need - 1, None) == 3
+
+
+# ---------------------------------------------------------------- scheduler (host build) vs oracle
+@pytest.fixture(scope="module")
+def sched():
+    tmp = tempfile.mkdtemp(prefix="ps_sched_")
+    so = os.path.join(tmp, "sched_host.so")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-I",
+                    os.path.join(ROOT, "bounded_kv_cache_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "host", "sched_host.cpp"), "-o", so], check=True)
+    lib = ctypes.CDLL(so)
+    lib.ps_host_plan.restype = ctypes.c_int
+    lib.ps_host_plan.argtypes = [ctypes.c_int] * 4 + [ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                                      ctypes.c_void_p, ctypes.c_int]
+    return lib
+
+
+def _host_plan(sched, T, Nk, L, W, start, bm, bn):
+    n = sched.ps_host_plan(T, Nk, L, W, start, bm, bn, None, 0)
+    buf = np.zeros((max(n, 1), 3), dtype=np.int32)
+    sched.ps_host_plan(T, Nk, L, W, start, bm, bn, buf.ctypes.data, n)
+    return [tuple(int(x) for x in r) for r in buf[:n]]
+
+
+def test_scheduler_matches_oracle_golden(sched):
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "tile_plan_small.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        got = _host_plan(sched, c["T"], c["Nk"], c["L"], c["W"], c["kv_start"], c["BM"], c["BN"])
+        assert got == oracle.tile_plan(c["T"], c["Nk"], c["L"], c["W"], c["kv_start"], c["BM"], c["BN"])
+
+
+def test_scheduler_matches_oracle_random(sched):
+    rs = np.random.default_rng(0)
+    for _ in range(300):
+        bm, bn = [(128, 64), (64, 64), (4, 4), (2, 3), (16, 8)][rs.integers(5)]
+        L = int(rs.integers(0, 40))
+        chunk = int(rs.integers(1, 200))
+        nk = L + chunk
+        contiguous = rs.random() < 0.4
+        if contiguous:
+            start = L
+            T = int(rs.integers(1, nk + 1))
+        else:
+            start = L + int(rs.integers(0, 500))
+            T = int(rs.integers(1, chunk + 1))
+        W = int(rs.integers(1, 300))
+        got = _host_plan(sched, T, nk, L, W, start, bm, bn)
+        want = oracle.tile_plan(T, nk, L, W, start, bm, bn)
+        assert got == want, (T, nk, L, W, start, bm, bn)
+
+
+def test_scheduler_matches_oracle_truncated_backprop_shape(sched):
+    got = _host_plan(sched, 8192, 8292, 100, 2048, 98304, 128, 64)
+    assert got == oracle.tile_plan(8192, 8292, 100, 2048, 98304, 128, 64)
