@@ -1,0 +1,380 @@
+#!/usr/bin/env python3
+"""Benchmark of the Prefix Sliding hot path on one MI355X.
+
+Workload (default): decode at position 131072 with a 100-token prefix and a
+4096-token window -- 256 sequences, 28 layers, Hq=16, Hkv=2, head_dim=128,
+bf16 (a Qwen3-1.7B attention geometry).  One step = for every layer, append
+the new token's K/V (RoPE at its absolute position) into the ring and run
+split-KV decode attention over the ring.  Timed: K steps after W warm-up
+steps, inputs resident in HBM, positions advancing by one per step.
+
+Printed (one JSON line): whole-job decode tok/s, the roofline of the decode
+attention kernel (algorithmic HBM bytes per launch / average launch time,
+against 8 TB/s), the float64 CPU oracle timed on a bounded sample of the
+same workload, the masked prefill kernel (truncated-backprop chunk: 8 x 8192
+queries behind a 100-token prefix, W=2048, Hq=28, Hkv=4) in TFLOP/s against
+the 2.5 PFLOP/s bf16 MFMA peak, and the full-attention decode comparator at
+the same position.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "prefix-sliding decode-attn tok/s & HBM GB/s %peak, W=4096 @128K pos"
+COUNTERS = os.path.join(ROOT, "profiles", "decode_bf16_128k_w4096_counters.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--window", type=int, default=4096)
+    ap.add_argument("--position", type=int, default=131072)
+    ap.add_argument("--num-seqs", type=int, default=256)
+    ap.add_argument("--layers", type=int, default=28)
+    ap.add_argument("--splits", type=int, default=0, help="decode splits (0: library's automatic choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-full", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--sweep", action="store_true", help="also time decode at a sweep of positions (flatness)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "ps_common.h", "ps_internal.h"):
+        with open(os.path.join(ROOT, "bounded_kv_cache_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------------- decode
+class DecodeBench:
+    def __init__(self, ps, torch, num_seqs, layers, window, prefix, position, splits, pool=16, seed=0):
+        self.ps, self.torch = ps, torch
+        self.n, self.layers, self.splits = num_seqs, layers, splits
+        self.attn = ps.AttnSpec(16, 2, 128, ps.PS_BF16, 10000.0, 1 / math.sqrt(128))
+        cap = -(-min(prefix + window, position + 4096) // 64) * 64
+        self.cache = ps.CacheSpec(window=window, slot_capacity=cap)
+        self.prefix, self.position, self.window = prefix, position, window
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        ks, vs = ps.cache_shapes(self.attn, self.cache, num_seqs)
+        self.k = [torch.empty(ks, dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+        self.v = [torch.empty(vs, dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+        self.pl = torch.full((num_seqs,), prefix, dtype=torch.int32, device="cuda")
+        # rings hold A(position - 1): prefix tokens, then the last window tokens, appended in bulk
+        n_pre = min(prefix, position)
+        w_start = max(prefix, position - window)
+        n_win = position - w_start
+        chunk = max(n_pre, n_win, 1)
+        kn = (torch.randn((num_seqs, chunk, 2, 128), generator=g, device="cuda") * 0.5).bfloat16()
+        vn = (torch.randn((num_seqs, chunk, 2, 128), generator=g, device="cuda") * 0.5).bfloat16()
+        for li in range(layers):
+            if n_pre:
+                ps.ps_kv_append(self.attn, self.cache, self.k[li], self.v[li], self.pl,
+                                torch.zeros(num_seqs, dtype=torch.int64, device="cuda"),
+                                kn[:, :n_pre].contiguous(), vn[:, :n_pre].contiguous())
+            if n_win:
+                ps.ps_kv_append(self.attn, self.cache, self.k[li], self.v[li], self.pl,
+                                torch.full((num_seqs,), w_start, dtype=torch.int64, device="cuda"),
+                                kn[:, :n_win].contiguous(), vn[:, :n_win].contiguous())
+        del kn, vn
+        self.pool = pool
+        self.q = [torch.randn((num_seqs, 16, 128), generator=g, device="cuda").bfloat16() for _ in range(pool)]
+        self.kn = [(torch.randn((num_seqs, 1, 2, 128), generator=g, device="cuda") * 0.5).bfloat16()
+                   for _ in range(pool)]
+        self.vn = [(torch.randn((num_seqs, 1, 2, 128), generator=g, device="cuda") * 0.5).bfloat16()
+                   for _ in range(pool)]
+        self.out = torch.empty((num_seqs, 16, 128), dtype=torch.bfloat16, device="cuda")
+        ws = ps.ps_decode_workspace_size(self.attn, self.cache, num_seqs, splits)
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+        self.max_steps = 0
+        self.pos = None
+
+    def prepare_positions(self, total_steps):
+        t = self.torch
+        self.pos = [t.full((self.n,), self.position + s, dtype=t.int64, device="cuda") for s in range(total_steps)]
+
+    def step(self, s):
+        ps = self.ps
+        pos = self.pos[s]
+        for li in range(self.layers):
+            i = (s * self.layers + li) % self.pool
+            ps.ps_kv_append(self.attn, self.cache, self.k[li], self.v[li], self.pl, pos, self.kn[i], self.vn[i])
+            ps.ps_decode_attn(self.attn, self.cache, self.k[li], self.v[li], self.pl, pos, self.q[i], self.out,
+                              num_splits=self.splits, workspace=self.ws)
+
+    def decode_only(self, reps, pos):
+        ps = self.ps
+        for r in range(reps):
+            ps.ps_decode_attn(self.attn, self.cache, self.k[0], self.v[0], self.pl, pos, self.q[r % self.pool],
+                              self.out, num_splits=self.splits, workspace=self.ws)
+
+    def n_vis(self, p):
+        return min(p + 1, self.prefix + self.window)
+
+    def kernel_bytes(self, p):
+        """Algorithmic HBM bytes of one decode-attention launch (one layer): the
+        visible K/V rows, the queries and the outputs."""
+        return self.n * (self.n_vis(p) * 2 * 128 * 2 * 2 + 16 * 128 * 2 * 2)
+
+    def release(self):
+        self.k.clear()
+        self.v.clear()
+
+
+def timed(torch, fn, iters):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    fn(iters)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1000.0
+
+
+def run_decode(ps, torch, args):
+    bench = DecodeBench(ps, torch, args.num_seqs, args.layers, args.window, 100, args.position, args.splits)
+    bench.prepare_positions(args.warmup + args.steps)
+    splits = args.splits or ps.ps_decode_num_splits(bench.attn, bench.cache, args.num_seqs)
+    for s in range(args.warmup):
+        bench.step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(args.warmup, args.warmup + args.steps):
+        bench.step(s)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = start.elapsed_time(end) / 1000.0
+    elapsed = max(wall, gpu_s)
+    # dominant kernel: decode attention of one layer, back to back, HIP events on the launch stream
+    p_last = args.position + args.warmup + args.steps - 1
+    pos = bench.pos[-1]
+    bench.decode_only(5, pos)
+    kt = timed(torch, lambda n: bench.decode_only(n, pos), args.kernel_reps) / args.kernel_reps
+    kbytes = bench.kernel_bytes(p_last)
+    res = {
+        "tok_s": args.num_seqs * args.steps / elapsed,
+        "ms_per_step": elapsed / args.steps * 1000.0,
+        "splits": splits,
+        "kernel_s": kt,
+        "kernel_bytes": kbytes,
+        "n_vis": bench.n_vis(p_last),
+    }
+    sweep = []
+    if args.sweep:
+        for p in (1024, 2048, 4196, 8192, 16384, 32768, 65536, 131072, 262144):
+            pt = torch.full((args.num_seqs,), p, dtype=torch.int64, device="cuda")
+            if bench.n_vis(p) > bench.cache.slot_capacity:
+                continue
+            kt_p = timed(torch, lambda n: bench.decode_only(n, pt), 20) / 20
+            sweep.append({"position": p, "n_vis": bench.n_vis(p), "us_per_layer": kt_p * 1e6,
+                          "tok_s": args.num_seqs / (kt_p * args.layers)})
+    bench.release()
+    del bench
+    torch.cuda.empty_cache()
+    return res, sweep
+
+
+def run_full_attention(ps, torch, args, steps=2):
+    """Full-attention comparator at the same position: the same decode kernel
+    with W >= n over a linear cache of the whole history.  One layer's buffer
+    (34 GB at 256 x 131073 slots) is launched once per layer."""
+    n, p = args.num_seqs, args.position
+    attn = ps.AttnSpec(16, 2, 128, ps.PS_BF16, 10000.0, 1 / math.sqrt(128))
+    cap = -(-(p + steps + 1) // 64) * 64
+    cache = ps.CacheSpec(window=1 << 30, slot_capacity=cap)
+    ks, vs = ps.cache_shapes(attn, cache, n)
+    k = torch.empty(ks, dtype=torch.bfloat16, device="cuda")
+    v = torch.empty(vs, dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    k.normal_(0.0, 0.5, generator=g)
+    v.normal_(0.0, 0.5, generator=g)
+    pl = torch.zeros(n, dtype=torch.int32, device="cuda")
+    q = torch.randn((n, 16, 128), generator=g, device="cuda").bfloat16()
+    kn = (torch.randn((n, 1, 2, 128), generator=g, device="cuda") * 0.5).bfloat16()
+    vn = (torch.randn((n, 1, 2, 128), generator=g, device="cuda") * 0.5).bfloat16()
+    out = torch.empty((n, 16, 128), dtype=torch.bfloat16, device="cuda")
+    splits = ps.ps_decode_num_splits(attn, cache, n)
+    ws = torch.empty(max(ps.ps_decode_workspace_size(attn, cache, n, 0), 1), dtype=torch.uint8, device="cuda")
+    pos = [torch.full((n,), p + s, dtype=torch.int64, device="cuda") for s in range(steps + 1)]
+
+    def one_step(s):
+        for _ in range(args.layers):
+            ps.ps_kv_append(attn, cache, k, v, pl, pos[s], kn, vn)
+            ps.ps_decode_attn(attn, cache, k, v, pl, pos[s], q, out, workspace=ws)
+
+    one_step(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(1, steps + 1):
+        one_step(s)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    nbytes = n * ((p + steps) * 2 * 128 * 2 * 2 + 16 * 128 * 4)
+    del k, v
+    torch.cuda.empty_cache()
+    return {"tok_s": n * steps / el, "ms_per_step": el / steps * 1e3, "position": p, "splits": splits,
+            "hbm_gbs": nbytes * args.layers * steps / el / 1e9}
+
+
+# ------------------------------------------------------------------------- prefill
+def run_prefill(ps, torch, reps=10, full_causal=True):
+    import synth
+    out = {}
+    for cfg in ([synth.C4_PREFILL, synth.C4_PREFILL_FULL] if full_causal else [synth.C4_PREFILL]):
+        attn = ps.AttnSpec(cfg.hq, cfg.hkv, cfg.dim, ps.PS_BF16, cfg.rope_theta, 1 / math.sqrt(cfg.dim))
+        g = torch.Generator(device="cuda").manual_seed(11)
+        q = torch.randn((cfg.batch, cfg.queries, cfg.hq, cfg.dim), generator=g, device="cuda").bfloat16()
+        k = torch.randn((cfg.batch, cfg.nk, cfg.hkv, cfg.dim), generator=g, device="cuda").bfloat16()
+        v = torch.randn((cfg.batch, cfg.nk, cfg.hkv, cfg.dim), generator=g, device="cuda").bfloat16()
+        o = torch.empty_like(q)
+        ws = torch.empty(ps.ps_prefill_workspace_size(attn, cfg.batch, cfg.queries, cfg.nk), dtype=torch.uint8,
+                         device="cuda")
+        r = reps if cfg is synth.C4_PREFILL else 2
+        ps.ps_prefill_attn(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, o, workspace=ws)
+        t = timed(torch, lambda n: [ps.ps_prefill_attn(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, o,
+                                                       workspace=ws) for _ in range(n)], r) / r
+        if cfg is synth.C4_PREFILL:   # every query sees the prefix and min(t+1, W) chunk keys
+            pairs = cfg.prefix * cfg.queries + sum(min(t_ + 1, cfg.window) for t_ in range(cfg.queries))
+        else:                         # full causal: query t sits at position Nk - T + t
+            pairs = sum(cfg.nk - cfg.queries + t_ + 1 for t_ in range(cfg.queries))
+        flops = 4.0 * cfg.dim * pairs * cfg.batch * cfg.hq
+        out[cfg.name] = {"ms": t * 1e3, "tflops": flops / t / 1e12, "useful_tflop": flops / 1e12,
+                         "mfma_frac": flops / t / 1e12 / BF16_PEAK_TFLOPS}
+        del q, k, v, o, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------------------------- CPU oracle
+def _oracle_worker(args):
+    idx, position, prefix, window, reps = args
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    import synth
+    k = synth.history(0, 3, synth.T_K, idx, 0, 0, position + 1, 2, 128, 0.5, "bf16")
+    v = synth.history(0, 3, synth.T_V, idx, 0, 0, position + 1, 2, 128, 0.5, "bf16")
+    qs = [synth.query(0, 3, idx, 0, r, 16, 128, 1.0, "bf16") for r in range(reps)]
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for q in qs:
+            oracle.decode_attention(q, k, v, position, prefix, window, 1 / math.sqrt(128), 10000.0)
+        el = time.perf_counter() - t0
+    return reps, el
+
+
+def run_cpu_baseline(args):
+    import concurrent.futures
+    import multiprocessing
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    reps = 2
+    jobs = [(i, args.position, 100, args.window, reps) for i in range(cores)]
+    ctx = multiprocessing.get_context("spawn")
+    with concurrent.futures.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
+        res = list(ex.map(_oracle_worker, jobs))
+    tuples = sum(r[0] for r in res)
+    slowest = max(r[1] for r in res)
+    tok_s = tuples / slowest / args.layers
+    return {"value": tok_s, "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"{tuples} (sequence, layer) decode tuples at position {args.position} over the full "
+                      f"un-evicted history, {cores} worker processes x 1 BLAS thread, {reps} tuples each; "
+                      f"tok/s = tuples / slowest worker's oracle time / {args.layers} layers",
+            "cpu_seconds": sum(r[1] for r in res)}
+
+
+def load_traffic(kernel_bytes):
+    """HBM traffic per launch from the committed counter summary, if it was
+    taken on the current kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except OSError:
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU sharding is "
+                                   "described in DESIGN.md, not implemented)"}))
+        sys.exit(2)
+    # the CPU oracle's worker processes start before anything initialises the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = run_cpu_baseline(args)
+        print(f"[bench] cpu oracle done: {cpu['value']:.3f} tok/s on {cpu['cores']} cores", file=sys.stderr,
+              flush=True)
+    import torch
+    import bounded_kv_cache_amd as ps
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    print(f"[bench] decode: {args.num_seqs} seqs x {args.layers} layers @ {args.position}, W={args.window}",
+          file=sys.stderr, flush=True)
+    dec, sweep = run_decode(ps, torch, args)
+    print(f"[bench] decode done: {dec['tok_s']:.0f} tok/s, kernel {dec['kernel_s'] * 1e6:.1f} us",
+          file=sys.stderr, flush=True)
+    prefill = None
+    if not args.no_prefill:
+        prefill = run_prefill(ps, torch)
+        print(f"[bench] prefill done: {prefill}", file=sys.stderr, flush=True)
+    full = None
+    if not args.no_full:
+        full = run_full_attention(ps, torch, args)
+        print(f"[bench] full attention done: {full['tok_s']:.0f} tok/s", file=sys.stderr, flush=True)
+    achieved = dec["kernel_bytes"] / dec["kernel_s"] / 1e9
+    line = {
+        "metric": METRIC,
+        "value": dec["tok_s"],
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode-{args.position}-w{args.window}", "num_seqs": args.num_seqs,
+                   "layers": args.layers, "position": args.position, "prefix": 100, "window": args.window,
+                   "hq": 16, "hkv": 2, "head_dim": 128, "splits": dec["splits"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(dec["kernel_bytes"]),
+                     "kernel": "decode_bf16_kernel", "kernel_us": dec["kernel_s"] * 1e6,
+                     "bytes_per_launch": dec["kernel_bytes"]},
+        "cpu_baseline": cpu,
+        "prefill": prefill,
+        "full_attention": full,
+    }
+    if sweep:
+        line["sweep"] = sweep
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -24,12 +24,13 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const CacheGeom& g = a.geom;
   const int32_t L = a.prefix_len[s];
   const int64_t start = a.start_pos[s];
-  if (L < 0 || (int64_t)L + g.window > g.slot_capacity || start < 0) return;  // invalid sequence: dropped
+  if (L < 0 || start < 0) return;  // invalid sequence: dropped
   const int64_t j = start + t;
   const int64_t last = start + n_tok - 1;
   // a token this same call would already evict is skipped (no two writes per slot)
   if (!(j < L || j > last - g.window)) return;
   const int32_t slot = ring_slot(j, L, g.window);
+  if (slot >= g.slot_capacity) return;  // the ring is too small for this position: dropped
   const int32_t D = g.head_dim;
   const int32_t half = D >> 1;
   const T* kn = static_cast<const T*>(a.k_new) + ((int64_t)s * a.tokens_per_seq + t) * g.hkv * D;

@@ -61,9 +61,10 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
 
   const int32_t L = a.prefix_len[s];
   const int64_t pos = a.pos[s];
-  bool bad = L < 0 || (int64_t)L + geo.window > geo.slot_capacity || pos < 0;
-  const int64_t nvis64 = bad ? 0 : (pos + 1 < (int64_t)L + geo.window ? pos + 1 : (int64_t)L + geo.window);
-  const int nvis = (int)nvis64;
+  // visible keys = ring slots [0, min(p+1, L+W)); every one must exist
+  const int64_t nvis64 = pos + 1 < (int64_t)L + geo.window ? pos + 1 : (int64_t)L + geo.window;
+  bool bad = L < 0 || pos < 0 || nvis64 > geo.slot_capacity;
+  const int nvis = bad ? 0 : (int)nvis64;
   const int kb = split * a.split_keys;
   const int ke = kb + a.split_keys < nvis ? kb + a.split_keys : nvis;
 
@@ -297,8 +298,9 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 
   const int32_t L = a.prefix_len[s];
   const int64_t pos = a.pos[s];
-  const bool seq_bad = L < 0 || (int64_t)L + geo.window > geo.slot_capacity || pos < 0;
-  const int nvis = seq_bad ? 0 : (int)(pos + 1 < (int64_t)L + geo.window ? pos + 1 : (int64_t)L + geo.window);
+  const int64_t nvis64 = pos + 1 < (int64_t)L + geo.window ? pos + 1 : (int64_t)L + geo.window;
+  const bool seq_bad = L < 0 || pos < 0 || nvis64 > geo.slot_capacity;
+  const int nvis = seq_bad ? 0 : (int)nvis64;
   const int kb = split * a.split_keys;
   const int ke = kb + a.split_keys < nvis ? kb + a.split_keys : nvis;
 

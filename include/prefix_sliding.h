@@ -26,10 +26,13 @@
  *    synchronisation.
  *  - Per-sequence values that live on the device (prefix_len, pos,
  *    start_pos, block_table entries) cannot be checked by the host.  A
- *    sequence whose values are out of range (prefix_len < 0,
- *    prefix_len + W > slot_capacity, pos < 0, a page id outside
- *    [0, num_pages)) is never read or written out of bounds: its appends are
- *    dropped and its decode output rows are set to NaN.
+ *    sequence whose values are out of range (prefix_len < 0, a position < 0,
+ *    a slot at or beyond slot_capacity -- i.e. min(p+1, L+W) > slot_capacity
+ *    -- or a page id outside [0, num_pages)) is never read or written out of
+ *    bounds: such appends are dropped and its decode output rows are NaN.
+ *    A ring of L + W <= slot_capacity slots serves any position; a window
+ *    wider than the capacity (the full-attention comparator, W >= n) works
+ *    while the sequence is shorter than the capacity.
  *  - The library keeps no mutable global state; calls are reentrant.
  *
  * KV cache layout (owned by the caller, defined here)
@@ -99,8 +102,8 @@ typedef struct {
 } ps_attn_desc;
 
 /* Cache geometry.  window = W >= 1.  page_size 0 (contiguous) or 64 (paged).
- * slot_capacity: slots per (sequence, KV head), a multiple of 64; every
- * sequence needs prefix_len + W <= slot_capacity.  Paged mode also needs
+ * slot_capacity: slots per (sequence, KV head), a multiple of 64; a
+ * sequence at position p uses slots [0, min(p+1, prefix_len + W)).  Paged mode also needs
  * max_pages_per_seq == slot_capacity/64 (row length of block_table) and
  * num_pages (pages in the pool, bound for block_table entries). */
 typedef struct {

@@ -81,3 +81,30 @@ def fill_ring(ps, attn, cache, k_cache, v_cache, prefix_len, p_before, k_hist, v
                         to_dev(kn, dt), to_dev(vn, dt), block_table=block_table,
                         seq_tokens=torch.tensor(np.asarray(counts, dtype=np.int32), device="cuda"),
                         slot_pos=slot_pos)
+
+
+def fill_rings_sampled(ps, attn, cache, k_cache, v_cache, prefix_len, p_before, sampled, block_table=None, seed=0):
+    """Like fill_ring for a large batch: every sequence's ring receives
+    A(p_before[s]); sequences in ``sampled`` (dict s -> (k_hist, v_hist) raw
+    arrays) get those exact values, all others seeded device-side random
+    values (never compared).  Uses two bulk appends with per-sequence counts."""
+    n = len(prefix_len)
+    hkv, d, dt = attn.num_kv_heads, attn.head_dim, attn.torch_dtype
+    pre_cnt = np.array([max(0, min(int(prefix_len[s]), int(p_before[s]) + 1)) for s in range(n)], dtype=np.int32)
+    win_start = np.array([max(int(prefix_len[s]), int(p_before[s]) - cache.window + 1) for s in range(n)],
+                         dtype=np.int64)
+    win_cnt = np.array([max(0, int(p_before[s]) - int(win_start[s]) + 1) for s in range(n)], dtype=np.int32)
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    pl = torch.tensor(np.asarray(prefix_len, dtype=np.int32), device="cuda")
+    for starts, counts in ((np.zeros(n, dtype=np.int64), pre_cnt), (win_start, win_cnt)):
+        t = int(max(int(counts.max()), 1))
+        kn = (torch.randn((n, t, hkv, d), generator=gen, device="cuda") * 0.5).to(dt)
+        vn = (torch.randn((n, t, hkv, d), generator=gen, device="cuda") * 0.5).to(dt)
+        for s, (kh, vh) in sampled.items():
+            c = int(counts[s])
+            if c:
+                kn[s, :c] = to_dev(kh[starts[s]:starts[s] + c], dt)
+                vn[s, :c] = to_dev(vh[starts[s]:starts[s] + c], dt)
+        ps.ps_kv_append(attn, cache, k_cache, v_cache, pl, torch.tensor(starts, device="cuda"), kn, vn,
+                        block_table=block_table, seq_tokens=torch.tensor(counts, device="cuda"))
+        del kn, vn

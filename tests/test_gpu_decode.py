@@ -123,7 +123,7 @@ def test_bf16_decode_small(ps, case, paged):
     q = np.stack([synth.query(2, 90 + case, s, 0, 0, hq, d, 1.0, "bf16") for s in range(n)])
     qd = to_dev(q, torch.bfloat16)
     max_splits = cap // 32
-    for splits in sorted({1, 2, 3, min(7, max_splits), 0}):
+    for splits in sorted({sp for sp in (1, 2, 3, 7, 0) if sp <= max_splits}):
         out = torch.empty((n, hq, d), dtype=torch.bfloat16, device="cuda")
         ps.ps_decode_attn(attn, cache, kc, vc, pl, pos, qd, out, block_table=bt, num_splits=splits)
         got = out.float().cpu().numpy()
@@ -177,10 +177,10 @@ def test_invalid_sequence_gives_nan_rows_and_leaves_others(ps):
     attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16, 10000.0, 1 / math.sqrt(d))
     cache = ps.CacheSpec(window=W, slot_capacity=128)
     n = 3
-    positions = [70, 70, 70]
-    prefix = [10, 100, 10]   # sequence 1: 100 + 64 > 128 slots
+    positions = [70, 130, 70]
+    prefix = [10, 100, 10]   # sequence 1 at 130 needs min(131, 164) = 131 > 128 slots
     kc, vc = new_cache(ps, attn, cache, n)
-    hist = [_hist(5, 66, s, 71, hkv, d, 0.5, "bf16") for s in range(n)]
+    hist = [_hist(5, 66, s, positions[s] + 1, hkv, d, 0.5, "bf16") for s in range(n)]
     fill_ring(ps, attn, cache, kc, vc, prefix, positions, [h[0] for h in hist], [h[1] for h in hist])
     pl = torch.tensor(prefix, dtype=torch.int32, device="cuda")
     pos = torch.tensor(positions, dtype=torch.int64, device="cuda")

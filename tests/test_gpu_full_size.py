@@ -1,0 +1,144 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench
+times (automatic split count): sampled sequences / query rows are checked
+against the float64 oracle over the full un-evicted history."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_common import BF16_TOL, fill_rings_sampled, normwise_err, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ps():
+    require_gpu()
+    import bounded_kv_cache_amd as ps
+    return ps
+
+
+def _decode_full_size(ps, cfg, sampled_seqs, prefix, positions, paged=False, seed=0):
+    """One decode step (append p, attend at p) of one layer for every sequence;
+    returns the worst row-normwise error over the sampled sequences."""
+    n = cfg.num_seqs
+    attn = ps.AttnSpec(cfg.hq, cfg.hkv, cfg.dim, ps.PS_BF16, cfg.rope_theta, 1 / math.sqrt(cfg.dim))
+    ring = [min(int(positions[s]) + 1, int(prefix[s]) + cfg.window) for s in range(n)]
+    cap = -(-max(int(prefix[s]) + min(cfg.window, int(positions[s]) + 1) for s in range(n)) // 64) * 64
+    bt = None
+    if paged:
+        pages = [-(-r // 64) for r in ring]
+        num_pages = int(sum(pages))
+        perm = synth.page_permutation(seed, num_pages)
+        table = np.full((n, cap // 64), -1, dtype=np.int32)
+        o = 0
+        for s in range(n):
+            table[s, :pages[s]] = perm[o:o + pages[s]]
+            o += pages[s]
+        bt = torch.from_numpy(table).cuda()
+        cache = ps.CacheSpec(window=cfg.window, slot_capacity=cap, page_size=64, num_pages=num_pages)
+    else:
+        cache = ps.CacheSpec(window=cfg.window, slot_capacity=cap)
+    ks, vs = ps.cache_shapes(attn, cache, n)
+    kc = torch.empty(ks, dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty(vs, dtype=torch.bfloat16, device="cuda")
+    hist = {s: (synth.history(seed, cfg.cfg_id, synth.T_K, s, 0, 0, int(positions[s]) + 1, cfg.hkv, cfg.dim,
+                              cfg.kv_std, "bf16"),
+                synth.history(seed, cfg.cfg_id, synth.T_V, s, 0, 0, int(positions[s]) + 1, cfg.hkv, cfg.dim,
+                              cfg.kv_std, "bf16")) for s in sampled_seqs}
+    fill_rings_sampled(ps, attn, cache, kc, vc, prefix, [int(p) - 1 for p in positions], hist, block_table=bt,
+                       seed=seed)
+    gen = torch.Generator(device="cuda").manual_seed(seed + 1)
+    kn = (torch.randn((n, 1, cfg.hkv, cfg.dim), generator=gen, device="cuda") * cfg.kv_std).bfloat16()
+    vn = (torch.randn((n, 1, cfg.hkv, cfg.dim), generator=gen, device="cuda") * cfg.kv_std).bfloat16()
+    q = torch.randn((n, cfg.hq, cfg.dim), generator=gen, device="cuda").bfloat16()
+    qs = {}
+    for s in sampled_seqs:
+        p = int(positions[s])
+        kn[s, 0] = to_dev(hist[s][0][p], torch.bfloat16)
+        vn[s, 0] = to_dev(hist[s][1][p], torch.bfloat16)
+        qs[s] = synth.query(seed, cfg.cfg_id, s, 0, 0, cfg.hq, cfg.dim, cfg.q_std, "bf16")
+        q[s] = to_dev(qs[s], torch.bfloat16)
+    pl = torch.tensor(np.asarray(prefix, dtype=np.int32), device="cuda")
+    pos = torch.tensor(np.asarray(positions, dtype=np.int64), device="cuda")
+    ps.ps_kv_append(attn, cache, kc, vc, pl, pos, kn, vn, block_table=bt)
+    out = torch.empty((n, cfg.hq, cfg.dim), dtype=torch.bfloat16, device="cuda")
+    ps.ps_decode_attn(attn, cache, kc, vc, pl, pos, q, out, block_table=bt)
+    got = out.float().cpu().numpy()
+    assert not np.isnan(got).any()
+    worst = 0.0
+    for s in sampled_seqs:
+        want = oracle.decode_attention(qs[s], hist[s][0], hist[s][1], int(positions[s]), int(prefix[s]), cfg.window,
+                                       1 / math.sqrt(cfg.dim), cfg.rope_theta)
+        worst = max(worst, normwise_err(got[s], want))
+    return worst
+
+
+def test_decode_32k_64_sequences(ps):
+    c = synth.C2_DECODE
+    err = _decode_full_size(ps, c, [0, 29, 63], [c.prefix] * c.num_seqs, [c.position] * c.num_seqs)
+    assert err <= BF16_TOL, err
+
+
+@pytest.mark.parametrize("cfg", [synth.C3_DECODE_W4096, synth.C3_DECODE_W8192], ids=lambda c: c.name)
+def test_decode_128k_256_sequences(ps, cfg):
+    err = _decode_full_size(ps, cfg, [0, 255], [cfg.prefix] * cfg.num_seqs, [cfg.position] * cfg.num_seqs)
+    assert err <= BF16_TOL, err
+
+
+def test_decode_ragged_paged_1024_sequences(ps):
+    c = synth.C5_DECODE
+    pos, pre = synth.ragged_draws(0, c.num_seqs)
+    # sampled: the longest, the shortest, one in warm-up if any, and one at random
+    warm = [s for s in range(c.num_seqs) if pos[s] + 1 < pre[s] + c.window]
+    sampled = sorted({int(np.argmax(pos)), int(np.argmin(pos)), 17} | set(warm[:1]))
+    err = _decode_full_size(ps, c, sampled, pre, pos, paged=True)
+    assert err <= BF16_TOL, err
+
+
+def _prefill_rows(ps, cfg, rows, batches, heads):
+    attn = ps.AttnSpec(cfg.hq, cfg.hkv, cfg.dim, ps.PS_BF16, cfg.rope_theta, 1 / math.sqrt(cfg.dim))
+    nk, T = cfg.nk, cfg.queries
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    q = torch.randn((cfg.batch, T, cfg.hq, cfg.dim), generator=gen, device="cuda").bfloat16()
+    k = torch.randn((cfg.batch, nk, cfg.hkv, cfg.dim), generator=gen, device="cuda").bfloat16()
+    v = torch.randn((cfg.batch, nk, cfg.hkv, cfg.dim), generator=gen, device="cuda").bfloat16()
+    host = {}
+    for b in batches:
+        qb = synth.history(3, cfg.cfg_id, synth.T_Q, b, 0, 0, T, cfg.hq, cfg.dim, 1.0, "bf16")
+        kb = synth.history(3, cfg.cfg_id, synth.T_K, b, 0, 0, nk, cfg.hkv, cfg.dim, 1.0, "bf16")
+        vb = synth.history(3, cfg.cfg_id, synth.T_V, b, 0, 0, nk, cfg.hkv, cfg.dim, 1.0, "bf16")
+        q[b] = to_dev(qb, torch.bfloat16)
+        k[b] = to_dev(kb, torch.bfloat16)
+        v[b] = to_dev(vb, torch.bfloat16)
+        host[b] = (qb, kb, vb)
+    out = torch.empty_like(q)
+    lse = torch.empty((cfg.batch, cfg.hq, T), dtype=torch.float32, device="cuda")
+    ps.ps_prefill_attn(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, out, lse=lse)
+    got = out.float().cpu().numpy()
+    worst = 0.0
+    for b in batches:
+        qb, kb, vb = host[b]
+        want, want_lse = oracle.prefill_attention(qb, kb, vb, cfg.prefix, cfg.window, cfg.kv_start,
+                                                  1 / math.sqrt(cfg.dim), cfg.rope_theta, rows=rows)
+        for h in heads:
+            worst = max(worst, normwise_err(got[b][rows][:, h], want[:, h]))
+        np.testing.assert_allclose(lse[b].cpu().numpy().T[rows], want_lse, rtol=0, atol=2e-2)
+    return worst
+
+
+def test_prefill_truncated_backprop_chunk(ps):
+    c = synth.C4_PREFILL
+    rows = [0, 1, 127, 128, 2047, 2048, 2049, 4100, 8063, 8064, 8191]
+    err = _prefill_rows(ps, c, rows, batches=[0, 7], heads=range(c.hq))
+    assert err <= BF16_TOL, err
+
+
+def test_prefill_full_causal_comparator(ps):
+    c = synth.C4_PREFILL_FULL
+    rows = [0, 4095, 8191]
+    err = _prefill_rows(ps, c, rows, batches=[5], heads=[0, 13, 27])
+    assert err <= BF16_TOL, err

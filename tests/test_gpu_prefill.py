@@ -21,7 +21,7 @@ def ps():
 
 
 def _plan(ps, attn, W, L, start, T, nk):
-    max_tiles = 1 << 16
+    max_tiles = 1 << 18
     tiles = torch.full((max_tiles, 3), -7, dtype=torch.int32, device="cuda")
     n = torch.zeros(1, dtype=torch.int32, device="cuda")
     ps.ps_prefill_plan(attn, W, L, start, T, nk, tiles, n)
