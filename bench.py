@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-full", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=50)
     ap.add_argument("--sweep", action="store_true", help="also time decode at a sweep of positions (flatness)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="run one device-to-device copy of BYTES first (reference for HBM counter scaling)")
     return ap.parse_args()
 
 
@@ -333,6 +335,13 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)   # a plain elementwise kernel: reads and writes BYTES each
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: {args.copy_probe} bytes read and written", file=sys.stderr, flush=True)
+        del src, dst
     print(f"[bench] decode: {args.num_seqs} seqs x {args.layers} layers @ {args.position}, W={args.window}",
           file=sys.stderr, flush=True)
     dec, sweep = run_decode(ps, torch, args)
