@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-full", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=50)
     ap.add_argument("--sweep", action="store_true", help="also time decode at a sweep of positions (flatness)")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="run only one leg (for profiling); the JSON line then carries that leg only")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run one device-to-device copy of BYTES first (reference for HBM counter scaling)")
     return ap.parse_args()
@@ -344,15 +346,18 @@ def main():
         del src, dst
     print(f"[bench] decode: {args.num_seqs} seqs x {args.layers} layers @ {args.position}, W={args.window}",
           file=sys.stderr, flush=True)
+    if args.only == "prefill":
+        print(json.dumps({"prefill": run_prefill(ps, torch, full_causal=not args.no_full)}))
+        return
     dec, sweep = run_decode(ps, torch, args)
     print(f"[bench] decode done: {dec['tok_s']:.0f} tok/s, kernel {dec['kernel_s'] * 1e6:.1f} us",
           file=sys.stderr, flush=True)
     prefill = None
-    if not args.no_prefill:
+    if not args.no_prefill and args.only is None:
         prefill = run_prefill(ps, torch)
         print(f"[bench] prefill done: {prefill}", file=sys.stderr, flush=True)
     full = None
-    if not args.no_full:
+    if not args.no_full and args.only is None:
         full = run_full_attention(ps, torch, args)
         print(f"[bench] full attention done: {full['tok_s']:.0f} tok/s", file=sys.stderr, flush=True)
     achieved = dec["kernel_bytes"] / dec["kernel_s"] / 1e9

@@ -35,9 +35,9 @@ def common_flags() -> list:
             "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, extra=(), build_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = (res.stdout + res.stderr)
     # the host pass does not know the device-only feature flag: harmless
@@ -49,17 +49,20 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB_PATH, defines=(), build_dir: str = BUILD_DIR) -> str:
+    """Compile every source and link ``out``.  ``defines`` (e.g. "PS_DECODE_WAVES=8")
+    override the kernels' compile-time launch-shape defaults."""
+    os.makedirs(build_dir, exist_ok=True)
+    extra = [f"-D{d}" for d in defines]
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, extra, build_dir), SOURCES))
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -28,6 +28,19 @@
 // chunk; running sums stay lane-local until the end.
 #include "ps_internal.h"
 
+// Launch shape of the bf16 kernel: waves per workgroup and the minimum number
+// of resident workgroups per CU the register allocation must allow.
+#ifndef PS_DECODE_WAVES
+#define PS_DECODE_WAVES 4
+#endif
+#ifndef PS_DECODE_MIN_BLOCKS
+#define PS_DECODE_MIN_BLOCKS 2
+#endif
+// 1: stream K/V with non-temporal loads (each byte is read exactly once)
+#ifndef PS_DECODE_NT
+#define PS_DECODE_NT 1
+#endif
+
 namespace ps {
 namespace {
 
@@ -35,16 +48,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ inline float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
-struct RegionRef {
-  const uint16_t* k;
-  const uint16_t* v;
-};
+__device__ inline u32x4 stream_load(const uint16_t* p) {
+#if PS_DECODE_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA partial kernel
 // ---------------------------------------------------------------------------
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NC = D / 32;   // QK k-steps (32 dims each)
   constexpr int NDT = D / 16;  // PV d-tiles (16 dims each)
   const int lane = threadIdx.x & 63;
@@ -124,9 +140,9 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
   const int c_end = (ke + 31) >> 5;   // chunks touching [kb, ke)
   int c = (kb >> 5) + wave;
 
-  uint4 kA[2][NC], vA[NDT], kB[2][NC], vB[NDT];
+  u32x4 kA[2][NC], vA[NDT], kB[2][NC], vB[NDT];
 
-  auto load_chunk = [&](int ci, uint4 (&kr)[2][NC], uint4 (&vr)[NDT]) {
+  auto load_chunk = [&](int ci, u32x4 (&kr)[2][NC], u32x4 (&vr)[NDT]) {
     const int key0 = ci << 5;
     const int64_t base = region_offset(geo, a.block_table, s, h, key0);
     if (base < 0) {
@@ -134,9 +150,9 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) kr[t][cc] = uint4{0, 0, 0, 0};
+        for (int cc = 0; cc < NC; ++cc) kr[t][cc] = u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vr[dt] = uint4{0, 0, 0, 0};
+      for (int dt = 0; dt < NDT; ++dt) vr[dt] = u32x4{0, 0, 0, 0};
       return;
     }
     const int in_reg = (key0 & 63) * D;
@@ -145,12 +161,12 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) kr[t][cc] = *reinterpret_cast<const uint4*>(kp + koff[t] + 32 * cc);
+      for (int cc = 0; cc < NC; ++cc) kr[t][cc] = stream_load(kp + koff[t] + 32 * cc);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) vr[dt] = *reinterpret_cast<const uint4*>(vp + voff + dt * 16 * 8);
+    for (int dt = 0; dt < NDT; ++dt) vr[dt] = stream_load(vp + voff + dt * 16 * 8);
   };
 
-  auto compute_chunk = [&](int ci, uint4 (&kr)[2][NC], uint4 (&vr)[NDT]) {
+  auto compute_chunk = [&](int ci, u32x4 (&kr)[2][NC], u32x4 (&vr)[NDT]) {
     f32x4 st0 = f32x4{0.f, 0.f, 0.f, 0.f}, st1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
@@ -171,14 +187,12 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
       // (slots past the visible length may hold anything, including NaN bits)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        uint32_t w[4] = {vr[dt].x, vr[dt].y, vr[dt].z, vr[dt].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int k0 = key0 + 2 * e;
-          if (k0 >= ke || k0 < kb) w[e] &= 0xffff0000u;
-          if (k0 + 1 >= ke || k0 + 1 < kb) w[e] &= 0x0000ffffu;
+          if (k0 >= ke || k0 < kb) vr[dt][e] &= 0xffff0000u;
+          if (k0 + 1 >= ke || k0 + 1 < kb) vr[dt][e] &= 0x0000ffffu;
         }
-        vr[dt] = uint4{w[0], w[1], w[2], w[3]};
       }
     }
     float mx = sv[0];
@@ -435,7 +449,7 @@ template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((uint32_t)((int64_t)a.num_seqs * a.geom.hkv * a.num_splits));
   if (a.dtype == PS_BF16) {
-    constexpr int NW = 4;
+    constexpr int NW = PS_DECODE_WAVES;
     hipLaunchKernelGGL((decode_bf16_kernel<D, NW>), grid, dim3(NW * 64), 0, stream, a);
   } else {
     hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(256), 0, stream, a);

@@ -8,14 +8,15 @@
 //
 // Pipeline of one call:
 //   1. prep kernel: rotate K at its absolute positions into a per-(batch, KV
-//      head) contiguous copy, write V transposed ([D][keys], keys padded to BN
-//      with zeros) and a cos/sin table for the query positions.
+//      head) contiguous copy, write V transposed ([D][keys], keys padded to a
+//      multiple of 64 with zeros, permuted inside each 16-key group -- see
+//      vt_slot) and a cos/sin table for the query positions.
 //   2. attention kernel: one workgroup per (batch, query head, BM-query tile),
 //      walking the scheduled key tiles (ps_sched.h).
-// The bf16 kernel is an MFMA kernel (v_mfma_f32_32x32x16_bf16): it computes
-// S^T = K Q^T so each lane owns one query column and the softmax reductions are
-// in-lane plus one cross-half exchange; the S^T registers feed the PV product
-// O^T += V^T P^T directly as its B operand, with V^T staged through LDS.
+// The bf16 kernel uses v_mfma_f32_32x32x16_bf16.  It computes S^T = K Q^T so
+// each lane owns one query column: softmax reductions are in-lane plus one
+// exchange between the two lane halves, and the S^T registers, rounded to bf16,
+// are directly the B operand of O^T += V^T P^T (V^T staged through LDS).
 #include "ps_internal.h"
 #include "ps_sched.h"
 
@@ -23,6 +24,15 @@ namespace ps {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994531f;
+// Lazy softmax rescaling: the reference max of a query only moves when a tile's
+// max exceeds it by more than this (log2 units), so probabilities stay <= 2^8
+// and the accumulator is rescaled rarely.  Exact: numerator and denominator
+// share the reference.
+constexpr float kRebase = 8.f;
+#ifndef PS_PREFILL_MIN_BLOCKS
+#define PS_PREFILL_MIN_BLOCKS 2
+#endif
+constexpr float kRebaseLow = 64.f;
 
 template <typename T>
 struct PfTraits;
@@ -35,7 +45,15 @@ struct PfTraits<float> {
   static constexpr int BM = 64, BN = 64;
 };
 
-__host__ __device__ inline int32_t nk_padded(int32_t nk, int32_t bn) { return (nk + bn - 1) / bn * bn; }
+__host__ __device__ inline int32_t nk_padded(int32_t nk) { return (nk + 63) / 64 * 64; }
+
+// Position of key k inside its 16-key group of the V^T rows.  Stored order per
+// group: keys 0-3, 8-11, 4-7, 12-15, so that the 8 keys one MFMA lane needs for
+// a PV k-step (16j + 8*(e/4) + 4*half + e%4, e = 0..7) are 16 contiguous bytes.
+__host__ __device__ inline int32_t vt_slot(int32_t k) {
+  const int32_t kl = k & 15;
+  return (k & ~15) | (((kl >> 2) & 1) << 3) | ((kl >> 3) << 2) | (kl & 3);
+}
 
 // ---------------------------------------------------------------------------
 // 1. prep: rotated K [b][hkv][nkp][D], V^T [b][hkv][D][nkp], query cos/sin table
@@ -50,7 +68,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
   __shared__ float cs_lds[TK][HALF][2];
   __shared__ T vt_lds[D][TK + 1];
   PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, a.bm, a.bn};
-  const int32_t nkp = nk_padded(a.num_k, a.bn);
+  const int32_t nkp = nk_padded(a.num_k);
   const int32_t nkt = nkp / TK;
   const int tid = threadIdx.x;
   const T* k = static_cast<const T*>(a.k);
@@ -88,8 +106,8 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
         }
         Elem<T>::store(kr + (bh * nkp + key) * D + i, y1);
         Elem<T>::store(kr + (bh * nkp + key) * D + i + HALF, y2);
-        vt_lds[i][j] = v1;
-        vt_lds[i + HALF][j] = v2;
+        vt_lds[i][vt_slot(j)] = v1;
+        vt_lds[i + HALF][vt_slot(j)] = v2;
       }
       __syncthreads();
       for (int idx = tid; idx < D * TK; idx += 256) {
@@ -151,8 +169,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int32_t t = it.qt * BM + tid;
   const bool row_ok = t < a.num_q;
+  const int32_t u = a.num_k - a.num_q + t;  // the query's key index
   const int32_t kvh = it.hq / a.group;
-  const int32_t nkp = nk_padded(a.num_k, BN);
+  const int32_t nkp = nk_padded(a.num_k);
   const float* q = static_cast<const float*>(a.q);
   const float* kr = static_cast<const float*>(a.k_rot) + ((int64_t)it.b * a.hkv + kvh) * nkp * D;
   const float* vt = static_cast<const float*>(a.k_rot) + (int64_t)a.batch * a.hkv * nkp * D +
@@ -166,7 +185,6 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
       qs[tid][i + D / 2] = (x2 * c + x1 * s) * a.scale_log2;
     }
   }
-  const int64_t pq = row_ok ? pf_query_pos(geo, t) : 0;
   float acc[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
@@ -181,7 +199,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     for (int idx = tid; idx < BN * D; idx += 64) {
       const int j = idx / D, d = idx % D;
       ks[j][d] = kr[((int64_t)kt * BN + j) * D + d];
-      vs[j][d] = vt[(int64_t)d * nkp + kt * BN + j];
+      vs[j][d] = vt[(int64_t)d * nkp + vt_slot(kt * BN + j)];
     }
     __syncthreads();
     if (!row_ok) continue;
@@ -191,11 +209,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
       float s = 0.f;
       for (int d = 0; d < D; ++d) s += qs[tid][d] * ks[j][d];
       const int32_t key = kt * BN + j;
-      bool vis = key < a.num_k;
-      if (kind == 2 && vis) {
-        const int64_t pk = pf_key_pos(geo, key);
-        vis = pk <= pq && (pk < a.prefix_len || pk > pq - a.window);
-      }
+      const bool vis = key < a.num_k && (kind == 1 || pf_visible(geo, u, key));
       sc[j] = vis ? s : -INFINITY;
       mx = fmaxf(mx, sc[j]);
     }
@@ -226,13 +240,19 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 //   D[m][n]: lane (n + 32*((m/4)%2)) register 4*(m/8) + m%4
 // The dim <-> k-slot map of QK is shared by both operands (dim 16*ks + 8*hf + e),
 // so it never matters which physical k the hardware pairs.
+//
+// Softmax bookkeeping per query column: `ref` is the reference max (log2
+// units); the S accumulator starts at -ref, so the MFMA itself yields s - ref
+// and the fast path is just max / exp2 / sum / convert.
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int BM = 128, BN = 64;
   constexpr int KS = D / 16;        // QK k-steps
   constexpr int MT = D / 32;        // PV output d-tiles
   constexpr int KPAD = D + 8;       // K row stride in LDS (bf16 elements)
-  constexpr int VPAD = BN + 4;      // V^T row stride in LDS
+  constexpr int VPAD = BN + 8;      // V^T row stride in LDS
+  constexpr int KPIECES = BN * D / 8 / 256;   // 16-byte pieces per thread per tile
+  constexpr int VPIECES = D * BN / 8 / 256;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KPAD];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VPAD];
 
@@ -244,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
   const int32_t kvh = it.hq / a.group;
-  const int32_t nkp = nk_padded(a.num_k, BN);
+  const int32_t nkp = nk_padded(a.num_k);
   const uint16_t* kr = static_cast<const uint16_t*>(a.k_rot) + ((int64_t)it.b * a.hkv + kvh) * nkp * D;
   const uint16_t* vt = static_cast<const uint16_t*>(a.k_rot) + (int64_t)a.batch * a.hkv * nkp * D +
                        ((int64_t)it.b * a.hkv + kvh) * D * nkp;
@@ -252,6 +272,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // ---- query operand (B of S^T = K Q^T): query row t, dims 16*ks + 8*hf + e ----
   const int32_t t = it.qt * BM + wave * 32 + col;
   const bool row_ok = t < a.num_q;
+  const int32_t u = a.num_k - a.num_q + t;  // key index of this lane's query
   bf16x8 qop[KS];
   {
     float qv[KS][8];
@@ -284,81 +305,81 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qop[ks][e] = (bf16)(row_ok ? qv[ks][e] * a.scale_log2 : 0.f);
   }
-  const int64_t pq = row_ok ? pf_query_pos(geo, t) : -1;
+  // per-lane visible key ranges: pinned keys [0, pre_end), chunk keys band_lo + [0, band_w]
+  const int32_t pre_end = row_ok ? pf_min(a.prefix_len, u + 1) : 0;
+  int32_t band_lo = pf_max(a.prefix_len, u - a.window + 1);
+  const int32_t band_hi = pf_min(u, a.num_k - 1);
+  uint32_t band_w = (uint32_t)(band_hi - band_lo);
+  if (!row_ok || band_hi < band_lo) {  // empty band: no key satisfies the unsigned range test
+    band_lo = 0x7fffffff;
+    band_w = 0;
+  }
 
   f32x16 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float ref = 0.f;     // reference max (log2 units)
+  float l_run = 0.f;   // lane-local partial sum of exp2(s - ref)
 
-  // ---- cooperative tile loads (global -> registers -> LDS) ----
-  // K tile: BN rows x D dims = BN*D/8 16-byte pieces; V^T tile: D rows x BN keys.
-  constexpr int KPIECES = BN * D / 8 / 256;   // per thread
-  constexpr int VPIECES = D * BN / 8 / 256;
-  uint4 kreg[KPIECES], vreg[VPIECES];
-  auto gload = [&](int32_t kt) {
-#pragma unroll
-    for (int p = 0; p < KPIECES; ++p) {
-      const int piece = tid + 256 * p;
-      const int row = piece / (D / 8), c8 = piece % (D / 8);
-      kreg[p] = *reinterpret_cast<const uint4*>(kr + ((int64_t)kt * BN + row) * D + c8 * 8);
-    }
-#pragma unroll
-    for (int p = 0; p < VPIECES; ++p) {
-      const int piece = tid + 256 * p;
-      const int row = piece / (BN / 8), c8 = piece % (BN / 8);
-      vreg[p] = *reinterpret_cast<const uint4*>(vt + (int64_t)row * nkp + (int64_t)kt * BN + c8 * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < KPIECES; ++p) {
-      const int piece = tid + 256 * p;
-      const int row = piece / (D / 8), c8 = piece % (D / 8);
-      *reinterpret_cast<uint4*>(&k_lds[buf][row * KPAD + c8 * 8]) = kreg[p];
-    }
-#pragma unroll
-    for (int p = 0; p < VPIECES; ++p) {
-      const int piece = tid + 256 * p;
-      const int row = piece / (BN / 8), c8 = piece % (BN / 8);
-      uint16_t* dst = &v_lds[buf][row * VPAD + c8 * 8];
-      // VPAD keeps rows 8-byte aligned only: store as two 8-byte halves
-      *reinterpret_cast<uint2*>(dst) = uint2{vreg[p].x, vreg[p].y};
-      *reinterpret_cast<uint2*>(dst + 4) = uint2{vreg[p].z, vreg[p].w};
-    }
-  };
+  u32x4 kreg[KPIECES], vreg[VPIECES];
+  // global -> registers (next tile) and registers -> LDS; plain code so that the
+  // staging arrays stay in registers
+#define PS_PF_GLOAD(KT)                                                                              \
+  do {                                                                                              \
+    _Pragma("unroll") for (int p = 0; p < KPIECES; ++p) {                                           \
+      const int piece = tid + 256 * p;                                                              \
+      kreg[p] = *reinterpret_cast<const u32x4*>(kr + ((int64_t)(KT) * BN + piece / (D / 8)) * D +   \
+                                                (piece % (D / 8)) * 8);                             \
+    }                                                                                               \
+    _Pragma("unroll") for (int p = 0; p < VPIECES; ++p) {                                           \
+      const int piece = tid + 256 * p;                                                              \
+      vreg[p] = *reinterpret_cast<const u32x4*>(vt + (int64_t)(piece / (BN / 8)) * nkp +            \
+                                                (int64_t)(KT) * BN + (piece % (BN / 8)) * 8);       \
+    }                                                                                               \
+  } while (0)
+#define PS_PF_LSTORE(BUF)                                                                            \
+  do {                                                                                              \
+    _Pragma("unroll") for (int p = 0; p < KPIECES; ++p) {                                           \
+      const int piece = tid + 256 * p;                                                              \
+      *reinterpret_cast<u32x4*>(&k_lds[BUF][(piece / (D / 8)) * KPAD + (piece % (D / 8)) * 8]) =    \
+          kreg[p];                                                                                  \
+    }                                                                                               \
+    _Pragma("unroll") for (int p = 0; p < VPIECES; ++p) {                                           \
+      const int piece = tid + 256 * p;                                                              \
+      *reinterpret_cast<u32x4*>(&v_lds[BUF][(piece / (BN / 8)) * VPAD + (piece % (BN / 8)) * 8]) =  \
+          vreg[p];                                                                                  \
+    }                                                                                               \
+  } while (0)
 
   const TileRange tr = pf_tile_range(geo, it.qt);
   const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
   auto cand_tile = [&](int32_t ci) { return ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix); };
 
-  // find the first scheduled tile
   int32_t ci = 0;
   int kind = 0;
   while (ci < n_cand && (kind = pf_classify(geo, it.qt, cand_tile(ci))) == 0) ++ci;
   if (ci < n_cand) {
-    gload(cand_tile(ci));
-    lstore(0);
+    PS_PF_GLOAD(cand_tile(ci));
+    PS_PF_LSTORE(0);
   }
   __syncthreads();
   int buf = 0;
   while (ci < n_cand) {
     const int32_t kt = cand_tile(ci);
     const int cur_kind = kind;
-    // next scheduled tile; its loads are in flight during this tile's math
     int32_t cn = ci + 1;
     int nkind = 0;
     while (cn < n_cand && (nkind = pf_classify(geo, it.qt, cand_tile(cn))) == 0) ++cn;
-    if (cn < n_cand) gload(cand_tile(cn));
+    if (cn < n_cand) PS_PF_GLOAD(cand_tile(cn));  // next tile's loads are in flight during this tile's math
 
-    // ---- S^T = K Q^T: two 32-key M-tiles ----
+    // ---- S^T - ref = K Q^T + (-ref): two 32-key M-tiles ----
     f32x16 st[2];
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st[m2][i] = 0.f;
+      for (int i = 0; i < 16; ++i) st[m2][i] = -ref;
       const uint16_t* krow = &k_lds[buf][(32 * m2 + col) * KPAD + 8 * hf];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -366,63 +387,76 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         st[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], st[m2], 0, 0, 0);
       }
     }
-    // key of register i of tile m2: 32*m2 + 8*(i/4) + 4*hf + i%4
+    // key of register i of tile m2: kt*BN + 32*m2 + 8*(i/4) + 4*hf + i%4
     if (cur_kind == 2) {
+      const int32_t kbase = kt * BN + 4 * hf;
 #pragma unroll
       for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int32_t key = kt * BN + 32 * m2 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          bool vis = row_ok && key < a.num_k;
-          if (vis) {
-            const int64_t pk = pf_key_pos(geo, key);
-            vis = pk <= pq && (pk < a.prefix_len || pk > pq - a.window);
-          }
+          const int32_t key = kbase + 32 * m2 + 8 * (i >> 2) + (i & 3);
+          const bool vis = key < pre_end || (uint32_t)(key - band_lo) <= band_w;
           if (!vis) st[m2][i] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    float mx = st[0][0];
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[m2][i]);
+      for (int i = (m2 == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, st[m2][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    // rare path (wave-uniform branch): this tile's max exceeds the reference by
+    // more than kRebase -> move the reference up and rescale what is accumulated
+    if (__any(mx > kRebase)) {
+      const float shift = mx > kRebase ? mx : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+      ref += shift;
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) st[m2] -= shift;
+    }
+    // nothing accumulated yet and every score far below the reference: move it
+    // down so the first probabilities do not underflow (no rescale needed)
+    if (__any(mx < -kRebaseLow)) {
+      const float ltot = l_run + __shfl_xor(l_run, 32, 64);
+      const float shift = (ltot == 0.f && mx < -kRebaseLow && mx != -INFINITY) ? mx : 0.f;
+      ref += shift;
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) st[m2] -= shift;
+    }
     bf16x8 pop[4];
     float psum = 0.f;
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(st[m2][i] - m_use);
+        const float p = __builtin_amdgcn_exp2f(st[m2][i]);
         psum += p;
         pop[2 * m2 + (i >> 3)][i & 7] = (bf16)p;
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+    l_run += psum;
 
     // ---- O^T += V^T P^T: PV k-step j covers keys 16j + 8*(e/4) + 4*hf + e%4 ----
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint16_t* vrow = &v_lds[buf][(32 * mt + col) * VPAD + 4 * hf];
+      const uint16_t* vrow = &v_lds[buf][(32 * mt + col) * VPAD + 8 * hf];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * j);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * j + 8);
-        const uint4 w = uint4{lo.x, lo.y, hi.x, hi.y};
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pop[j], acc[mt], 0, 0, 0);
+        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vrow + 16 * j);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[j], acc[mt], 0, 0, 0);
       }
     }
-    if (cn < n_cand) lstore(buf ^ 1);
+    if (cn < n_cand) PS_PF_LSTORE(buf ^ 1);
     __syncthreads();
     buf ^= 1;
     ci = cn;
     kind = nkind;
   }
+
+#undef PS_PF_GLOAD
+#undef PS_PF_LSTORE
 
   // ---- epilogue: l across the two halves, normalise, store ----
   l_run += __shfl_xor(l_run, 32, 64);
@@ -438,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
                             pack_bf16x2(acc[mt][4 * i4 + 2] * inv, acc[mt][4 * i4 + 3] * inv)};
       *reinterpret_cast<uint2*>(orow + d) = w;
     }
-  if (a.lse && hf == 0) a.lse[((int64_t)it.b * a.hq + it.hq) * a.num_q + t] = (m_run + __log2f(l_run)) * kLn2;
+  if (a.lse && hf == 0) a.lse[((int64_t)it.b * a.hq + it.hq) * a.num_q + t] = (ref + __log2f(l_run)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -492,7 +526,7 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillGeom 
 template <typename T, int D>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   {
-    int64_t blocks = (int64_t)a.batch * (nk_padded(a.num_k, a.bn) / 64);
+    int64_t blocks = (int64_t)a.batch * (nk_padded(a.num_k) / 64);
     blocks = blocks < 1 ? 1 : (blocks > 16384 ? 16384 : blocks);
     hipLaunchKernelGGL((prefill_prep_kernel<T, D>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();

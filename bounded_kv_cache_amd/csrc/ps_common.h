@@ -19,6 +19,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// 16-byte register type for global/LDS traffic (a native vector, so copies stay in registers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRegionSlots = 64;   // slots per cache region (page size of paged mode)
 constexpr int kMaxGroup = 16;      // query heads per KV head handled by one decode work item
