@@ -46,8 +46,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ inline float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
-
 __device__ inline u32x4 stream_load(const uint16_t* p) {
 #if PS_DECODE_NT
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -198,8 +196,8 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
     float mx = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
@@ -235,8 +233,8 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
   }
 
   // ---- finish the wave: sum the lane-local partial sums of each head ----
-  l_run += wave_shfl_xor(l_run, 16);
-  l_run += wave_shfl_xor(l_run, 32);
+  l_run = sum_xor16(l_run);
+  l_run = sum_xor32(l_run);
 
   // ---- merge the NW waves through LDS ----
   __shared__ float sm_o[NW][D][17];

@@ -59,18 +59,55 @@ __host__ __device__ inline int32_t vt_slot(int32_t k) {
 // 1. prep: rotated K [b][hkv][nkp][D], V^T [b][hkv][D][nkp], query cos/sin table
 // ---------------------------------------------------------------------------
 // One workgroup per (batch, 64-key tile): the tile's cos/sin are formed once in
-// LDS and reused for every KV head; V is transposed through LDS so that both
-// the reads and the V^T writes are row-contiguous.  Keys past num_k are zero.
+// LDS and reused for every KV head.  Each thread owns a quarter of one key row
+// (16-byte loads and stores); V is transposed through LDS so the V^T rows are
+// written contiguously.  Keys past num_k are written as zeros.
+template <typename T>
+__device__ inline void load_vec(const T* p, float* x, int n) {  // n contiguous elements, 16-byte loads
+  constexpr int E = 16 / sizeof(T);
+  for (int c = 0; c < n; c += E) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p + c);
+    if (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[c + 2 * e] = lo_bf16(w[e]);
+        x[c + 2 * e + 1] = hi_bf16(w[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[c + e] = __uint_as_float(w[e]);
+    }
+  }
+}
+template <typename T>
+__device__ inline void store_vec(T* p, const float* x, int n) {
+  constexpr int E = 16 / sizeof(T);
+  for (int c = 0; c < n; c += E) {
+    u32x4 w;
+    if (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[c + 2 * e], x[c + 2 * e + 1]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(x[c + e]);
+    }
+    *reinterpret_cast<u32x4*>(p + c) = w;
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
   constexpr int TK = 64;
   constexpr int HALF = D / 2;
+  constexpr int PQ = HALF / 4;   // rotation pairs per thread
+  constexpr int DQ = D / 4;      // V dims per thread
   __shared__ float cs_lds[TK][HALF][2];
-  __shared__ T vt_lds[D][TK + 1];
+  __shared__ T vt_lds[D][TK + 8];
   PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, a.bm, a.bn};
   const int32_t nkp = nk_padded(a.num_k);
   const int32_t nkt = nkp / TK;
   const int tid = threadIdx.x;
+  const int j = tid >> 2, qq = tid & 3;   // key row of the tile, quarter of the row
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
   T* kr = static_cast<T*>(a.k_rot);
@@ -80,39 +117,64 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
     const int32_t kt = (int32_t)(blk % nkt);
     const int32_t b = (int32_t)(blk / nkt);
     for (int idx = tid; idx < TK * HALF; idx += 256) {
-      const int j = idx / HALF, i = idx % HALF;
-      const int32_t key = kt * TK + j;
-      float c = 1.f, s = 0.f;
-      if (a.rope.enabled && key < a.num_k) rope_cos_sin(pf_key_pos(geo, key), a.rope.inv_freq[i], c, s);
-      cs_lds[j][i][0] = c;
-      cs_lds[j][i][1] = s;
+      const int jj = idx / HALF, i = idx % HALF;
+      const int32_t key = kt * TK + jj;
+      float c = 1.f, sn = 0.f;
+      if (a.rope.enabled && key < a.num_k) rope_cos_sin(pf_key_pos(geo, key), a.rope.inv_freq[i], c, sn);
+      cs_lds[jj][i][0] = c;
+      cs_lds[jj][i][1] = sn;
     }
     __syncthreads();
+    const int32_t key = kt * TK + j;
     for (int32_t h = 0; h < a.hkv; ++h) {
       const int64_t bh = (int64_t)b * a.hkv + h;
-      for (int idx = tid; idx < TK * HALF; idx += 256) {
-        const int j = idx / HALF, i = idx % HALF;
-        const int32_t key = kt * TK + j;
-        float y1 = 0.f, y2 = 0.f;
-        T v1 = T(0), v2 = T(0);
-        if (key < a.num_k) {
-          const int64_t src = (((int64_t)b * a.num_k + key) * a.hkv + h) * D;
-          const float x1 = Elem<T>::load(k + src + i), x2 = Elem<T>::load(k + src + i + HALF);
-          const float c = cs_lds[j][i][0], s = cs_lds[j][i][1];
-          y1 = x1 * c - x2 * s;
-          y2 = x2 * c + x1 * s;
-          v1 = v[src + i];
-          v2 = v[src + i + HALF];
+      float x1[PQ], x2[PQ], vv[DQ];
+      if (key < a.num_k) {
+        const int64_t src = (((int64_t)b * a.num_k + key) * a.hkv + h) * D;
+        load_vec(k + src + PQ * qq, x1, PQ);
+        load_vec(k + src + HALF + PQ * qq, x2, PQ);
+        load_vec(v + src + DQ * qq, vv, DQ);
+#pragma unroll
+        for (int e = 0; e < PQ; ++e) {
+          const float c = cs_lds[j][PQ * qq + e][0], sn = cs_lds[j][PQ * qq + e][1];
+          const float y1 = x1[e] * c - x2[e] * sn, y2 = x2[e] * c + x1[e] * sn;
+          x1[e] = y1;
+          x2[e] = y2;
         }
-        Elem<T>::store(kr + (bh * nkp + key) * D + i, y1);
-        Elem<T>::store(kr + (bh * nkp + key) * D + i + HALF, y2);
-        vt_lds[i][vt_slot(j)] = v1;
-        vt_lds[i + HALF][vt_slot(j)] = v2;
+      } else {
+#pragma unroll
+        for (int e = 0; e < PQ; ++e) x1[e] = x2[e] = 0.f;
+#pragma unroll
+        for (int e = 0; e < DQ; ++e) vv[e] = 0.f;
+      }
+      T* krow = kr + (bh * nkp + key) * D;
+      store_vec(krow + PQ * qq, x1, PQ);
+      store_vec(krow + HALF + PQ * qq, x2, PQ);
+      const int js = vt_slot(j);
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        T tv;
+        if (sizeof(T) == 2)
+          tv = (T)f32_to_bf16_bits(vv[e]);   // exact: vv holds bf16 values
+        else
+          tv = (T)vv[e];
+        vt_lds[DQ * qq + e][js] = tv;
       }
       __syncthreads();
-      for (int idx = tid; idx < D * TK; idx += 256) {
-        const int d = idx / TK, j = idx % TK;
-        vt[(bh * D + d) * nkp + kt * TK + j] = vt_lds[d][j];
+      // V^T rows: D rows x 64 keys, 16-byte pieces
+      constexpr int EP = 16 / sizeof(T);
+      for (int idx = tid; idx < D * (TK / EP); idx += 256) {
+        const int d = idx / (TK / EP), c = idx % (TK / EP);
+        u32x4 w;
+        if (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)(uint16_t)vt_lds[d][c * EP + 2 * e] | ((uint32_t)(uint16_t)vt_lds[d][c * EP + 2 * e + 1] << 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = __float_as_uint((float)vt_lds[d][c * EP + e]);
+        }
+        *reinterpret_cast<u32x4*>(vt + (bh * D + d) * nkp + kt * TK + c * EP) = w;
       }
       __syncthreads();
     }
@@ -122,10 +184,10 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
   for (int64_t idx = blockIdx.x * 256ll + tid; idx < tq; idx += (int64_t)gridDim.x * 256) {
     const int32_t i = (int32_t)(idx % HALF);
     const int32_t t = (int32_t)(idx / HALF);
-    float c = 1.f, s = 0.f;
-    if (a.rope.enabled) rope_cos_sin(pf_query_pos(geo, t), a.rope.inv_freq[i], c, s);
+    float c = 1.f, sn = 0.f;
+    if (a.rope.enabled) rope_cos_sin(pf_query_pos(geo, t), a.rope.inv_freq[i], c, sn);
     a.rope_cs[idx * 2 + 0] = c;
-    a.rope_cs[idx * 2 + 1] = s;
+    a.rope_cs[idx * 2 + 1] = sn;
   }
 }
 
@@ -269,6 +331,45 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
   const uint16_t* vt = static_cast<const uint16_t*>(a.k_rot) + (int64_t)a.batch * a.hkv * nkp * D +
                        ((int64_t)it.b * a.hkv + kvh) * D * nkp;
 
+  u32x4 kreg[KPIECES], vreg[VPIECES];
+  // global -> registers (next tile) and registers -> LDS; plain code so that the
+  // staging arrays stay in registers
+#define PS_PF_GLOAD(KT)                                                                              \
+  do {                                                                                              \
+    _Pragma("unroll") for (int p = 0; p < KPIECES; ++p) {                                           \
+      const int piece = tid + 256 * p;                                                              \
+      kreg[p] = *reinterpret_cast<const u32x4*>(kr + ((int64_t)(KT) * BN + piece / (D / 8)) * D +   \
+                                                (piece % (D / 8)) * 8);                             \
+    }                                                                                               \
+    _Pragma("unroll") for (int p = 0; p < VPIECES; ++p) {                                           \
+      const int piece = tid + 256 * p;                                                              \
+      vreg[p] = *reinterpret_cast<const u32x4*>(vt + (int64_t)(piece / (BN / 8)) * nkp +            \
+                                                (int64_t)(KT) * BN + (piece % (BN / 8)) * 8);       \
+    }                                                                                               \
+  } while (0)
+#define PS_PF_LSTORE(BUF)                                                                            \
+  do {                                                                                              \
+    _Pragma("unroll") for (int p = 0; p < KPIECES; ++p) {                                           \
+      const int piece = tid + 256 * p;                                                              \
+      *reinterpret_cast<u32x4*>(&k_lds[BUF][(piece / (D / 8)) * KPAD + (piece % (D / 8)) * 8]) =    \
+          kreg[p];                                                                                  \
+    }                                                                                               \
+    _Pragma("unroll") for (int p = 0; p < VPIECES; ++p) {                                           \
+      const int piece = tid + 256 * p;                                                              \
+      *reinterpret_cast<u32x4*>(&v_lds[BUF][(piece / (BN / 8)) * VPAD + (piece % (BN / 8)) * 8]) =  \
+          vreg[p];                                                                                  \
+    }                                                                                               \
+  } while (0)
+
+  const TileRange tr = pf_tile_range(geo, it.qt);
+  const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
+  auto cand_tile = [&](int32_t ci) { return ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix); };
+
+  int32_t ci = 0;
+  int kind = 0;
+  while (ci < n_cand && (kind = pf_classify(geo, it.qt, cand_tile(ci))) == 0) ++ci;
+  if (ci < n_cand) PS_PF_GLOAD(cand_tile(ci));   // in flight while the query prologue runs
+
   // ---- query operand (B of S^T = K Q^T): query row t, dims 16*ks + 8*hf + e ----
   const int32_t t = it.qt * BM + wave * 32 + col;
   const bool row_ok = t < a.num_q;
@@ -322,48 +423,11 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
   float ref = 0.f;     // reference max (log2 units)
   float l_run = 0.f;   // lane-local partial sum of exp2(s - ref)
+  f32x16 negref;       // -ref in every register: initial value of the S accumulators
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negref[i] = 0.f;
 
-  u32x4 kreg[KPIECES], vreg[VPIECES];
-  // global -> registers (next tile) and registers -> LDS; plain code so that the
-  // staging arrays stay in registers
-#define PS_PF_GLOAD(KT)                                                                              \
-  do {                                                                                              \
-    _Pragma("unroll") for (int p = 0; p < KPIECES; ++p) {                                           \
-      const int piece = tid + 256 * p;                                                              \
-      kreg[p] = *reinterpret_cast<const u32x4*>(kr + ((int64_t)(KT) * BN + piece / (D / 8)) * D +   \
-                                                (piece % (D / 8)) * 8);                             \
-    }                                                                                               \
-    _Pragma("unroll") for (int p = 0; p < VPIECES; ++p) {                                           \
-      const int piece = tid + 256 * p;                                                              \
-      vreg[p] = *reinterpret_cast<const u32x4*>(vt + (int64_t)(piece / (BN / 8)) * nkp +            \
-                                                (int64_t)(KT) * BN + (piece % (BN / 8)) * 8);       \
-    }                                                                                               \
-  } while (0)
-#define PS_PF_LSTORE(BUF)                                                                            \
-  do {                                                                                              \
-    _Pragma("unroll") for (int p = 0; p < KPIECES; ++p) {                                           \
-      const int piece = tid + 256 * p;                                                              \
-      *reinterpret_cast<u32x4*>(&k_lds[BUF][(piece / (D / 8)) * KPAD + (piece % (D / 8)) * 8]) =    \
-          kreg[p];                                                                                  \
-    }                                                                                               \
-    _Pragma("unroll") for (int p = 0; p < VPIECES; ++p) {                                           \
-      const int piece = tid + 256 * p;                                                              \
-      *reinterpret_cast<u32x4*>(&v_lds[BUF][(piece / (BN / 8)) * VPAD + (piece % (BN / 8)) * 8]) =  \
-          vreg[p];                                                                                  \
-    }                                                                                               \
-  } while (0)
-
-  const TileRange tr = pf_tile_range(geo, it.qt);
-  const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
-  auto cand_tile = [&](int32_t ci) { return ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix); };
-
-  int32_t ci = 0;
-  int kind = 0;
-  while (ci < n_cand && (kind = pf_classify(geo, it.qt, cand_tile(ci))) == 0) ++ci;
-  if (ci < n_cand) {
-    PS_PF_GLOAD(cand_tile(ci));
-    PS_PF_LSTORE(0);
-  }
+  if (ci < n_cand) PS_PF_LSTORE(0);
   __syncthreads();
   int buf = 0;
   while (ci < n_cand) {
@@ -374,37 +438,57 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
     while (cn < n_cand && (nkind = pf_classify(geo, it.qt, cand_tile(cn))) == 0) ++cn;
     if (cn < n_cand) PS_PF_GLOAD(cand_tile(cn));  // next tile's loads are in flight during this tile's math
 
-    // ---- S^T - ref = K Q^T + (-ref): two 32-key M-tiles ----
+    // ---- S^T - ref = K Q^T + (-ref): two 32-key M-tiles; the operands of
+    // k-step ks+1 are read from LDS while the MFMAs of k-step ks run ----
     f32x16 st[2];
-#pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st[m2][i] = -ref;
-      const uint16_t* krow = &k_lds[buf][(32 * m2 + col) * KPAD + 8 * hf];
+    {
+      const uint16_t* k0row = &k_lds[buf][col * KPAD + 8 * hf];
+      const uint16_t* k1row = k0row + 32 * KPAD;
+      bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(k0row);
+      bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(k1row);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
-        st[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], st[m2], 0, 0, 0);
+        bf16x8 kb0 = ka0, kb1 = ka1;
+        if (ks + 1 < KS) {
+          kb0 = *reinterpret_cast<const bf16x8*>(k0row + 16 * (ks + 1));
+          kb1 = *reinterpret_cast<const bf16x8*>(k1row + 16 * (ks + 1));
+        }
+        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qop[ks], ks == 0 ? negref : st[0], 0, 0, 0);
+        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qop[ks], ks == 0 ? negref : st[1], 0, 0, 0);
+        ka0 = kb0;
+        ka1 = kb1;
       }
     }
     // key of register i of tile m2: kt*BN + 32*m2 + 8*(i/4) + 4*hf + i%4
     if (cur_kind == 2) {
       const int32_t kbase = kt * BN + 4 * hf;
+      if (kt * BN >= a.prefix_len && kt * BN + BN <= a.num_k) {
+        // chunk keys only, all in range: visible iff 0 <= u - key < W, one unsigned compare
+        const uint32_t rel = (uint32_t)(row_ok ? u - kbase : -1 - a.window);
 #pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2)
+        for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int32_t key = kbase + 32 * m2 + 8 * (i >> 2) + (i & 3);
-          const bool vis = key < pre_end || (uint32_t)(key - band_lo) <= band_w;
-          if (!vis) st[m2][i] = -INFINITY;
-        }
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t off = 32 * m2 + 8 * (i >> 2) + (i & 3);
+            if (rel - off >= (uint32_t)a.window) st[m2][i] = -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int32_t key = kbase + 32 * m2 + 8 * (i >> 2) + (i & 3);
+            const bool vis = key < pre_end || (uint32_t)(key - band_lo) <= band_w;
+            if (!vis) st[m2][i] = -INFINITY;
+          }
+      }
     }
     float mx = st[0][0];
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
       for (int i = (m2 == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, st[m2][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_xor32(mx);
     // rare path (wave-uniform branch): this tile's max exceeds the reference by
     // more than kRebase -> move the reference up and rescale what is accumulated
     if (__any(mx > kRebase)) {
@@ -414,15 +498,17 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
       ref += shift;
+      negref -= shift;
 #pragma unroll
       for (int m2 = 0; m2 < 2; ++m2) st[m2] -= shift;
     }
     // nothing accumulated yet and every score far below the reference: move it
     // down so the first probabilities do not underflow (no rescale needed)
     if (__any(mx < -kRebaseLow)) {
-      const float ltot = l_run + __shfl_xor(l_run, 32, 64);
+      const float ltot = sum_xor32(l_run);
       const float shift = (ltot == 0.f && mx < -kRebaseLow && mx != -INFINITY) ? mx : 0.f;
       ref += shift;
+      negref -= shift;
 #pragma unroll
       for (int m2 = 0; m2 < 2; ++m2) st[m2] -= shift;
     }
@@ -438,14 +524,24 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
       }
     l_run += psum;
 
-    // ---- O^T += V^T P^T: PV k-step j covers keys 16j + 8*(e/4) + 4*hf + e%4 ----
+    // ---- O^T += V^T P^T: PV k-step j covers keys 16j + 8*(e/4) + 4*hf + e%4;
+    // the V^T operands of step j+1 are read while step j's MFMAs run ----
+    {
+      const uint16_t* vrow = &v_lds[buf][col * VPAD + 8 * hf];
+      bf16x8 va[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint16_t* vrow = &v_lds[buf][(32 * mt + col) * VPAD + 8 * hf];
+      for (int mt = 0; mt < MT; ++mt) va[mt] = *reinterpret_cast<const bf16x8*>(vrow + 32 * mt * VPAD);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vrow + 16 * j);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[j], acc[mt], 0, 0, 0);
+        bf16x8 vb[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          vb[mt] = (j + 1 < 4) ? *reinterpret_cast<const bf16x8*>(vrow + 32 * mt * VPAD + 16 * (j + 1)) : va[mt];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mt], pop[j], acc[mt], 0, 0, 0);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) va[mt] = vb[mt];
       }
     }
     if (cn < n_cand) PS_PF_LSTORE(buf ^ 1);
@@ -459,7 +555,7 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
 #undef PS_PF_LSTORE
 
   // ---- epilogue: l across the two halves, normalise, store ----
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = sum_xor32(l_run);
   if (!row_ok) return;
   const float inv = 1.f / l_run;
   uint16_t* orow = static_cast<uint16_t*>(a.out) + (((int64_t)it.b * a.num_q + t) * a.hq + it.hq) * D;
