@@ -48,8 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-full", action="store_true")
-    ap.add_argument("--kernel-reps", type=int, default=50)
-    ap.add_argument("--sweep", action="store_true", help="also time decode at a sweep of positions (flatness)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the decode position sweep (flatness)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other decode workloads")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="run only one leg (for profiling); the JSON line then carries that leg only")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -153,7 +153,7 @@ def timed(torch, fn, iters):
 
 def run_decode(ps, torch, args):
     bench = DecodeBench(ps, torch, args.num_seqs, args.layers, args.window, 100, args.position, args.splits)
-    bench.prepare_positions(args.warmup + args.steps)
+    bench.prepare_positions(args.warmup + 2 * args.steps)
     splits = args.splits or ps.ps_decode_num_splits(bench.attn, bench.cache, args.num_seqs)
     for s in range(args.warmup):
         bench.step(s)
@@ -169,33 +169,42 @@ def run_decode(ps, torch, args):
     wall = time.perf_counter() - t0
     gpu_s = start.elapsed_time(end) / 1000.0
     elapsed = max(wall, gpu_s)
-    # dominant kernel: decode attention of one layer, back to back, HIP events on the launch stream
-    p_last = args.position + args.warmup + args.steps - 1
-    pos = bench.pos[-1]
-    bench.decode_only(5, pos)
-    kt = timed(torch, lambda n: bench.decode_only(n, pos), args.kernel_reps) / args.kernel_reps
+    # dominant kernel: the decode-attention launches of the step loop.  The
+    # timed steps are replayed once more (same workload, next positions) with a
+    # pair of HIP events on the launch stream around every decode launch; the
+    # average is the kernel's in-step launch duration.  `value` above comes
+    # from the plain, un-instrumented steps.
+    n_steps = args.steps
+    evs = []
+    torch.cuda.synchronize()
+    for s_ in range(args.warmup + args.steps, args.warmup + 2 * args.steps):
+        pos = bench.pos[s_]
+        for li in range(bench.layers):
+            i = (s_ * bench.layers + li) % bench.pool
+            ps.ps_kv_append(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, pos, bench.kn[i], bench.vn[i])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ps.ps_decode_attn(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, pos, bench.q[i], bench.out,
+                              num_splits=bench.splits, workspace=bench.ws)
+            e1.record()
+            evs.append((e0, e1))
+    torch.cuda.synchronize()
+    kt = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs) / 1000.0
+    p_last = args.position + args.warmup + 2 * args.steps - 1
     kbytes = bench.kernel_bytes(p_last)
     res = {
         "tok_s": args.num_seqs * args.steps / elapsed,
         "ms_per_step": elapsed / args.steps * 1000.0,
         "splits": splits,
         "kernel_s": kt,
+        "kernel_launches": len(evs),
         "kernel_bytes": kbytes,
         "n_vis": bench.n_vis(p_last),
     }
-    sweep = []
-    if args.sweep:
-        for p in (1024, 2048, 4196, 8192, 16384, 32768, 65536, 131072, 262144):
-            pt = torch.full((args.num_seqs,), p, dtype=torch.int64, device="cuda")
-            if bench.n_vis(p) > bench.cache.slot_capacity:
-                continue
-            kt_p = timed(torch, lambda n: bench.decode_only(n, pt), 20) / 20
-            sweep.append({"position": p, "n_vis": bench.n_vis(p), "us_per_layer": kt_p * 1e6,
-                          "tok_s": args.num_seqs / (kt_p * args.layers)})
     bench.release()
     del bench
     torch.cuda.empty_cache()
-    return res, sweep
+    return res
 
 
 def run_full_attention(ps, torch, args, steps=2):
@@ -239,6 +248,107 @@ def run_full_attention(ps, torch, args, steps=2):
     return {"tok_s": n * steps / el, "ms_per_step": el / steps * 1e3, "position": p, "splits": splits,
             "hbm_gbs": nbytes * args.layers * steps / el / 1e9}
 
+
+
+SWEEP_POSITIONS = (1024, 2048, 4196, 8192, 16384, 32768, 65536, 131072, 262144)
+
+
+def run_sweep(ps, torch, num_seqs=256, layers=28, reps=10):
+    """Decode-kernel time per layer against query position for Prefix Sliding
+    (prefix 100, W=4096), plain sliding window (prefix 0, W=4096) and full
+    attention (W >= n), all the same kernel.  tok/s = sequences / (layers x
+    per-layer time).  Bounded methods go flat once the position passes L+W."""
+    attn = ps.AttnSpec(16, 2, 128, ps.PS_BF16, 10000.0, 1 / math.sqrt(128))
+    g = torch.Generator(device="cuda").manual_seed(9)
+    q = torch.randn((num_seqs, 16, 128), generator=g, device="cuda").bfloat16()
+    out = torch.empty_like(q)
+    rows = {}
+    for label, prefix, window, cap in (("prefix_sliding", 100, 4096, 4224), ("sliding_window", 0, 4096, 4096),
+                                       ("full", 0, 1 << 30, -(-(max(SWEEP_POSITIONS) + 1) // 64) * 64)):
+        cache = ps.CacheSpec(window=window, slot_capacity=cap)
+        ks, vs = ps.cache_shapes(attn, cache, num_seqs)
+        k = torch.empty(ks, dtype=torch.bfloat16, device="cuda").normal_(0, 0.5, generator=g)
+        v = torch.empty(vs, dtype=torch.bfloat16, device="cuda").normal_(0, 0.5, generator=g)
+        pl = torch.full((num_seqs,), prefix, dtype=torch.int32, device="cuda")
+        ws = torch.empty(max(ps.ps_decode_workspace_size(attn, cache, num_seqs, 0), 1), dtype=torch.uint8,
+                         device="cuda")
+        res = []
+        for p in SWEEP_POSITIONS:
+            pos = torch.full((num_seqs,), p, dtype=torch.int64, device="cuda")
+            run = lambda kk: [ps.ps_decode_attn(attn, cache, k, v, pl, pos, q, out, workspace=ws) for _ in range(kk)]
+            run(2)
+            t = timed(torch, run, reps) / reps
+            n_vis = min(p + 1, prefix + window)
+            nbytes = num_seqs * (n_vis * 2 * 128 * 2 * 2 + 16 * 128 * 4)
+            res.append({"position": p, "n_vis": n_vis, "us_per_layer": round(t * 1e6, 2),
+                        "tok_s": round(num_seqs / (t * layers), 1), "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)})
+        rows[label] = res
+        del k, v, ws
+        torch.cuda.empty_cache()
+    return rows
+
+
+# ------------------------------------------------------------------------- other decode workloads
+def run_decode_extra(ps, torch, layers=28, reps=30):
+    """Per-layer decode-kernel time of the other decode workloads (one layer's
+    cache each; tok/s assumes `layers` layers of decode attention per token):
+    64 sequences at 32768 (W=4096), 256 at 131072 with W=8192, and the ragged
+    paged batch of 1024 sequences (positions 1024..262144, prefixes 50..2000)."""
+    import numpy as np
+    import synth
+    out = {}
+    for name, n, p, W in (("decode-32768-w4096-64seq", 64, 32768, 4096),
+                          ("decode-131072-w8192", 256, 131072, 8192)):
+        b = DecodeBench(ps, torch, n, 1, W, 100, p, 0, pool=4)
+        pos = torch.full((n,), p, dtype=torch.int64, device="cuda")
+        b.decode_only(3, pos)
+        t = timed(torch, lambda k: b.decode_only(k, pos), reps) / reps
+        out[name] = {"us_per_layer": t * 1e6, "hbm_gbs": b.kernel_bytes(p) / t / 1e9,
+                     "hbm_frac": b.kernel_bytes(p) / t / 1e9 / HBM_PEAK_GBS,
+                     "tok_s_attention_only": n / (t * layers),
+                     "splits": ps.ps_decode_num_splits(b.attn, b.cache, n)}
+        b.release()
+        del b
+        torch.cuda.empty_cache()
+    # ragged paged batch
+    c = synth.C5_DECODE
+    n = c.num_seqs
+    pos_np, pre_np = synth.ragged_draws(0, n)
+    ring = [min(int(pos_np[s]) + 1, int(pre_np[s]) + c.window) for s in range(n)]
+    cap = -(-max(int(pre_np[s]) + c.window for s in range(n)) // 64) * 64
+    pages = [-(-r // 64) for r in ring]
+    num_pages = int(sum(pages))
+    perm = synth.page_permutation(0, num_pages)
+    table = np.full((n, cap // 64), -1, dtype=np.int32)
+    o = 0
+    for s_ in range(n):
+        table[s_, :pages[s_]] = perm[o:o + pages[s_]]
+        o += pages[s_]
+    attn = ps.AttnSpec(16, 2, 128, ps.PS_BF16, 10000.0, 1 / math.sqrt(128))
+    cache = ps.CacheSpec(window=c.window, slot_capacity=cap, page_size=64, num_pages=num_pages)
+    ks, vs = ps.cache_shapes(attn, cache, n)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    k = torch.empty(ks, dtype=torch.bfloat16, device="cuda").normal_(0, 0.5, generator=g)
+    v = torch.empty(vs, dtype=torch.bfloat16, device="cuda").normal_(0, 0.5, generator=g)
+    bt = torch.from_numpy(table).cuda()
+    pl = torch.from_numpy(pre_np.astype(np.int32)).cuda()
+    pos = torch.from_numpy(pos_np.astype(np.int64)).cuda()
+    q = torch.randn((n, 16, 128), generator=g, device="cuda").bfloat16()
+    o_ = torch.empty_like(q)
+    ws = torch.empty(max(ps.ps_decode_workspace_size(attn, cache, n, 0), 1), dtype=torch.uint8, device="cuda")
+    run = lambda kk: [ps.ps_decode_attn(attn, cache, k, v, pl, pos, q, o_, block_table=bt, workspace=ws)
+                      for _ in range(kk)]
+    run(3)
+    t = timed(torch, run, reps) / reps
+    nbytes = sum(r * 2 * 128 * 2 * 2 + 16 * 128 * 4 + -(-r // 64) * 4 for r in ring)
+    out["decode-ragged-paged-1024seq"] = {"us_per_layer": t * 1e6, "hbm_gbs": nbytes / t / 1e9,
+                                          "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS,
+                                          "tok_s_attention_only": n / (t * layers),
+                                          "mean_n_vis": float(np.mean(ring)),
+                                          "splits": ps.ps_decode_num_splits(attn, cache, n)}
+    del k, v
+    torch.cuda.empty_cache()
+    return out
 
 # ------------------------------------------------------------------------- prefill
 def run_prefill(ps, torch, reps=10, full_causal=True):
@@ -349,13 +459,21 @@ def main():
     if args.only == "prefill":
         print(json.dumps({"prefill": run_prefill(ps, torch, full_causal=not args.no_full)}))
         return
-    dec, sweep = run_decode(ps, torch, args)
+    dec = run_decode(ps, torch, args)
     print(f"[bench] decode done: {dec['tok_s']:.0f} tok/s, kernel {dec['kernel_s'] * 1e6:.1f} us",
           file=sys.stderr, flush=True)
     prefill = None
     if not args.no_prefill and args.only is None:
         prefill = run_prefill(ps, torch)
         print(f"[bench] prefill done: {prefill}", file=sys.stderr, flush=True)
+    sweep = None
+    if not args.no_sweep and args.only is None:
+        sweep = run_sweep(ps, torch, num_seqs=args.num_seqs, layers=args.layers)
+        print(f"[bench] position sweep done", file=sys.stderr, flush=True)
+    extra = None
+    if not args.no_extra and args.only is None:
+        extra = run_decode_extra(ps, torch, layers=args.layers)
+        print(f"[bench] other decode workloads done", file=sys.stderr, flush=True)
     full = None
     if not args.no_full and args.only is None:
         full = run_full_attention(ps, torch, args)
@@ -380,11 +498,14 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(dec["kernel_bytes"]),
                      "kernel": "decode_bf16_kernel", "kernel_us": dec["kernel_s"] * 1e6,
+                     "kernel_launches_timed": dec["kernel_launches"],
                      "bytes_per_launch": dec["kernel_bytes"]},
         "cpu_baseline": cpu,
         "prefill": prefill,
         "full_attention": full,
     }
+    if extra:
+        line["decode_other_workloads"] = extra
     if sweep:
         line["sweep"] = sweep
     print(json.dumps(line))

@@ -81,41 +81,7 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
   const int nvis = bad ? 0 : (int)nvis64;
   const int kb = split * a.split_keys;
   const int ke = kb + a.split_keys < nvis ? kb + a.split_keys : nvis;
-
-  // ---- query operand: rotate at pos, fold in scale*log2(e), round to bf16 ----
-  bf16x8 qop[NC];
-  {
-    const int G = a.group;
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)s * a.hq + h * G + (r < G ? r : 0)) * D;
-    float qv[NC][8];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint4 w = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[c][2 * e] = (r < G) ? lo_bf16(ww[e]) : 0.f;
-        qv[c][2 * e + 1] = (r < G) ? hi_bf16(ww[e]) : 0.f;
-      }
-    }
-    if (a.rope.enabled) {
-#pragma unroll
-      for (int c = 0; c < NC / 2; ++c) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float cs, sn;
-          rope_cos_sin(pos, a.rope.inv_freq[32 * c + 8 * g + i], cs, sn);
-          const float x1 = qv[c][i], x2 = qv[c + NC / 2][i];
-          qv[c][i] = x1 * cs - x2 * sn;
-          qv[c + NC / 2][i] = x2 * cs + x1 * sn;
-        }
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qop[c][i] = (bf16)(qv[c][i] * a.scale_log2);
-  }
+  bf16x8 qop[NC];   // query operand, filled after the first chunk's loads are issued
 
   // ---- per-lane load offsets inside a 32-key chunk (elements) ----
   // K tile t, row r -> key 8*(r/4) + 4t + r%4; k-step c covers dims 32c + 8g .. +8
@@ -140,9 +106,35 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
 
   u32x4 kA[2][NC], vA[NDT], kB[2][NC], vB[NDT];
 
+  // Paged cache: the page ids of this split's first 128 segments are fetched
+  // once (one coalesced load per 64 pages) and picked per chunk with a lane
+  // read, so a chunk's K/V loads never wait on a block-table load.
+  const int seg0 = kb >> 6;
+  int32_t page_cache[2] = {-1, -1};
+  if (geo.paged) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int seg = seg0 + 64 * j + lane;
+      if (seg < geo.max_pages) page_cache[j] = a.block_table[(int64_t)s * geo.max_pages + seg];
+    }
+  }
+  auto chunk_base = [&](int key0) -> int64_t {
+    if (!geo.paged) return region_offset(geo, a.block_table, s, h, key0);
+    const int rel = (key0 >> 6) - seg0;
+    int32_t page;
+    if (rel < 64)
+      page = __builtin_amdgcn_readlane(page_cache[0], rel);
+    else if (rel < 128)
+      page = __builtin_amdgcn_readlane(page_cache[1], rel - 64);
+    else
+      page = a.block_table[(int64_t)s * geo.max_pages + (key0 >> 6)];
+    if (page < 0 || (int64_t)page >= geo.num_pages) return -1;
+    return ((int64_t)page * geo.hkv + h) * (int64_t)(kRegionSlots * D);
+  };
+
   auto load_chunk = [&](int ci, u32x4 (&kr)[2][NC], u32x4 (&vr)[NDT]) {
     const int key0 = ci << 5;
-    const int64_t base = region_offset(geo, a.block_table, s, h, key0);
+    const int64_t base = chunk_base(key0);
     if (base < 0) {
       bad = true;
 #pragma unroll
@@ -221,7 +213,41 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vr[dt]), pop, acc[dt], 0, 0, 0);
   };
 
-  if (c < c_end) load_chunk(c, kA, vA);
+  if (c < c_end) load_chunk(c, kA, vA);   // the first chunk is in flight during the query prologue
+  // ---- query operand: rotate at pos, fold in scale*log2(e), round to bf16 ----
+  {
+    const int G = a.group;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)s * a.hq + h * G + (r < G ? r : 0)) * D;
+    float qv[NC][8];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[c][2 * e] = (r < G) ? lo_bf16(ww[e]) : 0.f;
+        qv[c][2 * e + 1] = (r < G) ? hi_bf16(ww[e]) : 0.f;
+      }
+    }
+    if (a.rope.enabled) {
+#pragma unroll
+      for (int c = 0; c < NC / 2; ++c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float cs, sn;
+          rope_cos_sin(pos, a.rope.inv_freq[32 * c + 8 * g + i], cs, sn);
+          const float x1 = qv[c][i], x2 = qv[c + NC / 2][i];
+          qv[c][i] = x1 * cs - x2 * sn;
+          qv[c + NC / 2][i] = x2 * cs + x1 * sn;
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qop[c][i] = (bf16)(qv[c][i] * a.scale_log2);
+  }
+
   while (c < c_end) {
     if (c + NW < c_end) load_chunk(c + NW, kB, vB);
     compute_chunk(c, kA, vA);
