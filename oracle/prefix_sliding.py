@@ -37,6 +37,9 @@ the pages; no page is quoted):
   "超长 rollouts 的反向传播：截断回传"): keys are the prefix followed by a chunk
   of consecutive positions starting at ``kv_start``; queries are the last T
   keys; nothing before the chunk other than the prefix exists.
+* Chunk continuing a trace (``chunk_prefill_attention``): queries at
+  start..start+T-1 over the whole history; the ring supplies what the earlier
+  trace left visible, so the result is again plain masked attention.
 * Tile plan (blog section "Kernel 实现：两层级过滤"): tiles with no visible pair
   are skipped, tiles whose every pair is visible need no element mask, the
   rest are partial.  The oracle decides this by enumerating every element.
@@ -210,6 +213,42 @@ def prefill_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, prefix_len: i
         kv = h // g
         s = scale * (qr[:, h, :] @ kr[:, kv, :].T)
         w, l = _masked_softmax_rows(s, mask)
+        out[:, h, :] = w @ v[:, kv, :]
+        lse[:, h] = l
+    return out, lse
+
+
+def chunk_prefill_attention(q: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray, start: int,
+                            prefix_len: int, window: int, scale: float, theta: float, rows=None):
+    """A chunk of T new tokens continues a trace: query t sits at absolute
+    position ``start + t`` and attends, under A(i), to the whole history
+    0..start+t -- the earlier trace and the chunk up to itself.  Blog
+    "Prefix Sliding 完全拆解", mask section (A(i) for every generated or
+    appended token); the case arises when long external content is poured into
+    a live trace (the blog's limitations section, multi-turn / tool output).
+
+    q: raw [T, Hq, D]; k_hist, v_hist: raw [start + T, Hkv, D] (positions
+    0..start+T-1, hidden ones included).  ``rows`` optionally limits the
+    evaluation to some chunk queries.  Returns (out [R, Hq, D], lse [R, Hq])
+    in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    t_all, hq, d = q.shape
+    n = start + t_all
+    hkv = k_hist.shape[1]
+    g = hq // hkv
+    rows = np.arange(t_all) if rows is None else np.asarray(rows, dtype=np.int64)
+    t_q = rows.size
+    posq = start + rows
+    posk = np.arange(n, dtype=np.int64)
+    qr = rope(q[rows], posq[:, None], theta)
+    kr = rope(np.asarray(k_hist[:n], dtype=np.float64), posk[:, None], theta)
+    v = np.asarray(v_hist[:n], dtype=np.float64)
+    mask = visible(posq[:, None], posk[None, :], prefix_len, window)
+    out = np.empty((t_q, hq, d), dtype=np.float64)
+    lse = np.empty((t_q, hq), dtype=np.float64)
+    for h in range(hq):
+        kv = h // g
+        w, l = _masked_softmax_rows(scale * (qr[:, h, :] @ kr[:, kv, :].T), mask)
         out[:, h, :] = w @ v[:, kv, :]
         lse[:, h] = l
     return out, lse

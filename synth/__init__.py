@@ -160,6 +160,32 @@ C5_DECODE = DecodeConfig("c5-ragged-paged", 5, num_seqs=1024, layers=28, hq=16, 
                          q_std=1.0, kv_std=0.5, ragged=True, page_size=64)
 
 
+@dataclasses.dataclass(frozen=True)
+class ChunkConfig:
+    """A chunk of new tokens continuing cached traces (ring + chunk attention)."""
+    name: str
+    cfg_id: int
+    num_seqs: int
+    hq: int
+    hkv: int
+    dim: int
+    dtype: str
+    prefix: int
+    window: int
+    position: int        # P: first chunk position (the ring holds positions < P)
+    chunk: int           # T: chunk tokens
+    q_std: float = 1.0
+    kv_std: float = 0.5
+    rope_theta: float = 10000.0
+    page_size: int = 0
+
+
+# Long external content (a tool output) poured into 64 live Qwen3-1.7B-shaped
+# traces at 32768: L=100, W=4096, 2048-token chunk.
+C6_CHUNK = ChunkConfig("c6-chunk-32k", 6, num_seqs=64, hq=16, hkv=2, dim=128, dtype="bf16", prefix=100,
+                       window=4096, position=32768, chunk=2048)
+
+
 def ragged_draws(seed: int, num_seqs: int, p_lo: int = 1024, p_hi: int = 262144,
                  l_lo: int = 50, l_hi: int = 2000):
     """Per-sequence query positions and prefix lengths, integer-uniform and inclusive."""

@@ -20,6 +20,9 @@ PIN_CHECKS = [
     lambda: pins.test_rope_frequencies_and_pairing(),
     lambda: pins.test_tile_plan_hand_worked_cases(),
     lambda: pins.test_zero_query_gives_mean_of_visible_values(4, 6),
+    lambda: pins.test_chunk_reduces_to_reference_attention(3, 6, 25, 12),
+    lambda: pins.test_chunk_rows_match_decode_with_rotation(),
+    lambda: pins.test_chunk_zero_query_gives_mean_of_visible_values(3, 5, 40),
 ]
 
 
@@ -74,6 +77,18 @@ def _decode_interleaved_gqa(q, k_hist, v_hist, p, L, W, scale, theta):
 
 
 ORIG_DECODE = ops.decode_attention
+ORIG_CHUNK = ops.chunk_prefill_attention
+
+
+def _chunk_forgets_trace(q, k_hist, v_hist, start, L, W, scale, theta):
+    # attends to the chunk alone, as if it started a new sequence
+    return ORIG_CHUNK(q, k_hist[start:], v_hist[start:], 0, L, W, scale, theta)
+
+
+def _chunk_query_one_early(q, k_hist, v_hist, start, L, W, scale, theta):
+    # query t placed at start + t - 1 (its own key falls outside its view)
+    s = max(start - 1, 0)
+    return ORIG_CHUNK(q, k_hist[:s + q.shape[0]], v_hist[:s + q.shape[0]], s, L, W, scale, theta)
 
 MUTANTS = {
     "window-off-by-one": ("visible", _window_off_by_one),
@@ -82,6 +97,8 @@ MUTANTS = {
     "rope-sign-flip": ("rope", _rope_sign_flip),
     "rope-wrong-frequency": ("rope", _rope_wrong_freq),
     "gqa-interleaved": ("decode_attention", _decode_interleaved_gqa),
+    "chunk-forgets-trace": ("chunk_prefill_attention", _chunk_forgets_trace),
+    "chunk-query-one-early": ("chunk_prefill_attention", _chunk_query_one_early),
 }
 
 

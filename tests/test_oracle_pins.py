@@ -269,6 +269,63 @@ def test_prefill_lse_matches_direct_sum():
             assert abs(lse[t, h] - want) < 1e-12
 
 
+# ---------------------------------------------------------------- chunk continuing a trace
+@pytest.mark.parametrize("L,W,start,T", [(0, 1 << 20, 20, 17), (3, 6, 0, 37), (3, 6, 25, 12), (4, 9, 2, 30),
+                                         (40, 3, 10, 20), (0, 1, 30, 7)])
+def test_chunk_reduces_to_reference_attention(L, W, start, T):
+    # no rotation: the chunk rows are the last T rows of plain band attention
+    rs = np.random.default_rng(5)
+    n, hq, hkv, d = start + T, 6, 2, 16
+    q = rs.standard_normal((T, hq, d))
+    k = rs.standard_normal((n, hkv, d))
+    v = rs.standard_normal((n, hkv, d))
+    got, _ = oracle.chunk_prefill_attention(q, k, v, start, L, W, 0.25, 0.0)
+    mask = _band_mask(n, min(L, n), W)[start:]
+    want_q = np.zeros((n, hq, d))
+    want_q[start:] = q
+    want = _sdpa(want_q, k, v, _band_mask(n, min(L, n), W), 0.25)[start:]
+    assert mask.shape == (T, n)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_chunk_rows_match_decode_with_rotation():
+    rs = np.random.default_rng(6)
+    L, W, start, T = 5, 11, 23, 19
+    k = rs.standard_normal((start + T, 2, 8))
+    v = rs.standard_normal((start + T, 2, 8))
+    q = rs.standard_normal((T, 4, 8))
+    got, _ = oracle.chunk_prefill_attention(q, k, v, start, L, W, 0.4, 10000.0)
+    for t in range(T):
+        dec = oracle.decode_attention(q[t], k, v, start + t, L, W, 0.4, 10000.0)
+        np.testing.assert_allclose(got[t], dec, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("L,W,start", [(3, 5, 40), (10, 4, 3), (0, 7, 15), (6, 100, 50)])
+def test_chunk_zero_query_gives_mean_of_visible_values(L, W, start):
+    # q = 0 -> uniform weights over A(p) for every chunk query p = start + t;
+    # v_j = (1, j, j^2) makes the output the count-normalised first and second
+    # moments of the visible positions, summed here in closed form
+    T, d = 25, 4
+    n = start + T
+    j = np.arange(n, dtype=np.float64)
+    v = np.zeros((n, 1, d))
+    v[:, 0, 0], v[:, 0, 1], v[:, 0, 2] = 1.0, j, j * j
+    k = np.random.default_rng(start).standard_normal((n, 1, d))
+    got, lse = oracle.chunk_prefill_attention(np.zeros((T, 2, d)), k, v, start, L, W, 1.0, 10000.0)
+    s1 = lambda a, b: (b - a) * (a + b - 1) / 2 if b > a else 0.0
+    f2 = lambda m: (m - 1) * m * (2 * m - 1) / 6
+    s2 = lambda a, b: f2(b) - f2(a) if b > a else 0.0
+    for t in range(T):
+        p = start + t
+        a = min(L, p + 1)
+        b = max(p - W + 1, a)
+        cnt = a + (p + 1 - b)
+        want = [1.0, (s1(0, a) + s1(b, p + 1)) / cnt, (s2(0, a) + s2(b, p + 1)) / cnt, 0.0]
+        np.testing.assert_allclose(got[t, 0], want, rtol=1e-13)
+        np.testing.assert_allclose(got[t, 1], want, rtol=1e-13)
+        assert abs(lse[t, 0] - math.log(cnt)) < 1e-12   # all scores 0: lse = log(count)
+
+
 # ---------------------------------------------------------------- tile plan
 def test_tile_plan_hand_worked_cases():
     for case in _golden("tile_plan_small.json")["cases"]:
