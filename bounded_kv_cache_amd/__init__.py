@@ -19,6 +19,7 @@ from . import _lib
 from ._lib import PS_BF16, PS_F32, PSError
 
 __all__ = ["AttnSpec", "CacheSpec", "PSError", "ps_kv_append", "ps_decode_attn", "ps_prefill_attn",
+           "ps_chunk_prefill_attn", "ps_chunk_prefill_workspace_size",
            "ps_prefill_plan", "ps_decode_workspace_size", "ps_decode_num_splits", "ps_prefill_workspace_size",
            "ps_prefill_tile_shape", "ps_abi_version", "cache_shapes", "PS_BF16", "PS_F32"]
 
@@ -185,6 +186,47 @@ def ps_prefill_attn(attn: AttnSpec, window: int, prefix_len: int, kv_start: int,
     _lib.check(_lib.load().ps_prefill_attn(ctypes.byref(a), window, prefix_len, kv_start, _ptr(q), _ptr(k), _ptr(v),
                                            batch, num_q, num_k, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                            _stream(stream)))
+    return out
+
+
+def ps_chunk_prefill_workspace_size(attn: AttnSpec, cache: CacheSpec, num_seqs: int, chunk_len: int) -> int:
+    a, c = attn.c(), cache.c()
+    return _lib.load().ps_chunk_prefill_workspace_size(ctypes.byref(a), ctypes.byref(c), num_seqs, chunk_len)
+
+
+def ps_chunk_prefill_attn(attn: AttnSpec, cache: CacheSpec, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          prefix_len: torch.Tensor, start_pos: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                          v_new: torch.Tensor, out: torch.Tensor, *, block_table: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None, slot_pos: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Chunk q/k_new/v_new [num_seqs, T, H, D] at positions start_pos[s] + t: attention over each ring plus
+    the chunk (writes out [num_seqs, T, Hq, D]), then the chunk is appended to the rings."""
+    dt = attn.torch_dtype
+    num_seqs, chunk = q.shape[0], q.shape[1]
+    _need(q, "q", dt, num_seqs * chunk * attn.num_q_heads * attn.head_dim)
+    _need(k_new, "k_new", dt, num_seqs * chunk * attn.num_kv_heads * attn.head_dim)
+    _need(v_new, "v_new", dt, k_new.numel())
+    _need(out, "out", dt, q.numel())
+    ks, vs = cache_shapes(attn, cache, num_seqs)
+    _need(k_cache, "k_cache", dt, math.prod(ks))
+    _need(v_cache, "v_cache", dt, math.prod(vs))
+    _need(prefix_len, "prefix_len", torch.int32, num_seqs)
+    _need(start_pos, "start_pos", torch.int64, num_seqs)
+    if block_table is not None:
+        _need(block_table, "block_table", torch.int32, num_seqs * (cache.slot_capacity // 64))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, num_seqs * attn.num_q_heads * chunk)
+    if slot_pos is not None:
+        _need(slot_pos, "slot_pos", torch.int32, num_seqs * cache.slot_capacity)
+    need = ps_chunk_prefill_workspace_size(attn, cache, num_seqs, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    a, c = attn.c(), cache.c()
+    _lib.check(_lib.load().ps_chunk_prefill_attn(ctypes.byref(a), ctypes.byref(c), _ptr(k_cache), _ptr(v_cache),
+                                                 _ptr(block_table), _ptr(prefix_len), _ptr(start_pos), chunk,
+                                                 _ptr(q), _ptr(k_new), _ptr(v_new), num_seqs, _ptr(out), _ptr(lse),
+                                                 _ptr(slot_pos), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

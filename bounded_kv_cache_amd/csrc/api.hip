@@ -151,6 +151,19 @@ size_t prefill_ws_bytes(const ps_attn_desc* a, int32_t batch, int32_t num_q, int
   return ((kv + 255) / 256) * 256 + table;
 }
 
+// Chunk prefill workspace: K / V^T copies of every sequence's key array (keys
+// padded to pad64(slot_capacity + T)) and the rotated queries.
+size_t chunk_nkp(const ps_cache_desc* c, int32_t chunk_len) {
+  return ((size_t)c->slot_capacity + chunk_len + 63) / 64 * 64;
+}
+
+size_t chunk_ws_bytes(const ps_attn_desc* a, const ps_cache_desc* c, int32_t num_seqs, int32_t chunk_len) {
+  const size_t elem = a->dtype == PS_BF16 ? 2 : 4;
+  const size_t kv = 2 * (size_t)num_seqs * a->num_kv_heads * chunk_nkp(c, chunk_len) * a->head_dim * elem;
+  const size_t qr = (size_t)num_seqs * chunk_len * a->num_q_heads * a->head_dim * elem;
+  return ((kv + 255) / 256) * 256 + ((qr + 255) / 256) * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -311,7 +324,99 @@ ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t pref
   a.rope_cs = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((kv + 255) / 256) * 256);
   a.scale_log2 = attn->softmax_scale * 1.4426950408889634f;
   a.rope = make_rope(attn);
+  a.nkp = (int32_t)nkp;
+  a.seq_prefix = nullptr;
+  a.seq_start = nullptr;
+  a.k_cache = nullptr;
+  a.v_cache = nullptr;
+  a.block_table = nullptr;
+  a.cg = ps::CacheGeom{};
+  a.q_rot = nullptr;
   return from_hip(ps::launch_prefill(a, stream), "ps_prefill_attn launch");
+}
+
+size_t ps_chunk_prefill_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* cache, int32_t num_seqs,
+                                       int32_t chunk_len) {
+  if (check_attn(attn) != PS_OK || !cache || cache->slot_capacity <= 0 || num_seqs < 0 || chunk_len < 0) return 0;
+  return chunk_ws_bytes(attn, cache, num_seqs, chunk_len);
+}
+
+ps_status ps_chunk_prefill_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, void* k_cache, void* v_cache,
+                                const int32_t* block_table, const int32_t* prefix_len, const int64_t* start_pos,
+                                int32_t chunk_len, const void* q, const void* k_new, const void* v_new,
+                                int32_t num_seqs, void* out, float* lse, int32_t* slot_pos, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  ps_status st = check_attn(attn);
+  if (st != PS_OK) return st;
+  if ((st = check_cache(cache, block_table)) != PS_OK) return st;
+  if (num_seqs < 0 || chunk_len < 0) return fail(PS_INVALID_ARGUMENT, "negative num_seqs or chunk_len");
+  if (num_seqs == 0 || chunk_len == 0) return ok();
+  if (!k_cache || !v_cache || !prefix_len || !start_pos || !q || !k_new || !v_new || !out)
+    return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if ((int64_t)cache->slot_capacity + chunk_len > ((int64_t)1 << 30))
+    return fail(PS_INVALID_ARGUMENT, "slot_capacity + chunk_len exceeds 2^30");
+  if ((int64_t)num_seqs * chunk_len > (int64_t)1 << 26)
+    return fail(PS_INVALID_ARGUMENT, "num_seqs*chunk_len exceeds 2^26 per call");
+  int32_t bm, bn;
+  ps::prefill_tile_shape(attn->dtype, attn->head_dim, &bm, &bn);
+  if ((int64_t)num_seqs * attn->num_q_heads * ((chunk_len + bm - 1) / bm) + 8 > (int64_t)1 << 31)
+    return fail(PS_INVALID_ARGUMENT, "chunk prefill grid too large");
+  const size_t need = chunk_ws_bytes(attn, cache, num_seqs, chunk_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(PS_WORKSPACE_TOO_SMALL, "chunk prefill needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  const size_t elem = attn->dtype == PS_BF16 ? 2 : 4;
+  const size_t nkp = chunk_nkp(cache, chunk_len);
+  const size_t kv = 2 * (size_t)num_seqs * attn->num_kv_heads * nkp * attn->head_dim * elem;
+  ps::PrefillArgs a;
+  a.dtype = attn->dtype;
+  a.hq = attn->num_q_heads;
+  a.hkv = attn->num_kv_heads;
+  a.group = attn->num_q_heads / attn->num_kv_heads;
+  a.head_dim = attn->head_dim;
+  a.window = cache->window;
+  a.prefix_len = 0;   // per sequence
+  a.kv_start = 0;     // per sequence
+  a.batch = num_seqs;
+  a.num_q = chunk_len;
+  a.num_k = 0;        // per sequence
+  a.bm = bm;
+  a.bn = bn;
+  a.q = q;
+  a.k = k_new;
+  a.v = v_new;
+  a.out = out;
+  a.lse = lse;
+  a.k_rot = workspace;
+  a.rope_cs = nullptr;
+  a.scale_log2 = attn->softmax_scale * 1.4426950408889634f;
+  a.rope = make_rope(attn);
+  a.nkp = (int32_t)nkp;
+  a.seq_prefix = prefix_len;
+  a.seq_start = start_pos;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.cg = make_geom(attn, cache);
+  a.q_rot = static_cast<char*>(workspace) + ((kv + 255) / 256) * 256;
+  hipError_t e = ps::launch_chunk_prefill(a, stream);
+  if (e != hipSuccess) return from_hip(e, "ps_chunk_prefill_attn launch");
+  // the chunk joins the ring only after every chunk query has read the ring
+  ps::AppendArgs ap;
+  ap.geom = a.cg;
+  ap.dtype = attn->dtype;
+  ap.k_cache = k_cache;
+  ap.v_cache = v_cache;
+  ap.block_table = block_table;
+  ap.prefix_len = prefix_len;
+  ap.start_pos = start_pos;
+  ap.seq_tokens = nullptr;
+  ap.tokens_per_seq = chunk_len;
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.num_seqs = num_seqs;
+  ap.slot_pos = slot_pos;
+  ap.rope = a.rope;
+  return from_hip(ps::launch_append(ap, stream), "ps_chunk_prefill_attn append launch");
 }
 
 ps_status ps_prefill_plan(const ps_attn_desc* attn, int32_t window, int32_t prefix_len, int64_t kv_start,

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
   __shared__ float cs_lds[TK][HALF][2];
   __shared__ T vt_lds[D][TK + 8];
   PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, a.bm, a.bn};
-  const int32_t nkp = nk_padded(a.num_k);
+  const int32_t nkp = a.nkp;
   const int32_t nkt = nkp / TK;
   const int tid = threadIdx.x;
   const int j = tid >> 2, qq = tid & 3;   // key row of the tile, quarter of the row
@@ -215,10 +215,167 @@ __device__ inline Item decode_item(const PrefillArgs& a, int32_t n_qt) {
   return it;
 }
 
+// Geometry of a chunk that continues a cached trace.  Sequence b holds
+// positions [0, P) in its ring and the chunk is positions [P, P + T).  Its key
+// array is the pinned positions [0, min(L, P + T)) followed by the contiguous
+// run [w0, P + T), w0 = max(L, P - W + 1): every key any chunk query can see
+// (blog "Prefix Sliding 完全拆解", section "核心机制：注意力掩码上的两个区间";
+// the window of the first chunk query starts at P - W + 1).  Keys below P come
+// from the ring, the rest from the chunk.  false: the sequence cannot be served
+// (negative values, or ring slots beyond the capacity would be read).
+__device__ inline bool chunk_geom(const PrefillArgs& a, int32_t b, int32_t bm, int32_t bn, PrefillGeom& g) {
+  const int32_t L = a.seq_prefix[b];
+  const int64_t P = a.seq_start[b];
+  if (L < 0 || P < 0) return false;
+  const int64_t lw = (int64_t)L + a.window;
+  if ((P < lw ? P : lw) > a.cg.slot_capacity) return false;
+  const int64_t w0 = P - a.window + 1 > L ? P - a.window + 1 : (int64_t)L;
+  g.T = a.num_q;
+  g.Nk = (int32_t)(L + P + a.num_q - w0);  // <= slot_capacity + T <= nkp
+  g.L = L;
+  g.W = a.window;
+  g.kv_start = w0;
+  g.bm = bm;
+  g.bn = bn;
+  return true;
+}
+
+// Chunk prep: the same K / V^T copies as the prep kernel, gathered per key
+// from the ring (keys below P: already rotated, copied as stored) or from the
+// chunk (rotated here at the key's position), plus the chunk queries rotated at
+// P + t and multiplied by scale * log2(e).  A ring page outside the pool gives
+// NaN keys (so the rows that see them become NaN).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a) {
+  constexpr int TK = 64;
+  constexpr int HALF = D / 2;
+  constexpr int PQ = HALF / 4;   // rotation pairs per thread
+  constexpr int DQ = D / 4;      // V dims per thread
+  __shared__ float cs_lds[TK][HALF][2];
+  __shared__ T vt_lds[D][TK + 8];
+  const int32_t nkp = a.nkp;
+  const int32_t nkt = nkp / TK;
+  const int tid = threadIdx.x;
+  const int j = tid >> 2, qq = tid & 3;   // key row of the tile, quarter of the row
+  const T* kn = static_cast<const T*>(a.k);
+  const T* vn = static_cast<const T*>(a.v);
+  const T* kc = static_cast<const T*>(a.k_cache);
+  const T* vc = static_cast<const T*>(a.v_cache);
+  T* kr = static_cast<T*>(a.k_rot);
+  T* vt = kr + (int64_t)a.batch * a.hkv * nkp * D;
+
+  for (int64_t blk = blockIdx.x; blk < (int64_t)a.batch * nkt; blk += gridDim.x) {
+    const int32_t kt = (int32_t)(blk % nkt);
+    const int32_t b = (int32_t)(blk / nkt);
+    PrefillGeom geo;
+    const bool ok = chunk_geom(a, b, 64, 64, geo);
+    const int64_t P = ok ? a.seq_start[b] : 0;
+    __syncthreads();   // the previous tile's V^T reads of vt_lds / cs_lds are done
+    for (int idx = tid; idx < TK * HALF; idx += 256) {
+      const int jj = idx / HALF, i = idx % HALF;
+      const int32_t key = kt * TK + jj;
+      float c = 1.f, sn = 0.f;
+      if (ok && a.rope.enabled && key < geo.Nk) {
+        const int64_t pos = pf_key_pos(geo, key);
+        if (pos >= P) rope_cos_sin(pos, a.rope.inv_freq[i], c, sn);
+      }
+      cs_lds[jj][i][0] = c;
+      cs_lds[jj][i][1] = sn;
+    }
+    __syncthreads();
+    const int32_t key = kt * TK + j;
+    const bool live = ok && key < geo.Nk;
+    const int64_t pos = live ? pf_key_pos(geo, key) : 0;
+    for (int32_t h = 0; h < a.hkv; ++h) {
+      const int64_t bh = (int64_t)b * a.hkv + h;
+      float x1[PQ], x2[PQ], vv[DQ];
+      if (live && pos < P) {   // from the ring: stored rotated
+        const int32_t slot = ring_slot(pos, geo.L, a.window);
+        const int64_t base = region_offset(a.cg, a.block_table, b, h, slot);
+        if (base >= 0) {
+          load_vec(kc + base + k_in_region(slot, PQ * qq, D), x1, PQ);
+          load_vec(kc + base + k_in_region(slot, HALF + PQ * qq, D), x2, PQ);
+#pragma unroll
+          for (int e = 0; e < DQ; ++e) vv[e] = Elem<T>::load(vc + base + v_in_region(slot, DQ * qq + e, D));
+        } else {
+#pragma unroll
+          for (int e = 0; e < PQ; ++e) x1[e] = x2[e] = __builtin_nanf("");
+#pragma unroll
+          for (int e = 0; e < DQ; ++e) vv[e] = __builtin_nanf("");
+        }
+      } else if (live) {       // from the chunk: rotate at the key's position
+        const int64_t src = (((int64_t)b * a.num_q + (pos - P)) * a.hkv + h) * D;
+        load_vec(kn + src + PQ * qq, x1, PQ);
+        load_vec(kn + src + HALF + PQ * qq, x2, PQ);
+        load_vec(vn + src + DQ * qq, vv, DQ);
+#pragma unroll
+        for (int e = 0; e < PQ; ++e) {
+          const float c = cs_lds[j][PQ * qq + e][0], sn = cs_lds[j][PQ * qq + e][1];
+          const float y1 = x1[e] * c - x2[e] * sn, y2 = x2[e] * c + x1[e] * sn;
+          x1[e] = y1;
+          x2[e] = y2;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < PQ; ++e) x1[e] = x2[e] = 0.f;
+#pragma unroll
+        for (int e = 0; e < DQ; ++e) vv[e] = 0.f;
+      }
+      T* krow = kr + (bh * nkp + key) * D;
+      store_vec(krow + PQ * qq, x1, PQ);
+      store_vec(krow + HALF + PQ * qq, x2, PQ);
+      const int js = vt_slot(j);
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        T tv;
+        if (sizeof(T) == 2)
+          tv = (T)f32_to_bf16_bits(vv[e]);   // exact: vv holds bf16 values
+        else
+          tv = (T)vv[e];
+        vt_lds[DQ * qq + e][js] = tv;
+      }
+      __syncthreads();
+      constexpr int EP = 16 / sizeof(T);
+      for (int idx = tid; idx < D * (TK / EP); idx += 256) {
+        const int d = idx / (TK / EP), c = idx % (TK / EP);
+        u32x4 w;
+        if (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)(uint16_t)vt_lds[d][c * EP + 2 * e] | ((uint32_t)(uint16_t)vt_lds[d][c * EP + 2 * e + 1] << 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = __float_as_uint((float)vt_lds[d][c * EP + e]);
+        }
+        *reinterpret_cast<u32x4*>(vt + (bh * D + d) * nkp + kt * TK + c * EP) = w;
+      }
+      __syncthreads();
+    }
+  }
+  // chunk queries: rotated at P + t, scaled; one thread per (sequence, query, pair)
+  const int64_t pairs = (int64_t)a.batch * a.num_q * HALF;
+  const T* q = static_cast<const T*>(a.q);
+  T* qr = static_cast<T*>(a.q_rot);
+  for (int64_t idx = blockIdx.x * 256ll + tid; idx < pairs; idx += (int64_t)gridDim.x * 256) {
+    const int32_t i = (int32_t)(idx % HALF);
+    const int64_t bt = idx / HALF;          // b * T + t
+    const int32_t b = (int32_t)(bt / a.num_q);
+    const int64_t P = a.seq_start[b];
+    float c = 1.f, sn = 0.f;
+    if (a.rope.enabled && P >= 0) rope_cos_sin(P + bt % a.num_q, a.rope.inv_freq[i], c, sn);
+    for (int32_t h = 0; h < a.hq; ++h) {
+      const int64_t row = (bt * a.hq + h) * D;
+      const float x1 = Elem<T>::load(q + row + i), x2 = Elem<T>::load(q + row + i + HALF);
+      Elem<T>::store(qr + row + i, (x1 * c - x2 * sn) * a.scale_log2);
+      Elem<T>::store(qr + row + i + HALF, (x2 * c + x1 * sn) * a.scale_log2);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 2a. fp32 debug kernel: one thread per query row, LDS-tiled, same schedule
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool kPerSeq>
 __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   constexpr int BM = PfTraits<float>::BM, BN = PfTraits<float>::BN;
   __shared__ float qs[BM][D + 1];
@@ -231,14 +388,24 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int32_t t = it.qt * BM + tid;
   const bool row_ok = t < a.num_q;
-  const int32_t u = a.num_k - a.num_q + t;  // the query's key index
+  if (kPerSeq && !chunk_geom(a, it.b, BM, BN, geo)) {   // sequence cannot be served: NaN rows
+    if (!row_ok) return;
+    float* o = static_cast<float*>(a.out) + (((int64_t)it.b * a.num_q + t) * a.hq + it.hq) * D;
+    for (int d = 0; d < D; ++d) o[d] = __builtin_nanf("");
+    if (a.lse) a.lse[((int64_t)it.b * a.hq + it.hq) * a.num_q + t] = __builtin_nanf("");
+    return;
+  }
+  const int32_t u = geo.Nk - a.num_q + t;  // the query's key index
   const int32_t kvh = it.hq / a.group;
-  const int32_t nkp = nk_padded(a.num_k);
+  const int32_t nkp = a.nkp;
   const float* q = static_cast<const float*>(a.q);
   const float* kr = static_cast<const float*>(a.k_rot) + ((int64_t)it.b * a.hkv + kvh) * nkp * D;
   const float* vt = static_cast<const float*>(a.k_rot) + (int64_t)a.batch * a.hkv * nkp * D +
                     ((int64_t)it.b * a.hkv + kvh) * D * nkp;
-  if (row_ok) {
+  if (row_ok && kPerSeq) {   // rotated and scaled by the chunk prep
+    const float* qrow = static_cast<const float*>(a.q_rot) + (((int64_t)it.b * a.num_q + t) * a.hq + it.hq) * D;
+    for (int d = 0; d < D; ++d) qs[tid][d] = qrow[d];
+  } else if (row_ok) {
     const float* qrow = q + (((int64_t)it.b * a.num_q + t) * a.hq + it.hq) * D;
     for (int i = 0; i < D / 2; ++i) {
       const float c = a.rope_cs[((int64_t)t * (D / 2) + i) * 2], s = a.rope_cs[((int64_t)t * (D / 2) + i) * 2 + 1];
@@ -271,7 +438,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
       float s = 0.f;
       for (int d = 0; d < D; ++d) s += qs[tid][d] * ks[j][d];
       const int32_t key = kt * BN + j;
-      const bool vis = key < a.num_k && (kind == 1 || pf_visible(geo, u, key));
+      const bool vis = key < geo.Nk && (kind == 1 || pf_visible(geo, u, key));
       sc[j] = vis ? s : -INFINITY;
       mx = fmaxf(mx, sc[j]);
     }
@@ -306,7 +473,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 // Softmax bookkeeping per query column: `ref` is the reference max (log2
 // units); the S accumulator starts at -ref, so the MFMA itself yields s - ref
 // and the fast path is just max / exp2 / sum / convert.
-template <int D>
+template <int D, bool kPerSeq>
 __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int BM = 128, BN = 64;
   constexpr int KS = D / 16;        // QK k-steps
@@ -325,8 +492,17 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
+  if (kPerSeq && !chunk_geom(a, it.b, BM, BN, geo)) {   // sequence cannot be served: NaN rows
+    const int32_t tn = it.qt * BM + wave * 32 + col;
+    if (tn >= a.num_q) return;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + (((int64_t)it.b * a.num_q + tn) * a.hq + it.hq) * D;
+    for (int d = hf * (D / 2); d < (hf + 1) * (D / 2); ++d) orow[d] = 0x7fc0;
+    if (a.lse && hf == 0) a.lse[((int64_t)it.b * a.hq + it.hq) * a.num_q + tn] = __builtin_nanf("");
+    return;
+  }
+  const int32_t num_k = geo.Nk, prefix_len = geo.L;
   const int32_t kvh = it.hq / a.group;
-  const int32_t nkp = nk_padded(a.num_k);
+  const int32_t nkp = a.nkp;
   const uint16_t* kr = static_cast<const uint16_t*>(a.k_rot) + ((int64_t)it.b * a.hkv + kvh) * nkp * D;
   const uint16_t* vt = static_cast<const uint16_t*>(a.k_rot) + (int64_t)a.batch * a.hkv * nkp * D +
                        ((int64_t)it.b * a.hkv + kvh) * D * nkp;
@@ -373,9 +549,17 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
   // ---- query operand (B of S^T = K Q^T): query row t, dims 16*ks + 8*hf + e ----
   const int32_t t = it.qt * BM + wave * 32 + col;
   const bool row_ok = t < a.num_q;
-  const int32_t u = a.num_k - a.num_q + t;  // key index of this lane's query
+  const int32_t u = num_k - a.num_q + t;  // key index of this lane's query
   bf16x8 qop[KS];
-  {
+  if (kPerSeq) {   // rotated and scaled by the chunk prep
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q_rot) +
+                           (((int64_t)it.b * a.num_q + (row_ok ? t : 0)) * a.hq + it.hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qop[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hf);
+      if (!row_ok) qop[ks] = bf16x8{};
+    }
+  } else {
     float qv[KS][8];
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            (((int64_t)it.b * a.num_q + (row_ok ? t : 0)) * a.hq + it.hq) * D;
@@ -407,9 +591,9 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
       for (int e = 0; e < 8; ++e) qop[ks][e] = (bf16)(row_ok ? qv[ks][e] * a.scale_log2 : 0.f);
   }
   // per-lane visible key ranges: pinned keys [0, pre_end), chunk keys band_lo + [0, band_w]
-  const int32_t pre_end = row_ok ? pf_min(a.prefix_len, u + 1) : 0;
-  int32_t band_lo = pf_max(a.prefix_len, u - a.window + 1);
-  const int32_t band_hi = pf_min(u, a.num_k - 1);
+  const int32_t pre_end = row_ok ? pf_min(prefix_len, u + 1) : 0;
+  int32_t band_lo = pf_max(prefix_len, u - a.window + 1);
+  const int32_t band_hi = pf_min(u, num_k - 1);
   uint32_t band_w = (uint32_t)(band_hi - band_lo);
   if (!row_ok || band_hi < band_lo) {  // empty band: no key satisfies the unsigned range test
     band_lo = 0x7fffffff;
@@ -462,7 +646,7 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
     // key of register i of tile m2: kt*BN + 32*m2 + 8*(i/4) + 4*hf + i%4
     if (cur_kind == 2) {
       const int32_t kbase = kt * BN + 4 * hf;
-      if (kt * BN >= a.prefix_len && kt * BN + BN <= a.num_k) {
+      if (kt * BN >= prefix_len && kt * BN + BN <= num_k) {
         // chunk keys only, all in range: visible iff 0 <= u - key < W, one unsigned compare
         const uint32_t rel = (uint32_t)(row_ok ? u - kbase : -1 - a.window);
 #pragma unroll
@@ -619,23 +803,37 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillGeom 
   }
 }
 
-template <typename T, int D>
-hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-  {
-    int64_t blocks = (int64_t)a.batch * (nk_padded(a.num_k) / 64);
-    blocks = blocks < 1 ? 1 : (blocks > 16384 ? 16384 : blocks);
-    hipLaunchKernelGGL((prefill_prep_kernel<T, D>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+template <typename T, int D, bool kPerSeq>
+hipError_t launch_attention_t(const PrefillArgs& a, hipStream_t stream) {
   const int32_t n_qt = (a.num_q + a.bm - 1) / a.bm;
   const int64_t total = (int64_t)a.batch * a.hq * n_qt;
   const dim3 grid((uint32_t)(((total + 7) / 8) * 8));
   if (sizeof(T) == 2)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, kPerSeq>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_f32_kernel<D>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((prefill_f32_kernel<D, kPerSeq>), grid, dim3(64), 0, stream, a);
   return hipGetLastError();
+}
+
+int64_t prep_blocks(const PrefillArgs& a) {
+  int64_t blocks = (int64_t)a.batch * (a.nkp / 64);
+  return blocks < 1 ? 1 : (blocks > 16384 ? 16384 : blocks);
+}
+
+template <typename T, int D>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_prep_kernel<T, D>), dim3((uint32_t)prep_blocks(a)), dim3(256), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attention_t<T, D, false>(a, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_chunk_t(const PrefillArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((chunk_prep_kernel<T, D>), dim3((uint32_t)prep_blocks(a)), dim3(256), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attention_t<T, D, true>(a, stream);
 }
 
 }  // namespace
@@ -656,6 +854,13 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.dtype == PS_BF16)
     return a.head_dim == 64 ? launch_prefill_t<uint16_t, 64>(a, stream) : launch_prefill_t<uint16_t, 128>(a, stream);
   return a.head_dim == 64 ? launch_prefill_t<float, 64>(a, stream) : launch_prefill_t<float, 128>(a, stream);
+}
+
+hipError_t launch_chunk_prefill(const PrefillArgs& a, hipStream_t stream) {
+  if (a.batch == 0 || a.num_q == 0) return hipSuccess;
+  if (a.dtype == PS_BF16)
+    return a.head_dim == 64 ? launch_chunk_t<uint16_t, 64>(a, stream) : launch_chunk_t<uint16_t, 128>(a, stream);
+  return a.head_dim == 64 ? launch_chunk_t<float, 64>(a, stream) : launch_chunk_t<float, 128>(a, stream);
 }
 
 hipError_t launch_prefill_plan(int32_t num_q, int32_t num_k, int32_t prefix_len, int32_t window,

@@ -62,11 +62,21 @@ struct PrefillArgs {
   float* rope_cs;         // workspace: [num_q][D/2][2] cos/sin of query positions
   float scale_log2;
   RopeFreq rope;
+  int32_t nkp;            // key stride of the K / V^T copies (multiple of 64)
+  // chunk mode: per-sequence geometry, keys below start_pos read from the ring
+  const int32_t* seq_prefix;   // [batch] L of each sequence
+  const int64_t* seq_start;    // [batch] first chunk position P of each sequence
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  CacheGeom cg;
+  void* q_rot;            // workspace: rotated, scaled queries [batch][num_q][hq][D]
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_chunk_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_plan(int32_t num_q, int32_t num_k, int32_t prefix_len, int32_t window,
                                int64_t kv_start, int32_t bm, int32_t bn, int32_t* tiles,
                                int32_t max_tiles, int32_t* num_tiles, hipStream_t stream);

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 1
+#define PS_ABI_VERSION 2
 
 typedef enum {
   PS_OK = 0,
@@ -192,6 +192,43 @@ ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t pref
 
 size_t ps_prefill_workspace_size(const ps_attn_desc* attn, int32_t batch, int32_t num_queries,
                                  int32_t num_keys);
+
+/* ps_chunk_prefill_attn -- a chunk of new tokens continues cached traces:
+ * attention of the chunk's queries over each sequence's ring plus the chunk
+ * itself, after which the chunk joins the ring.  Blog "Prefix Sliding
+ * 完全拆解": section "核心机制：注意力掩码上的两个区间" (A(i) for every
+ * query; the ring keeps only prefix and window), the paged fixed-cap memory
+ * remark that closes that section, and the multi-turn / tool-output case of
+ * its limitations section (long external content poured into a live trace).
+ *   prefix_len, start_pos : [num_seqs] device int32 / int64.  Sequence s
+ *          holds positions [0, P) in its ring (P = start_pos[s], appended
+ *          earlier through ps_kv_append / this call); the chunk is positions
+ *          [P, P + chunk_len).
+ *   q, k_new, v_new : [num_seqs][chunk_len][H][D] raw chunk queries / keys /
+ *          values (H = Hq for q, Hkv for k_new and v_new), dtype of attn.
+ *   out  : [num_seqs][chunk_len][Hq][D]; query t (position P + t) sees every
+ *          visible key: ring keys below P and chunk keys up to itself.
+ *   lse  : NULL or [num_seqs][Hq][chunk_len] float (as ps_prefill_attn).
+ *   slot_pos : NULL or the ps_kv_append sidecar, updated by the append.
+ *   workspace : >= ps_chunk_prefill_workspace_size(...) bytes.
+ * Order: every chunk query reads the ring before any chunk token is written
+ * into it (a chunk token may reuse the slot of a window key an earlier chunk
+ * query still needs); both steps are enqueued on `stream`.
+ * Device values that cannot be served -- negative L or P, or
+ * min(P, L + W) > slot_capacity -- give NaN rows for that sequence (its
+ * appends follow the ps_kv_append rules); a ring page outside the pool gives
+ * NaN rows for the queries that see it. */
+ps_status ps_chunk_prefill_attn(const ps_attn_desc* attn, const ps_cache_desc* cache,
+                                void* k_cache, void* v_cache, const int32_t* block_table,
+                                const int32_t* prefix_len, const int64_t* start_pos,
+                                int32_t chunk_len, const void* q, const void* k_new,
+                                const void* v_new, int32_t num_seqs, void* out, float* lse,
+                                int32_t* slot_pos, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* Workspace bytes ps_chunk_prefill_attn needs (0 on invalid arguments). */
+size_t ps_chunk_prefill_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* cache,
+                                       int32_t num_seqs, int32_t chunk_len);
 
 /* Tile shape (BM queries x BN keys) ps_prefill_attn uses for this geometry. */
 ps_status ps_prefill_tile_shape(const ps_attn_desc* attn, int32_t* block_m, int32_t* block_n);

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ps_abi_version() == 1
+    assert lib.ps_abi_version() == 2
     assert lib.ps_status_string(0) == b"ok"
     assert lib.ps_status_string(3) == b"workspace too small"
 
@@ -184,3 +184,32 @@ def test_scheduler_matches_oracle_random(sched):
 def test_scheduler_matches_oracle_truncated_backprop_shape(sched):
     got = _host_plan(sched, 8192, 8292, 100, 2048, 98304, 128, 64)
     assert got == oracle.tile_plan(8192, 8292, 100, 2048, 98304, 128, 64)
+
+
+def test_chunk_prefill_validation_and_workspace(lib):
+    a, c = _descs()
+    S, T = 3, 100
+    nkp = (4224 + T + 63) // 64 * 64
+    align = lambda x: (x + 255) // 256 * 256
+    need = lib.ps_chunk_prefill_workspace_size(ctypes.byref(a), ctypes.byref(c), S, T)
+    assert need == align(2 * S * 2 * nkp * 128 * 2) + align(S * T * 16 * 128 * 2)
+    a32, _ = _descs(dtype=1)
+    assert lib.ps_chunk_prefill_workspace_size(ctypes.byref(a32), ctypes.byref(c), S, T) == \
+        align(2 * S * 2 * nkp * 128 * 4) + align(S * T * 16 * 128 * 4)
+
+    def call(attn=a, cache=c, kc=FAKE, q=FAKE, chunk=T, seqs=S, ws=FAKE, wsb=need, bt=None):
+        return lib.ps_chunk_prefill_attn(ctypes.byref(attn), ctypes.byref(cache), kc, FAKE, bt, FAKE, FAKE, chunk,
+                                         q, FAKE, FAKE, seqs, FAKE, None, None, ws, wsb, None)
+
+    assert call(wsb=need - 1) == 3
+    assert call(ws=None) == 3
+    assert call(kc=None) == 1
+    assert call(q=None) == 1
+    assert call(chunk=-1) == 1
+    assert call(seqs=-2) == 1
+    assert call(seqs=0) == 0 and call(chunk=0) == 0          # nothing to do, nothing launched
+    bad_a, _ = _descs(hq=15)
+    assert call(attn=bad_a) == 1
+    _, paged = _descs(page=64, mp=66, npages=100)
+    assert call(cache=paged) == 1                              # paged cache without a block table
+    assert lib.ps_last_error()
