@@ -13,8 +13,9 @@ attention kernel (algorithmic HBM bytes per launch / average launch time,
 against 8 TB/s), the float64 CPU oracle timed on a bounded sample of the
 same workload, the masked prefill kernel (truncated-backprop chunk: 8 x 8192
 queries behind a 100-token prefix, W=2048, Hq=28, Hkv=4) in TFLOP/s against
-the 2.5 PFLOP/s bf16 MFMA peak, and the full-attention decode comparator at
-the same position.
+the 2.5 PFLOP/s bf16 MFMA peak, the chunk prefill that reads the ring (64
+rings at 32768, a 2048-token chunk each), and the full-attention decode
+comparator at the same position.
 """
 from __future__ import annotations
 
@@ -50,7 +51,8 @@ def parse():
     ap.add_argument("--no-full", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the decode position sweep (flatness)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other decode workloads")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+    ap.add_argument("--no-chunk", action="store_true", help="skip the chunk prefill that reads the ring")
+    ap.add_argument("--only", choices=["decode", "prefill", "chunk"], default=None,
                     help="run only one leg (for profiling); the JSON line then carries that leg only")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run one device-to-device copy of BYTES first (reference for HBM counter scaling)")
@@ -379,6 +381,43 @@ def run_prefill(ps, torch, reps=10, full_causal=True):
     return out
 
 
+def run_chunk(ps, torch, reps=5):
+    """Chunk continuing live traces (C6): 64 rings at 32768 (L=100, W=4096), a 2048-token chunk each.
+    One call = chunk prep (ring gather + rotations), attention, append of the chunk into the rings."""
+    import synth
+    cfg = synth.C6_CHUNK
+    attn = ps.AttnSpec(cfg.hq, cfg.hkv, cfg.dim, ps.PS_BF16, cfg.rope_theta, 1 / math.sqrt(cfg.dim))
+    cap = (cfg.prefix + cfg.window + 63) // 64 * 64
+    cache = ps.CacheSpec(window=cfg.window, slot_capacity=cap)
+    n, T = cfg.num_seqs, cfg.chunk
+    g = torch.Generator(device="cuda").manual_seed(13)
+    ks, vs = ps.cache_shapes(attn, cache, n)
+    kc = (torch.randn(ks, generator=g, device="cuda") * cfg.kv_std).bfloat16()
+    vc = (torch.randn(vs, generator=g, device="cuda") * cfg.kv_std).bfloat16()
+    q = torch.randn((n, T, cfg.hq, cfg.dim), generator=g, device="cuda").bfloat16()
+    kn = (torch.randn((n, T, cfg.hkv, cfg.dim), generator=g, device="cuda") * cfg.kv_std).bfloat16()
+    vn = (torch.randn((n, T, cfg.hkv, cfg.dim), generator=g, device="cuda") * cfg.kv_std).bfloat16()
+    out = torch.empty_like(q)
+    pl = torch.full((n,), cfg.prefix, dtype=torch.int32, device="cuda")
+    sp = torch.full((n,), cfg.position, dtype=torch.int64, device="cuda")
+    ws = torch.empty(ps.ps_chunk_prefill_workspace_size(attn, cache, n, T), dtype=torch.uint8, device="cuda")
+
+    def call(k_):
+        for _ in range(k_):
+            ps.ps_chunk_prefill_attn(attn, cache, kc, vc, pl, sp, q, kn, vn, out, workspace=ws)
+    call(1)
+    t = timed(torch, call, reps) / reps
+    # every chunk query sits beyond L + W: it sees exactly L + W keys
+    pairs = sum(min(cfg.position + t_ + 1, cfg.prefix + cfg.window) for t_ in range(T))
+    flops = 4.0 * cfg.dim * pairs * n * cfg.hq
+    res = {"workload": cfg.name, "num_seqs": n, "chunk": T, "position": cfg.position, "prefix": cfg.prefix,
+           "window": cfg.window, "ms": t * 1e3, "tflops": flops / t / 1e12, "useful_tflop": flops / 1e12,
+           "mfma_frac": flops / t / 1e12 / BF16_PEAK_TFLOPS, "tok_s": n * T / t}
+    del kc, vc, q, kn, vn, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------------- CPU oracle
 def _oracle_worker(args):
     idx, position, prefix, window, reps = args
@@ -459,6 +498,9 @@ def main():
     if args.only == "prefill":
         print(json.dumps({"prefill": run_prefill(ps, torch, full_causal=not args.no_full)}))
         return
+    if args.only == "chunk":
+        print(json.dumps({"chunk_prefill": run_chunk(ps, torch)}))
+        return
     dec = run_decode(ps, torch, args)
     print(f"[bench] decode done: {dec['tok_s']:.0f} tok/s, kernel {dec['kernel_s'] * 1e6:.1f} us",
           file=sys.stderr, flush=True)
@@ -466,6 +508,10 @@ def main():
     if not args.no_prefill and args.only is None:
         prefill = run_prefill(ps, torch)
         print(f"[bench] prefill done: {prefill}", file=sys.stderr, flush=True)
+    chunk = None
+    if not args.no_chunk and args.only is None:
+        chunk = run_chunk(ps, torch)
+        print(f"[bench] chunk prefill done: {chunk['tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
     sweep = None
     if not args.no_sweep and args.only is None:
         sweep = run_sweep(ps, torch, num_seqs=args.num_seqs, layers=args.layers)
@@ -502,6 +548,7 @@ def main():
                      "bytes_per_launch": dec["kernel_bytes"]},
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "chunk_prefill": chunk,
         "full_attention": full,
     }
     if extra:

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_common import BF16_TOL, fill_rings_sampled, normwise_err, require_gpu, to_dev
+from tests.gpu_common import BF16_TOL, fill_rings_sampled, new_cache, normwise_err, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -142,3 +142,42 @@ def test_prefill_full_causal_comparator(ps):
     rows = [0, 4095, 8191]
     err = _prefill_rows(ps, c, rows, batches=[5], heads=[0, 13, 27])
     assert err <= BF16_TOL, err
+
+
+def test_chunk_prefill_tool_output_64_sequences(ps):
+    # 64 rings at 32768 (L=100, W=4096) receive a 2048-token chunk each; sampled
+    # rows of sampled sequences against the oracle over the full 34816-token history
+    cfg = synth.C6_CHUNK
+    attn = ps.AttnSpec(cfg.hq, cfg.hkv, cfg.dim, ps.PS_BF16, cfg.rope_theta, 1 / math.sqrt(cfg.dim))
+    cap = (cfg.prefix + cfg.window + 63) // 64 * 64
+    cache = ps.CacheSpec(window=cfg.window, slot_capacity=cap)
+    n, T, P = cfg.num_seqs, cfg.chunk, cfg.position
+    print(f"chunk full size: {n} seqs, T={T}, P={P}", flush=True)
+    kc, vc = new_cache(ps, attn, cache, n)
+    sampled = {}
+    for s in (0, 37, 63):
+        kh = synth.history(0, cfg.cfg_id, synth.T_K, s, 0, 0, P + T, cfg.hkv, cfg.dim, cfg.kv_std, "bf16")
+        vh = synth.history(0, cfg.cfg_id, synth.T_V, s, 0, 0, P + T, cfg.hkv, cfg.dim, cfg.kv_std, "bf16")
+        sampled[s] = (kh, vh)
+    fill_rings_sampled(ps, attn, cache, kc, vc, [cfg.prefix] * n, [P - 1] * n, sampled, seed=3)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    q = torch.randn((n, T, cfg.hq, cfg.dim), generator=gen, device="cuda").bfloat16()
+    kn = (torch.randn((n, T, cfg.hkv, cfg.dim), generator=gen, device="cuda") * cfg.kv_std).bfloat16()
+    vn = (torch.randn((n, T, cfg.hkv, cfg.dim), generator=gen, device="cuda") * cfg.kv_std).bfloat16()
+    qh = {}
+    for s, (kh, vh) in sampled.items():
+        qh[s] = synth.history(0, cfg.cfg_id, synth.T_Q, s, 0, P, P + T, cfg.hq, cfg.dim, cfg.q_std, "bf16")
+        q[s] = to_dev(qh[s], torch.bfloat16)
+        kn[s] = to_dev(kh[P:P + T], torch.bfloat16)
+        vn[s] = to_dev(vh[P:P + T], torch.bfloat16)
+    out = torch.empty_like(q)
+    pl = torch.full((n,), cfg.prefix, dtype=torch.int32, device="cuda")
+    sp = torch.full((n,), P, dtype=torch.int64, device="cuda")
+    ps.ps_chunk_prefill_attn(attn, cache, kc, vc, pl, sp, q, kn, vn, out)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 1000, 2046, 2047])
+    for s, (kh, vh) in sampled.items():
+        want, _ = oracle.chunk_prefill_attention(qh[s], kh, vh, P, cfg.prefix, cfg.window,
+                                                 1 / math.sqrt(cfg.dim), cfg.rope_theta, rows=rows)
+        got = out[s].float().cpu().numpy()[rows]
+        assert normwise_err(got, want) <= BF16_TOL, s
