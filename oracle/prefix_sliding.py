@@ -40,6 +40,9 @@ the pages; no page is quoted):
 * Chunk continuing a trace (``chunk_prefill_attention``): queries at
   start..start+T-1 over the whole history; the ring supplies what the earlier
   trace left visible, so the result is again plain masked attention.
+* Backward of the masked prefill (``prefill_attention_backward``): the chain
+  rule of masked softmax attention, written out; gradients are taken with
+  respect to the raw (un-rotated) inputs.
 * Tile plan (blog section "Kernel 实现：两层级过滤"): tiles with no visible pair
   are skipped, tiles whose every pair is visible need no element mask, the
   rest are partial.  The oracle decides this by enumerating every element.
@@ -252,6 +255,48 @@ def chunk_prefill_attention(q: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarra
         out[:, h, :] = w @ v[:, kv, :]
         lse[:, h] = l
     return out, lse
+
+
+def prefill_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, d_out: np.ndarray,
+                               prefix_len: int, window: int, kv_start: int, scale: float, theta: float):
+    """Gradients of the masked prefill attention with respect to its raw
+    inputs, for an upstream gradient ``d_out`` [T, Hq, D] (the truncated-backprop
+    trainer of the blog's section "超长 rollouts 的反向传播：截断回传" back-propagates
+    through the same masked attention; its loss mask only decides which rows
+    of d_out are non-zero).
+
+    Chain rule written out, per query head h with KV head g:
+      S = scale * Q' K'^T (masked), P = softmax(S), O = P V
+      dV_g += P^T dO;  dP = dO V^T;  dS = P * (dP - rowsum(P * dP))
+      dQ' = scale * dS K';  dK'_g += scale * dS^T Q'
+    and since Q' = R(pos) Q with R orthogonal, dQ = R(pos)^T dQ' (the rotation
+    by -pos), likewise dK.  Returns (dq [T, Hq, D], dk [Nk, Hkv, D],
+    dv [Nk, Hkv, D]) in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    t_q, hq, d = q.shape
+    nk, hkv, _ = k.shape
+    g = hq // hkv
+    posk = key_positions(nk, prefix_len, kv_start)
+    posq = posk[nk - t_q:]
+    qr = rope(q, posq[:, None], theta)
+    kr = rope(np.asarray(k, dtype=np.float64), posk[:, None], theta)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(d_out, dtype=np.float64)
+    mask = visible(posq[:, None], posk[None, :], prefix_len, window)
+    dqr = np.zeros_like(qr)
+    dkr = np.zeros_like(kr)
+    dv = np.zeros_like(v)
+    for h in range(hq):
+        kv = h // g
+        p, _ = _masked_softmax_rows(scale * (qr[:, h, :] @ kr[:, kv, :].T), mask)
+        dv[:, kv, :] += p.T @ do[:, h, :]
+        dp = do[:, h, :] @ v[:, kv, :].T
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        dqr[:, h, :] = scale * (ds @ kr[:, kv, :])
+        dkr[:, kv, :] += scale * (ds.T @ qr[:, h, :])
+    dq = rope(dqr, -posq[:, None], theta)
+    dk = rope(dkr, -posk[:, None], theta)
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------

@@ -23,6 +23,9 @@ PIN_CHECKS = [
     lambda: pins.test_chunk_reduces_to_reference_attention(3, 6, 25, 12),
     lambda: pins.test_chunk_rows_match_decode_with_rotation(),
     lambda: pins.test_chunk_zero_query_gives_mean_of_visible_values(3, 5, 40),
+    lambda: pins.test_backward_matches_central_differences(3, 4, 3, 10000.0),
+    lambda: pins.test_backward_matches_torch_autograd(4, 5),
+    lambda: pins.test_backward_invariants_and_loss_mask_structure(),
 ]
 
 
@@ -90,6 +93,31 @@ def _chunk_query_one_early(q, k_hist, v_hist, start, L, W, scale, theta):
     s = max(start - 1, 0)
     return ORIG_CHUNK(q, k_hist[:s + q.shape[0]], v_hist[:s + q.shape[0]], s, L, W, scale, theta)
 
+def _backward_with(bug):
+    def f(q, k, v, d_out, L, W, kv_start, scale, theta):
+        q = np.asarray(q, dtype=np.float64)
+        t_q, hq, d = q.shape
+        nk, hkv, _ = k.shape
+        g = hq // hkv
+        posk = ops.key_positions(nk, L, kv_start)
+        posq = posk[nk - t_q:]
+        qr, kr = ops.rope(q, posq[:, None], theta), ops.rope(k, posk[:, None], theta)
+        mask = ops.visible(posq[:, None], posk[None, :], L, W)
+        dqr, dkr, dv = np.zeros_like(qr), np.zeros_like(kr), np.zeros_like(np.asarray(v, dtype=np.float64))
+        for h in range(hq):
+            kv = h // g
+            p, _ = ops._masked_softmax_rows(scale * (qr[:, h] @ kr[:, kv].T), mask)
+            dv[:, kv] += p.T @ d_out[:, h]
+            dp = d_out[:, h] @ np.asarray(v, dtype=np.float64)[:, kv].T
+            ds = p * dp if bug == "no-rowsum" else p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dqr[:, h] = scale * (ds @ kr[:, kv])
+            dkr[:, kv] += scale * (ds.T @ qr[:, h])
+        if bug == "no-unrotate":
+            return dqr, dkr, dv
+        return ops.rope(dqr, -posq[:, None], theta), ops.rope(dkr, -posk[:, None], theta), dv
+    return f
+
+
 MUTANTS = {
     "window-off-by-one": ("visible", _window_off_by_one),
     "prefix-not-causal": ("visible", _prefix_not_causal),
@@ -99,6 +127,8 @@ MUTANTS = {
     "gqa-interleaved": ("decode_attention", _decode_interleaved_gqa),
     "chunk-forgets-trace": ("chunk_prefill_attention", _chunk_forgets_trace),
     "chunk-query-one-early": ("chunk_prefill_attention", _chunk_query_one_early),
+    "backward-no-rowsum": ("prefill_attention_backward", _backward_with("no-rowsum")),
+    "backward-no-unrotate": ("prefill_attention_backward", _backward_with("no-unrotate")),
 }
 
 

@@ -326,6 +326,94 @@ def test_chunk_zero_query_gives_mean_of_visible_values(L, W, start):
         assert abs(lse[t, 0] - math.log(cnt)) < 1e-12   # all scores 0: lse = log(count)
 
 
+# ---------------------------------------------------------------- backward of the masked prefill
+def _bwd_case(seed, t_q=9, nk=14, hq=4, hkv=2, d=8):
+    rs = np.random.default_rng(seed)
+    return (rs.standard_normal((t_q, hq, d)), rs.standard_normal((nk, hkv, d)), rs.standard_normal((nk, hkv, d)),
+            rs.standard_normal((t_q, hq, d)))
+
+
+@pytest.mark.parametrize("L,W,kv_start,theta", [(3, 4, 3, 10000.0), (2, 3, 7, 10000.0), (0, 1 << 20, 0, 500.0),
+                                                (5, 2, 5, 0.0)])
+def test_backward_matches_central_differences(L, W, kv_start, theta):
+    q, k, v, do = _bwd_case(1)
+    sc = 0.37
+    dq, dk, dv = oracle.prefill_attention_backward(q, k, v, do, L, W, kv_start, sc, theta)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.prefill_attention(q_, k_, v_, L, W, kv_start, sc, theta)
+        return float((o * do).sum())
+
+    eps = 1e-6
+    for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
+
+
+def _torch_rope(x, pos, theta):
+    # rotation written as complex multiplication of the pairs (x_i, x_{i+D/2})
+    d = x.shape[-1]
+    h = d // 2
+    if not theta:
+        return x
+    f = theta ** (-2.0 * torch.arange(h, dtype=torch.float64) / d)
+    rot = torch.polar(torch.ones(pos.shape[0], h, dtype=torch.float64), pos[:, None].double() * f)[:, None, :]
+    z = torch.complex(x[..., :h], x[..., h:]) * rot
+    return torch.cat([z.real, z.imag], dim=-1)
+
+
+@pytest.mark.parametrize("L,W", [(4, 5), (0, 6), (30, 3)])
+def test_backward_matches_torch_autograd(L, W):
+    q, k, v, do = _bwd_case(2, t_q=21, nk=21, hq=6, hkv=3, d=16)
+    sc, theta = 0.25, 10000.0
+    dq, dk, dv = oracle.prefill_attention_backward(q, k, v, do, L, W, L, sc, theta)
+    n = 21
+    pos = torch.arange(n)
+    tq = torch.from_numpy(q).requires_grad_()
+    tk = torch.from_numpy(k).requires_grad_()
+    tv = torch.from_numpy(v).requires_grad_()
+    qr = _torch_rope(tq, pos, theta)
+    kr = _torch_rope(tk, pos, theta)
+    mask = torch.from_numpy(_band_mask(n, min(L, n), W))
+    g = 2
+    kk = kr.permute(1, 0, 2).repeat_interleave(g, dim=0)
+    vv = tv.permute(1, 0, 2).repeat_interleave(g, dim=0)
+    s = sc * qr.permute(1, 0, 2) @ kk.transpose(1, 2)
+    o = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=-1) @ vv
+    (o.permute(1, 0, 2) * torch.from_numpy(do)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_backward_invariants_and_loss_mask_structure():
+    q, k, v, do = _bwd_case(3, t_q=30, nk=40, hq=4, hkv=2, d=8)
+    L, W, ks = 3, 5, 13
+    # without rotation: scores are unchanged by adding one vector to every key, so dk sums to 0;
+    # every probability row sums to 1, so dv sums to the upstream gradient of the group's heads
+    dq, dk, dv = oracle.prefill_attention_backward(q, k, v, do, L, W, ks, 0.5, 0.0)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(axis=0), do.reshape(30, 2, 2, 8).sum(axis=(0, 2)), atol=1e-12)
+    # loss mask on the last r rows (the trainer's last-W rule): keys no such row can see get exactly 0
+    r = 6
+    dom = do.copy()
+    dom[:-r] = 0.0
+    dq, dk, dv = oracle.prefill_attention_backward(q, k, v, dom, L, W, ks, 0.5, 10000.0)
+    posk = oracle.key_positions(40, L, ks)
+    posq = posk[-30:][-r:]
+    seen = oracle.visible(posq[:, None], posk[None, :], L, W).any(axis=0)
+    assert (~seen).sum() > 0 and seen.sum() > 0
+    assert np.all(dk[~seen] == 0.0) and np.all(dv[~seen] == 0.0)
+    assert np.all(np.abs(dv[seen]).sum(axis=(1, 2)) > 0)
+    assert np.all(dq[:-r] == 0.0)
+
+
 # ---------------------------------------------------------------- tile plan
 def test_tile_plan_hand_worked_cases():
     for case in _golden("tile_plan_small.json")["cases"]:
