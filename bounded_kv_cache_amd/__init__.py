@@ -19,7 +19,8 @@ from . import _lib
 from ._lib import PS_BF16, PS_F32, PSError
 
 __all__ = ["AttnSpec", "CacheSpec", "PSError", "ps_kv_append", "ps_decode_attn", "ps_prefill_attn",
-           "ps_chunk_prefill_attn", "ps_chunk_prefill_workspace_size",
+           "ps_chunk_prefill_attn", "ps_chunk_prefill_workspace_size", "ps_prefill_attn_backward",
+           "ps_prefill_backward_workspace_size",
            "ps_prefill_plan", "ps_decode_workspace_size", "ps_decode_num_splits", "ps_prefill_workspace_size",
            "ps_prefill_tile_shape", "ps_abi_version", "cache_shapes", "PS_BF16", "PS_F32"]
 
@@ -187,6 +188,40 @@ def ps_prefill_attn(attn: AttnSpec, window: int, prefix_len: int, kv_start: int,
                                            batch, num_q, num_k, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                            _stream(stream)))
     return out
+
+
+def ps_prefill_backward_workspace_size(attn: AttnSpec, batch: int, num_queries: int, num_keys: int) -> int:
+    a = attn.c()
+    return _lib.load().ps_prefill_backward_workspace_size(ctypes.byref(a), batch, num_queries, num_keys)
+
+
+def ps_prefill_attn_backward(attn: AttnSpec, window: int, prefix_len: int, kv_start: int, q: torch.Tensor,
+                             k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, d_out: torch.Tensor,
+                             lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, *,
+                             workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients of ps_prefill_attn: writes dq [B, T, Hq, D], dk and dv [B, Nk, Hkv, D]."""
+    dt = attn.torch_dtype
+    batch, num_q = q.shape[0], q.shape[1]
+    num_k = k.shape[1]
+    _need(q, "q", dt, batch * num_q * attn.num_q_heads * attn.head_dim)
+    _need(k, "k", dt, batch * num_k * attn.num_kv_heads * attn.head_dim)
+    _need(v, "v", dt, k.numel())
+    _need(out, "out", dt, q.numel())
+    _need(d_out, "d_out", dt, q.numel())
+    _need(lse, "lse", torch.float32, batch * attn.num_q_heads * num_q)
+    _need(dq, "dq", dt, q.numel())
+    _need(dk, "dk", dt, k.numel())
+    _need(dv, "dv", dt, k.numel())
+    need = ps_prefill_backward_workspace_size(attn, batch, num_q, num_k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    a = attn.c()
+    _lib.check(_lib.load().ps_prefill_attn_backward(ctypes.byref(a), window, prefix_len, kv_start, _ptr(q), _ptr(k),
+                                                    _ptr(v), _ptr(out), _ptr(d_out), _ptr(lse), batch, num_q, num_k,
+                                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                                                    _stream(stream)))
+    return dq, dk, dv
 
 
 def ps_chunk_prefill_workspace_size(attn: AttnSpec, cache: CacheSpec, num_seqs: int, chunk_len: int) -> int:

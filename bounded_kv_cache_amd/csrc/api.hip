@@ -164,6 +164,37 @@ size_t chunk_ws_bytes(const ps_attn_desc* a, const ps_cache_desc* c, int32_t num
   return ((kv + 255) / 256) * 256 + ((qr + 255) / 256) * 256;
 }
 
+// Backward workspace layout (each piece 256-byte aligned).
+struct BwdLayout {
+  size_t kr, krt, vr, qs, qst, dot, lse2, di, cs_q, cs_k, total;
+  int32_t nkp, tqp;
+};
+
+BwdLayout bwd_layout(const ps_attn_desc* a, int32_t batch, int32_t num_q, int32_t num_k) {
+  BwdLayout l;
+  l.nkp = (num_k + 127) / 128 * 128;
+  l.tqp = (num_q + 63) / 64 * 64;
+  const size_t elem = a->dtype == PS_BF16 ? 2 : 4;
+  const size_t d = a->head_dim;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t kv = al((size_t)batch * a->num_kv_heads * l.nkp * d * elem);
+  const size_t qv = al((size_t)batch * a->num_q_heads * l.tqp * d * elem);
+  const size_t rows = al((size_t)batch * a->num_q_heads * l.tqp * sizeof(float));
+  size_t o = 0;
+  l.kr = o; o += kv;
+  l.krt = o; o += kv;
+  l.vr = o; o += kv;
+  l.qs = o; o += qv;
+  l.qst = o; o += qv;
+  l.dot = o; o += qv;
+  l.lse2 = o; o += rows;
+  l.di = o; o += rows;
+  l.cs_q = o; o += al((size_t)num_q * d * sizeof(float));
+  l.cs_k = o; o += al((size_t)l.nkp * d * sizeof(float));
+  l.total = o;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -333,6 +364,70 @@ ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t pref
   a.cg = ps::CacheGeom{};
   a.q_rot = nullptr;
   return from_hip(ps::launch_prefill(a, stream), "ps_prefill_attn launch");
+}
+
+size_t ps_prefill_backward_workspace_size(const ps_attn_desc* attn, int32_t batch, int32_t num_queries,
+                                          int32_t num_keys) {
+  if (check_attn(attn) != PS_OK || batch < 0 || num_queries < 0 || num_keys < 0) return 0;
+  return bwd_layout(attn, batch, num_queries, num_keys).total;
+}
+
+ps_status ps_prefill_attn_backward(const ps_attn_desc* attn, int32_t window, int32_t prefix_len, int64_t kv_start,
+                                   const void* q, const void* k, const void* v, const void* out, const void* d_out,
+                                   const float* lse, int32_t batch, int32_t num_queries, int32_t num_keys, void* dq,
+                                   void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ps_status st = check_attn(attn);
+  if (st != PS_OK) return st;
+  if ((st = check_prefill_geom(window, prefix_len, kv_start, batch, num_queries, num_keys)) != PS_OK) return st;
+  if (batch == 0 || num_queries == 0) return ok();
+  if (!q || !k || !v || !out || !d_out || !lse || !dq || !dk || !dv)
+    return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if ((int64_t)batch * attn->num_q_heads * ((num_queries + 127) / 128) + 8 > (int64_t)1 << 31 ||
+      (int64_t)batch * attn->num_q_heads * num_queries > (int64_t)1 << 31 ||
+      (int64_t)batch * attn->num_kv_heads * num_keys > (int64_t)1 << 31)
+    return fail(PS_INVALID_ARGUMENT, "backward grid too large");
+  if (num_keys > ((int32_t)1 << 30)) return fail(PS_INVALID_ARGUMENT, "num_keys exceeds 2^30");
+  const BwdLayout l = bwd_layout(attn, batch, num_queries, num_keys);
+  if (!workspace || workspace_bytes < l.total)
+    return fail(PS_WORKSPACE_TOO_SMALL, "backward needs %zu workspace bytes, got %zu", l.total, workspace_bytes);
+  char* w = static_cast<char*>(workspace);
+  ps::BackwardArgs a;
+  a.dtype = attn->dtype;
+  a.hq = attn->num_q_heads;
+  a.hkv = attn->num_kv_heads;
+  a.group = attn->num_q_heads / attn->num_kv_heads;
+  a.head_dim = attn->head_dim;
+  a.window = window;
+  a.prefix_len = prefix_len;
+  a.kv_start = kv_start;
+  a.batch = batch;
+  a.num_q = num_queries;
+  a.num_k = num_keys;
+  a.nkp = l.nkp;
+  a.tqp = l.tqp;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.d_out = d_out;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.kr = w + l.kr;
+  a.krt = w + l.krt;
+  a.vr = w + l.vr;
+  a.qs = w + l.qs;
+  a.qst = w + l.qst;
+  a.dot = w + l.dot;
+  a.lse2 = reinterpret_cast<float*>(w + l.lse2);
+  a.di = reinterpret_cast<float*>(w + l.di);
+  a.cs_q = reinterpret_cast<float*>(w + l.cs_q);
+  a.cs_k = reinterpret_cast<float*>(w + l.cs_k);
+  a.scale = attn->softmax_scale;
+  a.scale_log2 = attn->softmax_scale * 1.4426950408889634f;
+  a.rope = make_rope(attn);
+  return from_hip(ps::launch_backward(a, stream), "ps_prefill_attn_backward launch");
 }
 
 size_t ps_chunk_prefill_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* cache, int32_t num_seqs,

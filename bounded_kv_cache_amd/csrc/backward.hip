@@ -1,0 +1,756 @@
+// Backward of the masked prefill attention: dq, dk, dv for the raw inputs.
+//
+// Blog "Prefix Sliding 完全拆解" (pinghaoyang.com.cn): section
+// "超长 rollouts 的反向传播：截断回传" (the trainer back-propagates through the
+// masked attention of the last 4W tokens; its loss mask only zeroes rows of the
+// upstream gradient) and section "Kernel 实现：两层级过滤" (only tiles holding a
+// visible pair are visited; element masks only on partly visible tiles).
+//
+// Per query head h with KV head g, log2 units (Q'' = scale*log2(e) * Q'):
+//   P = exp2(Q'' K'^T - lse2)   (the forward's LSE, so no running max)
+//   dV_g += P^T dO,  dP = dO V^T,  dS = P (dP - Di),  Di = rowsum(dO * O)
+//   dQ' = scale * dS K',   dK'_g += ln2 * dS^T Q''
+// and dQ, dK are dQ', dK' rotated back by -position (the rotation is orthogonal).
+//
+// Pipeline of one call:
+//   1. key prep: K' row-major and d-major (keys permuted per 16, vt_slot), V
+//      row-major, zero padded to nkp keys; cos/sin of the key positions.
+//   2. query prep: Q'' row-major and d-major (queries permuted per 16), dO
+//      d-major (permuted), lse2 (+inf on padding rows so their P is 0), Di;
+//      cos/sin of the query positions.
+//   3. dk/dv kernel: one workgroup per (batch, KV head, 128-key tile), each wave
+//      owning 32 keys whose K' and V stay in registers as MFMA B operands; it
+//      walks the query heads of the group and the 64-query blocks that see the
+//      tile.  S = Q'' K'^T and dP = dO V^T put queries on the M side, so each
+//      lane owns one key and the S / dS registers are directly the B operands of
+//      dV^T += dO^T P and dK^T += Q''^T dS (the d-major copies carry the matching
+//      query permutation).  No atomics: every dk / dv row has one writer.
+//   4. dq kernel: the forward's work decomposition and key-tile schedule:
+//      S^T = K' Q''^T, dP^T = V dO^T, dS^T, then dQ^T += K'^T dS^T.
+// All arithmetic on MFMA is bf16 x bf16 -> fp32; P and dS are rounded to bf16
+// as MFMA operands.  The fp32 kernels at the end are the debug path (plain
+// loops, one thread per query or key row).
+#include "ps_internal.h"
+#include "ps_sched.h"
+#include "ps_tiles.h"
+
+namespace ps {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2f = 0.69314718055994531f;
+
+// ---------------------------------------------------------------------------
+// 1. key prep: one workgroup per (batch, 64-key tile); thread = quarter of a key row
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_key_prep_kernel(BackwardArgs a) {
+  constexpr int TK = 64;
+  constexpr int HALF = D / 2;
+  constexpr int PQ = HALF / 4;   // rotation pairs per thread
+  constexpr int DQ = D / 4;      // value dims per thread
+  __shared__ float cs_lds[TK][HALF][2];
+  __shared__ T t_lds[D][TK + 8];
+  PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, 64, 64};
+  const int32_t nkt = a.nkp / TK;
+  const int tid = threadIdx.x;
+  const int j = tid >> 2, qq = tid & 3;
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  T* kr = static_cast<T*>(a.kr);
+  T* krt = static_cast<T*>(a.krt);
+  T* vr = static_cast<T*>(a.vr);
+  for (int64_t blk = blockIdx.x; blk < (int64_t)a.batch * nkt; blk += gridDim.x) {
+    const int32_t kt = (int32_t)(blk % nkt);
+    const int32_t b = (int32_t)(blk / nkt);
+    __syncthreads();
+    for (int idx = tid; idx < TK * HALF; idx += 256) {
+      const int jj = idx / HALF, i = idx % HALF;
+      const int32_t key = kt * TK + jj;
+      float c = 1.f, sn = 0.f;
+      if (a.rope.enabled && key < a.num_k) rope_cos_sin(pf_key_pos(geo, key), a.rope.inv_freq[i], c, sn);
+      cs_lds[jj][i][0] = c;
+      cs_lds[jj][i][1] = sn;
+      if (b == 0) {
+        a.cs_k[((int64_t)key * HALF + i) * 2 + 0] = c;
+        a.cs_k[((int64_t)key * HALF + i) * 2 + 1] = sn;
+      }
+    }
+    __syncthreads();
+    const int32_t key = kt * TK + j;
+    for (int32_t h = 0; h < a.hkv; ++h) {
+      const int64_t bh = (int64_t)b * a.hkv + h;
+      float x1[PQ], x2[PQ], vv[DQ];
+      if (key < a.num_k) {
+        const int64_t src = (((int64_t)b * a.num_k + key) * a.hkv + h) * D;
+        load_vec(k + src + PQ * qq, x1, PQ);
+        load_vec(k + src + HALF + PQ * qq, x2, PQ);
+        load_vec(v + src + DQ * qq, vv, DQ);
+#pragma unroll
+        for (int e = 0; e < PQ; ++e) {
+          const float c = cs_lds[j][PQ * qq + e][0], sn = cs_lds[j][PQ * qq + e][1];
+          const float y1 = x1[e] * c - x2[e] * sn, y2 = x2[e] * c + x1[e] * sn;
+          x1[e] = y1;
+          x2[e] = y2;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < PQ; ++e) x1[e] = x2[e] = 0.f;
+#pragma unroll
+        for (int e = 0; e < DQ; ++e) vv[e] = 0.f;
+      }
+      T* krow = kr + (bh * a.nkp + key) * D;
+      store_vec(krow + PQ * qq, x1, PQ);
+      store_vec(krow + HALF + PQ * qq, x2, PQ);
+      store_vec(vr + (bh * a.nkp + key) * D + DQ * qq, vv, DQ);
+      // K'^T through LDS (rounded exactly as the row-major copy)
+      const int js = vt_slot(j);
+#pragma unroll
+      for (int e = 0; e < PQ; ++e) {
+        Elem<T>::store(&t_lds[PQ * qq + e][js], x1[e]);
+        Elem<T>::store(&t_lds[HALF + PQ * qq + e][js], x2[e]);
+      }
+      __syncthreads();
+      constexpr int EP = 16 / sizeof(T);
+      for (int idx = tid; idx < D * (TK / EP); idx += 256) {
+        const int d = idx / (TK / EP), c = idx % (TK / EP);
+        *reinterpret_cast<u32x4*>(krt + (bh * D + d) * a.nkp + kt * TK + c * EP) =
+            *reinterpret_cast<const u32x4*>(&t_lds[d][c * EP]);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. query prep: one workgroup per (batch, query head, 64-query tile)
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_query_prep_kernel(BackwardArgs a) {
+  constexpr int TQ = 64;
+  constexpr int HALF = D / 2;
+  constexpr int PQ = HALF / 4;
+  constexpr int DQ = D / 4;
+  __shared__ float cs_lds[TQ][HALF][2];
+  __shared__ T t_lds[D][TQ + 8];
+  __shared__ T o_lds[D][TQ + 8];
+  PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, 64, 64};
+  const int32_t nqt = a.tqp / TQ;
+  const int tid = threadIdx.x;
+  const int j = tid >> 2, qq = tid & 3;
+  const T* q = static_cast<const T*>(a.q);
+  const T* o = static_cast<const T*>(a.out);
+  const T* dout = static_cast<const T*>(a.d_out);
+  T* qs = static_cast<T*>(a.qs);
+  T* qst = static_cast<T*>(a.qst);
+  T* dot = static_cast<T*>(a.dot);
+  for (int64_t blk = blockIdx.x; blk < (int64_t)a.batch * a.hq * nqt; blk += gridDim.x) {
+    const int32_t qt = (int32_t)(blk % nqt);
+    const int64_t rest = blk / nqt;
+    const int32_t h = (int32_t)(rest % a.hq);
+    const int32_t b = (int32_t)(rest / a.hq);
+    __syncthreads();
+    for (int idx = tid; idx < TQ * HALF; idx += 256) {
+      const int jj = idx / HALF, i = idx % HALF;
+      const int32_t t = qt * TQ + jj;
+      float c = 1.f, sn = 0.f;
+      if (a.rope.enabled && t < a.num_q) rope_cos_sin(pf_query_pos(geo, t), a.rope.inv_freq[i], c, sn);
+      cs_lds[jj][i][0] = c;
+      cs_lds[jj][i][1] = sn;
+      if (b == 0 && h == 0 && t < a.num_q) {
+        a.cs_q[((int64_t)t * HALF + i) * 2 + 0] = c;
+        a.cs_q[((int64_t)t * HALF + i) * 2 + 1] = sn;
+      }
+    }
+    __syncthreads();
+    const int32_t t = qt * TQ + j;
+    const bool row_ok = t < a.num_q;
+    const int64_t bh = (int64_t)b * a.hq + h;
+    float x1[PQ], x2[PQ], od[DQ];
+    float dsum = 0.f;
+    if (row_ok) {
+      const int64_t src = (((int64_t)b * a.num_q + t) * a.hq + h) * D;
+      load_vec(q + src + PQ * qq, x1, PQ);
+      load_vec(q + src + HALF + PQ * qq, x2, PQ);
+#pragma unroll
+      for (int e = 0; e < PQ; ++e) {
+        const float c = cs_lds[j][PQ * qq + e][0], sn = cs_lds[j][PQ * qq + e][1];
+        const float y1 = x1[e] * c - x2[e] * sn, y2 = x2[e] * c + x1[e] * sn;
+        x1[e] = y1 * a.scale_log2;
+        x2[e] = y2 * a.scale_log2;
+      }
+      float ov[DQ];
+      load_vec(dout + src + DQ * qq, od, DQ);
+      load_vec(o + src + DQ * qq, ov, DQ);
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) dsum += od[e] * ov[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < PQ; ++e) x1[e] = x2[e] = 0.f;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) od[e] = 0.f;
+    }
+    // the four quarter-rows of a query are four consecutive lanes
+    dsum += __shfl_xor(dsum, 1);
+    dsum += __shfl_xor(dsum, 2);
+    T* qrow = qs + (bh * a.tqp + t) * D;
+    store_vec(qrow + PQ * qq, x1, PQ);
+    store_vec(qrow + HALF + PQ * qq, x2, PQ);
+    const int js = vt_slot(j);
+#pragma unroll
+    for (int e = 0; e < PQ; ++e) {
+      Elem<T>::store(&t_lds[PQ * qq + e][js], x1[e]);
+      Elem<T>::store(&t_lds[HALF + PQ * qq + e][js], x2[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) Elem<T>::store(&o_lds[DQ * qq + e][js], od[e]);
+    if (qq == 0) {
+      a.lse2[bh * a.tqp + t] = row_ok ? a.lse[bh * a.num_q + t] * kLog2e : INFINITY;
+      a.di[bh * a.tqp + t] = dsum;
+    }
+    __syncthreads();
+    constexpr int EP = 16 / sizeof(T);
+    for (int idx = tid; idx < D * (TQ / EP); idx += 256) {
+      const int d = idx / (TQ / EP), c = idx % (TQ / EP);
+      *reinterpret_cast<u32x4*>(qst + (bh * D + d) * a.tqp + qt * TQ + c * EP) =
+          *reinterpret_cast<const u32x4*>(&t_lds[d][c * EP]);
+      *reinterpret_cast<u32x4*>(dot + (bh * D + d) * a.tqp + qt * TQ + c * EP) =
+          *reinterpret_cast<const u32x4*>(&o_lds[d][c * EP]);
+    }
+  }
+}
+
+// 32x32x16 MFMA lane layout (lane l, half hf = l/32, col = l%32):
+//   A[m][k]: lane (m + 32*(k/8)) element k%8        B[k][n]: lane (n + 32*(k/8)) element k%8
+//   D[m][n]: lane (n + 32*((m/4)%2)) register 4*(m/8) + m%4
+// so register r of a D tile holds row m = 8*(r/4) + 4*hf + r%4 of column col.
+
+// ---------------------------------------------------------------------------
+// 3. dk / dv (bf16 MFMA)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
+  constexpr int BK = 128;          // keys per workgroup, 32 per wave
+  constexpr int BQ = 64;           // queries per step
+  constexpr int KS = D / 16;
+  constexpr int MT = D / 32;
+  constexpr int RPAD = D + 8;      // row-major query rows in LDS
+  constexpr int TPAD = BQ + 8;     // d-major rows in LDS
+  constexpr int RP = BQ * D / 8 / 256;   // 16-byte pieces per thread per block (row-major)
+  constexpr int TP = D * BQ / 8 / 256;   // (d-major)
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][BQ * RPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t o_lds[2][BQ * RPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[2][D * TPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t ot_lds[2][D * TPAD];
+  __shared__ __attribute__((aligned(16))) float l_lds[2][BQ];
+  __shared__ __attribute__((aligned(16))) float di_lds[2][BQ];
+
+  const int32_t n_kt = (a.num_k + BK - 1) / BK;
+  const int64_t pairs = (int64_t)a.batch * a.hkv;
+  // key-tile-major order: the tiles holding pinned keys (seen by every query,
+  // the longest) start first; tiles of one (batch, KV head) land on one XCD
+  const int64_t lin = blockIdx.x;
+  if (lin >= pairs * n_kt) return;
+  const int32_t kt = (int32_t)(lin / pairs);
+  const int32_t kvh = (int32_t)((lin % pairs) % a.hkv);
+  const int32_t b = (int32_t)((lin % pairs) / a.hkv);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int32_t k0 = kt * BK;
+  const int32_t kw = k0 + 32 * wave + col;     // this lane's key
+  const int64_t bkv = (int64_t)b * a.hkv + kvh;
+  const uint16_t* kr = static_cast<const uint16_t*>(a.kr) + bkv * a.nkp * D;
+  const uint16_t* vr = static_cast<const uint16_t*>(a.vr) + bkv * a.nkp * D;
+
+  // the wave's keys as B operands: B[k = dim][n = key]
+  bf16x8 kop[KS], vop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kop[ks] = *reinterpret_cast<const bf16x8*>(kr + (int64_t)kw * D + 16 * ks + 8 * hf);
+    vop[ks] = *reinterpret_cast<const bf16x8*>(vr + (int64_t)kw * D + 16 * ks + 8 * hf);
+  }
+
+  // query blocks that can see the tile: from the first query at or after k0 to
+  // the last query (pinned keys) or to the end of the last key's window
+  const int32_t k1 = pf_min(k0 + BK, a.num_k) - 1;
+  const int32_t off = a.num_k - a.num_q;          // key index of query 0
+  const int32_t t_lo = pf_max(0, k0 - off);
+  const int32_t t_hi = k0 < a.prefix_len ? a.num_q - 1 : pf_min(a.num_q - 1, k1 + a.window - 1 - off);
+  const int32_t qb_lo = t_lo / BQ, qb_hi = t_lo <= t_hi ? t_hi / BQ : -1;
+  const int32_t n_qb = qb_hi - qb_lo + 1;
+  const int32_t n_it = n_qb > 0 ? n_qb * a.group : 0;
+  PrefillGeom cg{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, BQ, BK};
+
+  u32x4 qreg[RP], oreg[RP], qtreg[TP], otreg[TP];
+  float lreg = 0.f;
+  // block (head h, query block qb) -> registers
+#define PS_BW_GLOAD(H, QB)                                                                           \
+  do {                                                                                              \
+    const int64_t bh_ = (int64_t)b * a.hq + (H);                                                    \
+    const uint16_t* qsb_ = static_cast<const uint16_t*>(a.qs) + (bh_ * a.tqp + (int64_t)(QB) * BQ) * D; \
+    const uint16_t* qtb_ = static_cast<const uint16_t*>(a.qst) + bh_ * D * a.tqp + (int64_t)(QB) * BQ; \
+    const uint16_t* otb_ = static_cast<const uint16_t*>(a.dot) + bh_ * D * a.tqp + (int64_t)(QB) * BQ; \
+    _Pragma("unroll") for (int pc_ = 0; pc_ < RP; ++pc_) {                                          \
+      const int piece_ = tid + 256 * pc_;                                                           \
+      const int r_ = piece_ / (D / 8), c_ = (piece_ % (D / 8)) * 8;                                 \
+      qreg[pc_] = *reinterpret_cast<const u32x4*>(qsb_ + (int64_t)r_ * D + c_);                     \
+      const int32_t tr_ = pf_min((QB) * BQ + r_, a.num_q - 1);                                       \
+      oreg[pc_] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.d_out) +           \
+                                                  (((int64_t)b * a.num_q + tr_) * a.hq + (H)) * D + c_); \
+    }                                                                                               \
+    _Pragma("unroll") for (int pc_ = 0; pc_ < TP; ++pc_) {                                          \
+      const int piece_ = tid + 256 * pc_;                                                           \
+      const int r_ = piece_ / (BQ / 8), c_ = (piece_ % (BQ / 8)) * 8;                               \
+      qtreg[pc_] = *reinterpret_cast<const u32x4*>(qtb_ + (int64_t)r_ * a.tqp + c_);                \
+      otreg[pc_] = *reinterpret_cast<const u32x4*>(otb_ + (int64_t)r_ * a.tqp + c_);                \
+    }                                                                                               \
+    if (tid < 2 * BQ)                                                                               \
+      lreg = (tid < BQ ? a.lse2 : a.di)[bh_ * a.tqp + (int64_t)(QB) * BQ + (tid & (BQ - 1))];        \
+  } while (0)
+#define PS_BW_LSTORE(BUF)                                                                            \
+  do {                                                                                              \
+    _Pragma("unroll") for (int pc_ = 0; pc_ < RP; ++pc_) {                                          \
+      const int piece_ = tid + 256 * pc_;                                                           \
+      const int r_ = piece_ / (D / 8), c_ = (piece_ % (D / 8)) * 8;                                 \
+      *reinterpret_cast<u32x4*>(&q_lds[BUF][r_ * RPAD + c_]) = qreg[pc_];                           \
+      *reinterpret_cast<u32x4*>(&o_lds[BUF][r_ * RPAD + c_]) = oreg[pc_];                           \
+    }                                                                                               \
+    _Pragma("unroll") for (int pc_ = 0; pc_ < TP; ++pc_) {                                          \
+      const int piece_ = tid + 256 * pc_;                                                           \
+      const int r_ = piece_ / (BQ / 8), c_ = (piece_ % (BQ / 8)) * 8;                               \
+      *reinterpret_cast<u32x4*>(&qt_lds[BUF][r_ * TPAD + c_]) = qtreg[pc_];                         \
+      *reinterpret_cast<u32x4*>(&ot_lds[BUF][r_ * TPAD + c_]) = otreg[pc_];                         \
+    }                                                                                               \
+    if (tid < 2 * BQ) (tid < BQ ? l_lds[BUF] : di_lds[BUF])[tid & (BQ - 1)] = lreg;                 \
+  } while (0)
+
+  f32x16 dk[MT], dv[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dk[mt][i] = dv[mt][i] = 0.f;
+  f32x16 zero;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) zero[i] = 0.f;
+
+  // iteration it -> (head in group, query block); blocks with no visible pair are skipped
+  int32_t it = 0;
+  int kind = 0;
+  while (it < n_it && (kind = pf_classify(cg, qb_lo + it % n_qb, kt)) == 0) ++it;
+  if (it < n_it) {
+    PS_BW_GLOAD(kvh * a.group + it / n_qb, qb_lo + it % n_qb);
+    PS_BW_LSTORE(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (it < n_it) {
+    const int32_t h = kvh * a.group + it / n_qb;
+    const int32_t qb = qb_lo + it % n_qb;
+    const int cur_kind = kind;
+    int32_t nx = it + 1;
+    int nkind = 0;
+    while (nx < n_it && (nkind = pf_classify(cg, qb_lo + nx % n_qb, kt)) == 0) ++nx;
+    if (nx < n_it) PS_BW_GLOAD(kvh * a.group + nx / n_qb, qb_lo + nx % n_qb);
+    (void)h;
+
+    // S = Q'' K'^T and dP = dO V^T: two 32-query M-tiles
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+      const uint16_t* qrow = &q_lds[buf][(32 * m2 + col) * RPAD + 8 * hf];
+      const uint16_t* orow = &o_lds[buf][(32 * m2 + col) * RPAD + 8 * hf];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(orow + 16 * ks);
+        s[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[ks], ks == 0 ? zero : s[m2], 0, 0, 0);
+        dp[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vop[ks], ks == 0 ? zero : dp[m2], 0, 0, 0);
+      }
+    }
+    // register r of tile m2 <-> query 32*m2 + 8*(r/4) + 4*hf + r%4 of the block
+    bf16x8 pb[4], sb[4];
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ql = 32 * m2 + 8 * r4 + 4 * hf;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&l_lds[buf][ql]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&di_lds[buf][ql]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          float p = __builtin_amdgcn_exp2f(s[m2][r] - l4[e]);
+          if (cur_kind == 2) {
+            const int32_t u = off + qb * BQ + ql + e;
+            if (!pf_visible(cg, u, kw) || kw >= a.num_k) p = 0.f;
+          }
+          const float ds = p * (dp[m2][r] - d4[e]);
+          pb[2 * m2 + (r >> 3)][r & 7] = (bf16)p;
+          sb[2 * m2 + (r >> 3)][r & 7] = (bf16)ds;
+        }
+      }
+    // dV^T += dO^T P and dK^T += Q''^T dS over the block's 64 queries (4 k-steps)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&ot_lds[buf][(32 * mt + col) * TPAD + 16 * j + 8 * hf]);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qt_lds[buf][(32 * mt + col) * TPAD + 16 * j + 8 * hf]);
+        dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pb[j], dv[mt], 0, 0, 0);
+        dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb[j], dk[mt], 0, 0, 0);
+      }
+    if (nx < n_it) PS_BW_LSTORE(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    it = nx;
+    kind = nkind;
+  }
+#undef PS_BW_GLOAD
+#undef PS_BW_LSTORE
+
+  // ---- epilogue: register r of tile mt <-> dim 32*mt + 8*(r/4) + 4*hf + r%4 of key kw;
+  // dK' = ln2 * acc, rotated back by -position (dims d and d + D/2 pair up: tiles mt, mt + MT/2)
+  if (kw >= a.num_k) return;
+  uint16_t* dkrow = static_cast<uint16_t*>(a.dk) + (((int64_t)b * a.num_k + kw) * a.hkv + kvh) * D;
+  uint16_t* dvrow = static_cast<uint16_t*>(a.dv) + (((int64_t)b * a.num_k + kw) * a.hkv + kvh) * D;
+  const float* cs = a.cs_k + (int64_t)kw * D;
+#pragma unroll
+  for (int mt = 0; mt < MT / 2; ++mt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * mt + 8 * r4 + 4 * hf;
+      float g1[4], g2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float c = cs[2 * (d + e)], sn = cs[2 * (d + e) + 1];
+        const float x1 = dk[mt][4 * r4 + e] * kLn2f, x2 = dk[mt + MT / 2][4 * r4 + e] * kLn2f;
+        g1[e] = x1 * c + x2 * sn;
+        g2[e] = x2 * c - x1 * sn;
+      }
+      *reinterpret_cast<uint2*>(dkrow + d) = uint2{pack_bf16x2(g1[0], g1[1]), pack_bf16x2(g1[2], g1[3])};
+      *reinterpret_cast<uint2*>(dkrow + d + D / 2) = uint2{pack_bf16x2(g2[0], g2[1]), pack_bf16x2(g2[2], g2[3])};
+    }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * mt + 8 * r4 + 4 * hf;
+      *reinterpret_cast<uint2*>(dvrow + d) = uint2{pack_bf16x2(dv[mt][4 * r4], dv[mt][4 * r4 + 1]),
+                                                   pack_bf16x2(dv[mt][4 * r4 + 2], dv[mt][4 * r4 + 3])};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4. dq (bf16 MFMA): the forward's decomposition and key-tile schedule
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
+  constexpr int BM = 128, BN = 64;
+  constexpr int KS = D / 16;
+  constexpr int MT = D / 32;
+  constexpr int KPAD = D + 8;
+  constexpr int TPAD = BN + 8;
+  constexpr int RP = BN * D / 8 / 256;
+  constexpr int TP = D * BN / 8 / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN * KPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t t_lds[2][D * TPAD];
+
+  PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, BM, BN};
+  const int32_t n_qt = pf_num_qtiles(geo);
+  // items ordered (batch, KV head, q-tile, head-in-group), each XCD a contiguous run
+  const int64_t total = (int64_t)a.batch * a.hq * n_qt;
+  const int64_t per = (total + 7) / 8;
+  const int64_t lin = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (lin >= total) return;
+  const int32_t hg = (int32_t)(lin % a.group);
+  int64_t rest = lin / a.group;
+  const int32_t qt = (int32_t)(rest % n_qt);
+  rest /= n_qt;
+  const int32_t kvh = (int32_t)(rest % a.hkv);
+  const int32_t b = (int32_t)(rest / a.hkv);
+  const int32_t hq = kvh * a.group + hg;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int64_t bkv = (int64_t)b * a.hkv + kvh;
+  const uint16_t* kr = static_cast<const uint16_t*>(a.kr) + bkv * a.nkp * D;
+  const uint16_t* vr = static_cast<const uint16_t*>(a.vr) + bkv * a.nkp * D;
+  const uint16_t* ktr = static_cast<const uint16_t*>(a.krt) + bkv * D * a.nkp;
+
+  u32x4 kreg[RP], vreg[RP], treg[TP];
+#define PS_BQ_GLOAD(KT)                                                                              \
+  do {                                                                                              \
+    _Pragma("unroll") for (int pc_ = 0; pc_ < RP; ++pc_) {                                          \
+      const int piece_ = tid + 256 * pc_;                                                           \
+      const int64_t o_ = ((int64_t)(KT) * BN + piece_ / (D / 8)) * D + (piece_ % (D / 8)) * 8;     \
+      kreg[pc_] = *reinterpret_cast<const u32x4*>(kr + o_);                                         \
+      vreg[pc_] = *reinterpret_cast<const u32x4*>(vr + o_);                                         \
+    }                                                                                               \
+    _Pragma("unroll") for (int pc_ = 0; pc_ < TP; ++pc_) {                                          \
+      const int piece_ = tid + 256 * pc_;                                                           \
+      treg[pc_] = *reinterpret_cast<const u32x4*>(ktr + (int64_t)(piece_ / (BN / 8)) * a.nkp +     \
+                                                  (int64_t)(KT) * BN + (piece_ % (BN / 8)) * 8);    \
+    }                                                                                               \
+  } while (0)
+#define PS_BQ_LSTORE(BUF)                                                                            \
+  do {                                                                                              \
+    _Pragma("unroll") for (int pc_ = 0; pc_ < RP; ++pc_) {                                          \
+      const int piece_ = tid + 256 * pc_;                                                           \
+      const int o_ = (piece_ / (D / 8)) * KPAD + (piece_ % (D / 8)) * 8;                            \
+      *reinterpret_cast<u32x4*>(&k_lds[BUF][o_]) = kreg[pc_];                                       \
+      *reinterpret_cast<u32x4*>(&v_lds[BUF][o_]) = vreg[pc_];                                       \
+    }                                                                                               \
+    _Pragma("unroll") for (int pc_ = 0; pc_ < TP; ++pc_) {                                          \
+      const int piece_ = tid + 256 * pc_;                                                           \
+      *reinterpret_cast<u32x4*>(&t_lds[BUF][(piece_ / (BN / 8)) * TPAD + (piece_ % (BN / 8)) * 8]) = \
+          treg[pc_];                                                                                \
+    }                                                                                               \
+  } while (0)
+
+  const TileRange tr = pf_tile_range(geo, qt);
+  const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
+  auto cand_tile = [&](int32_t ci) { return ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix); };
+  int32_t ci = 0;
+  int kind = 0;
+  while (ci < n_cand && (kind = pf_classify(geo, qt, cand_tile(ci))) == 0) ++ci;
+  if (ci < n_cand) PS_BQ_GLOAD(cand_tile(ci));
+
+  // this lane's query: B operands of S^T = K' Q''^T and dP^T = V dO^T
+  const int32_t t = qt * BM + wave * 32 + col;
+  const bool row_ok = t < a.num_q;
+  const int32_t tc = row_ok ? t : 0;
+  const int32_t u = a.num_k - a.num_q + t;
+  const int64_t bh = (int64_t)b * a.hq + hq;
+  bf16x8 qop[KS], dop[KS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.qs) + (bh * a.tqp + tc) * D;
+    const uint16_t* drow = static_cast<const uint16_t*>(a.d_out) + (((int64_t)b * a.num_q + tc) * a.hq + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qop[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hf);
+      dop[ks] = *reinterpret_cast<const bf16x8*>(drow + 16 * ks + 8 * hf);
+    }
+  }
+  const float lse2 = row_ok ? a.lse2[bh * a.tqp + t] : INFINITY;
+  const float di = row_ok ? a.di[bh * a.tqp + t] : 0.f;
+  const int32_t pre_end = row_ok ? pf_min(a.prefix_len, u + 1) : 0;
+  int32_t band_lo = pf_max(a.prefix_len, u - a.window + 1);
+  const int32_t band_hi = pf_min(u, a.num_k - 1);
+  uint32_t band_w = (uint32_t)(band_hi - band_lo);
+  if (!row_ok || band_hi < band_lo) {
+    band_lo = 0x7fffffff;
+    band_w = 0;
+  }
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+  f32x16 zero;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) zero[i] = 0.f;
+
+  if (ci < n_cand) PS_BQ_LSTORE(0);
+  __syncthreads();
+  int buf = 0;
+  while (ci < n_cand) {
+    const int32_t kt = cand_tile(ci);
+    const int cur_kind = kind;
+    int32_t cn = ci + 1;
+    int nkind = 0;
+    while (cn < n_cand && (nkind = pf_classify(geo, qt, cand_tile(cn))) == 0) ++cn;
+    if (cn < n_cand) PS_BQ_GLOAD(cand_tile(cn));
+
+    f32x16 st[2], dpt[2];
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+      const uint16_t* krow = &k_lds[buf][(32 * m2 + col) * KPAD + 8 * hf];
+      const uint16_t* vrow = &v_lds[buf][(32 * m2 + col) * KPAD + 8 * hf];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + 16 * ks);
+        st[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[ks], ks == 0 ? zero : st[m2], 0, 0, 0);
+        dpt[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dop[ks], ks == 0 ? zero : dpt[m2], 0, 0, 0);
+      }
+    }
+    // register i of tile m2 <-> key kt*BN + 32*m2 + 8*(i/4) + 4*hf + i%4
+    bf16x8 sb[4];
+    const int32_t kbase = kt * BN + 4 * hf;
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = __builtin_amdgcn_exp2f(st[m2][i] - lse2);
+        if (cur_kind == 2) {
+          const int32_t key = kbase + 32 * m2 + 8 * (i >> 2) + (i & 3);
+          const bool vis = key < pre_end || (uint32_t)(key - band_lo) <= band_w;
+          if (!vis) p = 0.f;
+        }
+        sb[2 * m2 + (i >> 3)][i & 7] = (bf16)(p * (dpt[m2][i] - di));
+      }
+    // dQ''^T += K'^T dS^T: k-step j covers keys 16j + 8*(e/4) + 4*hf + e%4
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&t_lds[buf][(32 * mt + col) * TPAD + 16 * j + 8 * hf]);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, sb[j], acc[mt], 0, 0, 0);
+      }
+    if (cn < n_cand) PS_BQ_LSTORE(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    ci = cn;
+    kind = nkind;
+  }
+#undef PS_BQ_GLOAD
+#undef PS_BQ_LSTORE
+
+  if (!row_ok) return;
+  // dQ' = scale * acc, rotated back by -position
+  uint16_t* dqrow = static_cast<uint16_t*>(a.dq) + (((int64_t)b * a.num_q + t) * a.hq + hq) * D;
+  const float* cs = a.cs_q + (int64_t)t * D;
+#pragma unroll
+  for (int mt = 0; mt < MT / 2; ++mt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * mt + 8 * r4 + 4 * hf;
+      float g1[4], g2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float c = cs[2 * (d + e)], sn = cs[2 * (d + e) + 1];
+        const float x1 = acc[mt][4 * r4 + e] * a.scale, x2 = acc[mt + MT / 2][4 * r4 + e] * a.scale;
+        g1[e] = x1 * c + x2 * sn;
+        g2[e] = x2 * c - x1 * sn;
+      }
+      *reinterpret_cast<uint2*>(dqrow + d) = uint2{pack_bf16x2(g1[0], g1[1]), pack_bf16x2(g1[2], g1[3])};
+      *reinterpret_cast<uint2*>(dqrow + d + D / 2) = uint2{pack_bf16x2(g2[0], g2[1]), pack_bf16x2(g2[2], g2[3])};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 debug path: one thread per query row (dq) / key row (dk, dv)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BackwardArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (idx >= (int64_t)a.batch * a.hq * a.num_q) return;
+  const int32_t t = (int32_t)(idx % a.num_q);
+  const int32_t hq = (int32_t)((idx / a.num_q) % a.hq);
+  const int32_t b = (int32_t)(idx / ((int64_t)a.num_q * a.hq));
+  const int32_t kvh = hq / a.group;
+  PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, 64, 64};
+  const int32_t u = a.num_k - a.num_q + t;
+  const int64_t bh = (int64_t)b * a.hq + hq;
+  const int64_t bkv = (int64_t)b * a.hkv + kvh;
+  const float* qrow = static_cast<const float*>(a.qs) + (bh * a.tqp + t) * D;
+  const float* drow = static_cast<const float*>(a.d_out) + (((int64_t)b * a.num_q + t) * a.hq + hq) * D;
+  const float* kr = static_cast<const float*>(a.kr) + bkv * a.nkp * D;
+  const float* vr = static_cast<const float*>(a.vr) + bkv * a.nkp * D;
+  const float lse2 = a.lse2[bh * a.tqp + t], di = a.di[bh * a.tqp + t];
+  float acc[D];
+  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+  for (int32_t key = 0; key <= pf_min(u, a.num_k - 1); ++key) {
+    if (!pf_visible(geo, u, key)) continue;
+    float s = 0.f, dp = 0.f;
+    for (int d = 0; d < D; ++d) {
+      s += qrow[d] * kr[(int64_t)key * D + d];
+      dp += drow[d] * vr[(int64_t)key * D + d];
+    }
+    const float ds = __builtin_amdgcn_exp2f(s - lse2) * (dp - di);
+    for (int d = 0; d < D; ++d) acc[d] += ds * kr[(int64_t)key * D + d];
+  }
+  float* dq = static_cast<float*>(a.dq) + (((int64_t)b * a.num_q + t) * a.hq + hq) * D;
+  const float* cs = a.cs_q + (int64_t)t * D;
+  for (int i = 0; i < D / 2; ++i) {
+    const float c = cs[2 * i], sn = cs[2 * i + 1];
+    const float x1 = acc[i] * a.scale, x2 = acc[i + D / 2] * a.scale;
+    dq[i] = x1 * c + x2 * sn;
+    dq[i + D / 2] = x2 * c - x1 * sn;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(BackwardArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (idx >= (int64_t)a.batch * a.hkv * a.num_k) return;
+  const int32_t key = (int32_t)(idx % a.num_k);
+  const int32_t kvh = (int32_t)((idx / a.num_k) % a.hkv);
+  const int32_t b = (int32_t)(idx / ((int64_t)a.num_k * a.hkv));
+  PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, 64, 64};
+  const int64_t bkv = (int64_t)b * a.hkv + kvh;
+  const float* krow = static_cast<const float*>(a.kr) + (bkv * a.nkp + key) * D;
+  const float* vrow = static_cast<const float*>(a.vr) + (bkv * a.nkp + key) * D;
+  const int32_t off = a.num_k - a.num_q;
+  float dk[D], dv[D];
+  for (int d = 0; d < D; ++d) dk[d] = dv[d] = 0.f;
+  for (int32_t g = 0; g < a.group; ++g) {
+    const int32_t hq = kvh * a.group + g;
+    const int64_t bh = (int64_t)b * a.hq + hq;
+    for (int32_t t = pf_max(0, key - off); t < a.num_q; ++t) {
+      if (!pf_visible(geo, off + t, key)) continue;
+      const float* qrow = static_cast<const float*>(a.qs) + (bh * a.tqp + t) * D;
+      const float* drow = static_cast<const float*>(a.d_out) + (((int64_t)b * a.num_q + t) * a.hq + hq) * D;
+      float s = 0.f, dp = 0.f;
+      for (int d = 0; d < D; ++d) {
+        s += qrow[d] * krow[d];
+        dp += drow[d] * vrow[d];
+      }
+      const float p = __builtin_amdgcn_exp2f(s - a.lse2[bh * a.tqp + t]);
+      const float ds = p * (dp - a.di[bh * a.tqp + t]);
+      for (int d = 0; d < D; ++d) {
+        dk[d] += ds * qrow[d];
+        dv[d] += p * drow[d];
+      }
+    }
+  }
+  float* dkr = static_cast<float*>(a.dk) + (((int64_t)b * a.num_k + key) * a.hkv + kvh) * D;
+  float* dvr = static_cast<float*>(a.dv) + (((int64_t)b * a.num_k + key) * a.hkv + kvh) * D;
+  const float* cs = a.cs_k + (int64_t)key * D;
+  for (int i = 0; i < D / 2; ++i) {
+    const float c = cs[2 * i], sn = cs[2 * i + 1];
+    const float x1 = dk[i] * kLn2f, x2 = dk[i + D / 2] * kLn2f;
+    dkr[i] = x1 * c + x2 * sn;
+    dkr[i + D / 2] = x2 * c - x1 * sn;
+  }
+  for (int d = 0; d < D; ++d) dvr[d] = dv[d];
+}
+
+template <typename T, int D>
+hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t stream) {
+  auto clamp = [](int64_t x) { return (uint32_t)(x < 1 ? 1 : (x > 16384 ? 16384 : x)); };
+  hipLaunchKernelGGL((bwd_key_prep_kernel<T, D>), dim3(clamp((int64_t)a.batch * (a.nkp / 64))), dim3(256), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_query_prep_kernel<T, D>), dim3(clamp((int64_t)a.batch * a.hq * (a.tqp / 64))), dim3(256),
+                     0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (sizeof(T) == 2) {
+    const int64_t kv_items = (int64_t)a.batch * a.hkv * ((a.num_k + 127) / 128);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((uint32_t)kv_items), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t q_items = (int64_t)a.batch * a.hq * ((a.num_q + 127) / 128);
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((uint32_t)(((q_items + 7) / 8) * 8)), dim3(256), 0, stream, a);
+  } else {
+    const int64_t kv_rows = (int64_t)a.batch * a.hkv * a.num_k;
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), dim3((uint32_t)((kv_rows + 63) / 64)), dim3(64), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t q_rows = (int64_t)a.batch * a.hq * a.num_q;
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), dim3((uint32_t)((q_rows + 63) / 64)), dim3(64), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
+  if (a.batch == 0 || a.num_q == 0) return hipSuccess;
+  if (a.dtype == PS_BF16)
+    return a.head_dim == 64 ? launch_backward_t<uint16_t, 64>(a, stream) : launch_backward_t<uint16_t, 128>(a, stream);
+  return a.head_dim == 64 ? launch_backward_t<float, 64>(a, stream) : launch_backward_t<float, 128>(a, stream);
+}
+
+}  // namespace ps

@@ -19,6 +19,7 @@
 // are directly the B operand of O^T += V^T P^T (V^T staged through LDS).
 #include "ps_internal.h"
 #include "ps_sched.h"
+#include "ps_tiles.h"
 
 namespace ps {
 namespace {
@@ -45,16 +46,6 @@ struct PfTraits<float> {
   static constexpr int BM = 64, BN = 64;
 };
 
-__host__ __device__ inline int32_t nk_padded(int32_t nk) { return (nk + 63) / 64 * 64; }
-
-// Position of key k inside its 16-key group of the V^T rows.  Stored order per
-// group: keys 0-3, 8-11, 4-7, 12-15, so that the 8 keys one MFMA lane needs for
-// a PV k-step (16j + 8*(e/4) + 4*half + e%4, e = 0..7) are 16 contiguous bytes.
-__host__ __device__ inline int32_t vt_slot(int32_t k) {
-  const int32_t kl = k & 15;
-  return (k & ~15) | (((kl >> 2) & 1) << 3) | ((kl >> 3) << 2) | (kl & 3);
-}
-
 // ---------------------------------------------------------------------------
 // 1. prep: rotated K [b][hkv][nkp][D], V^T [b][hkv][D][nkp], query cos/sin table
 // ---------------------------------------------------------------------------
@@ -62,39 +53,6 @@ __host__ __device__ inline int32_t vt_slot(int32_t k) {
 // LDS and reused for every KV head.  Each thread owns a quarter of one key row
 // (16-byte loads and stores); V is transposed through LDS so the V^T rows are
 // written contiguously.  Keys past num_k are written as zeros.
-template <typename T>
-__device__ inline void load_vec(const T* p, float* x, int n) {  // n contiguous elements, 16-byte loads
-  constexpr int E = 16 / sizeof(T);
-  for (int c = 0; c < n; c += E) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(p + c);
-    if (sizeof(T) == 2) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[c + 2 * e] = lo_bf16(w[e]);
-        x[c + 2 * e + 1] = hi_bf16(w[e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[c + e] = __uint_as_float(w[e]);
-    }
-  }
-}
-template <typename T>
-__device__ inline void store_vec(T* p, const float* x, int n) {
-  constexpr int E = 16 / sizeof(T);
-  for (int c = 0; c < n; c += E) {
-    u32x4 w;
-    if (sizeof(T) == 2) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[c + 2 * e], x[c + 2 * e + 1]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(x[c + e]);
-    }
-    *reinterpret_cast<u32x4*>(p + c) = w;
-  }
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
   constexpr int TK = 64;

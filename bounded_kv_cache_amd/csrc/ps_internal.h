@@ -73,7 +73,42 @@ struct PrefillArgs {
   void* q_rot;            // workspace: rotated, scaled queries [batch][num_q][hq][D]
 };
 
+// Backward of the masked prefill (dq, dk, dv for the raw inputs).
+struct BackwardArgs {
+  int32_t dtype;
+  int32_t hq, hkv, group, head_dim;
+  int32_t window, prefix_len;
+  int64_t kv_start;
+  int32_t batch, num_q, num_k;
+  int32_t nkp;            // keys padded to a multiple of 128
+  int32_t tqp;            // queries padded to a multiple of 64
+  const void* q;          // [batch][num_q][hq][D] raw
+  const void* k;          // [batch][num_k][hkv][D] raw
+  const void* v;
+  const void* out;        // forward output [batch][num_q][hq][D]
+  const void* d_out;      // upstream gradient, same layout
+  const float* lse;       // forward LSE [batch][hq][num_q] (natural log)
+  void* dq;
+  void* dk;
+  void* dv;
+  // workspace
+  void* kr;               // [batch][hkv][nkp][D] rotated keys
+  void* krt;              // [batch][hkv][D][nkp] rotated keys, d-major, keys permuted per 16 (vt_slot)
+  void* vr;               // [batch][hkv][nkp][D] values, zero padded
+  void* qs;               // [batch][hq][tqp][D] rotated queries * scale * log2(e)
+  void* qst;              // [batch][hq][D][tqp] the same, d-major, queries permuted per 16
+  void* dot;              // [batch][hq][D][tqp] upstream gradient, d-major, queries permuted per 16
+  float* lse2;            // [batch][hq][tqp] lse * log2(e); +inf on padding rows
+  float* di;              // [batch][hq][tqp] rowsum(d_out * out)
+  float* cs_q;            // [num_q][D/2][2] cos/sin of the query positions
+  float* cs_k;            // [nkp][D/2][2] cos/sin of the key positions
+  float scale;            // softmax scale
+  float scale_log2;       // scale * log2(e)
+  RopeFreq rope;
+};
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_chunk_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -1,0 +1,54 @@
+// Tile helpers shared by the prefill-family kernels (forward, chunk, backward).
+#pragma once
+
+#include "ps_common.h"
+
+namespace ps {
+
+__host__ __device__ inline int32_t nk_padded(int32_t nk) { return (nk + 63) / 64 * 64; }
+
+// Position of index k inside its 16-wide group of a d-major ("transposed")
+// operand row.  Stored order per group: 0-3, 8-11, 4-7, 12-15, so that the 8
+// indices one 32x32x16 MFMA lane needs for a k-step (16j + 8*(e/4) + 4*half +
+// e%4, e = 0..7) -- the order in which an S / S^T accumulator holds them --
+// are 16 contiguous bytes.
+__host__ __device__ inline int32_t vt_slot(int32_t k) {
+  const int32_t kl = k & 15;
+  return (k & ~15) | (((kl >> 2) & 1) << 3) | ((kl >> 3) << 2) | (kl & 3);
+}
+
+// n contiguous elements <-> floats, 16-byte loads / stores
+template <typename T>
+__device__ inline void load_vec(const T* p, float* x, int n) {
+  constexpr int E = 16 / sizeof(T);
+  for (int c = 0; c < n; c += E) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p + c);
+    if (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[c + 2 * e] = lo_bf16(w[e]);
+        x[c + 2 * e + 1] = hi_bf16(w[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[c + e] = __uint_as_float(w[e]);
+    }
+  }
+}
+template <typename T>
+__device__ inline void store_vec(T* p, const float* x, int n) {
+  constexpr int E = 16 / sizeof(T);
+  for (int c = 0; c < n; c += E) {
+    u32x4 w;
+    if (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[c + 2 * e], x[c + 2 * e + 1]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(x[c + e]);
+    }
+    *reinterpret_cast<u32x4*>(p + c) = w;
+  }
+}
+
+}  // namespace ps

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 2
+#define PS_ABI_VERSION 3
 
 typedef enum {
   PS_OK = 0,
@@ -192,6 +192,32 @@ ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t pref
 
 size_t ps_prefill_workspace_size(const ps_attn_desc* attn, int32_t batch, int32_t num_queries,
                                  int32_t num_keys);
+
+/* ps_prefill_attn_backward -- gradients of ps_prefill_attn for the raw
+ * inputs: dq, dk, dv from the upstream gradient d_out.  Blog "Prefix Sliding
+ * 完全拆解", section "超长 rollouts 的反向传播：截断回传": the trainer receives
+ * the last 4W tokens of a trace and back-propagates through the same masked
+ * attention (its loss mask on the last W tokens only decides which rows of
+ * d_out are non-zero); section "Kernel 实现：两层级过滤": the same tile
+ * skipping applies.
+ *   window, prefix_len, kv_start, q, k, v, batch, num_queries, num_keys :
+ *          exactly as given to ps_prefill_attn.
+ *   out  : the forward output [batch][num_queries][Hq][D].
+ *   d_out: upstream gradient, same layout and dtype.
+ *   lse  : the forward's LSE [batch][Hq][num_queries] (required).
+ *   dq   : [batch][num_queries][Hq][D]; dk, dv : [batch][num_keys][Hkv][D];
+ *          dtype of attn; fully overwritten (keys no query sees get zeros).
+ *   workspace : >= ps_prefill_backward_workspace_size(...) bytes.
+ * Deterministic: every output row has exactly one writer (no atomics). */
+ps_status ps_prefill_attn_backward(const ps_attn_desc* attn, int32_t window, int32_t prefix_len,
+                                   int64_t kv_start, const void* q, const void* k, const void* v,
+                                   const void* out, const void* d_out, const float* lse,
+                                   int32_t batch, int32_t num_queries, int32_t num_keys,
+                                   void* dq, void* dk, void* dv, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+size_t ps_prefill_backward_workspace_size(const ps_attn_desc* attn, int32_t batch,
+                                          int32_t num_queries, int32_t num_keys);
 
 /* ps_chunk_prefill_attn -- a chunk of new tokens continues cached traces:
  * attention of the chunk's queries over each sequence's ring plus the chunk

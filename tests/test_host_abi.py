@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ps_abi_version() == 2
+    assert lib.ps_abi_version() == 3
     assert lib.ps_status_string(0) == b"ok"
     assert lib.ps_status_string(3) == b"workspace too small"
 
@@ -213,3 +213,27 @@ def test_chunk_prefill_validation_and_workspace(lib):
     _, paged = _descs(page=64, mp=66, npages=100)
     assert call(cache=paged) == 1                              # paged cache without a block table
     assert lib.ps_last_error()
+
+
+def test_backward_validation_and_workspace(lib):
+    a, _ = _descs()
+    B, T, NK = 2, 300, 420
+    nkp, tqp = 512, 320
+    al = lambda x: (x + 255) // 256 * 256
+    want = (3 * al(B * 2 * nkp * 128 * 2) + 3 * al(B * 16 * tqp * 128 * 2) + 2 * al(B * 16 * tqp * 4)
+            + al(T * 128 * 4) + al(nkp * 128 * 4))
+    need = lib.ps_prefill_backward_workspace_size(ctypes.byref(a), B, T, NK)
+    assert need == want
+
+    def call(window=64, L=20, ks=500, nq=T, nk=NK, lse=FAKE, dq=FAKE, wsb=need, ws=FAKE):
+        return lib.ps_prefill_attn_backward(ctypes.byref(a), window, L, ks, FAKE, FAKE, FAKE, FAKE, FAKE, lse, B, nq, nk,
+                                            dq, FAKE, FAKE, ws, wsb, None)
+    assert call(wsb=need - 1) == 3
+    assert call(lse=None) == 1
+    assert call(dq=None) == 1
+    assert call(window=0) == 1
+    assert call(L=500) == 1                 # prefix longer than the key array
+    assert call(ks=10) == 1                 # kv_start before the end of the prefix
+    assert call(nq=NK + 1) == 1             # more queries than keys
+    assert call(nq=NK, ks=600) == 1         # queries reach into the prefix with a gap
+    assert call(nq=0) == 0
