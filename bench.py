@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the decode position sweep (flatness)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other decode workloads")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunk prefill that reads the ring")
-    ap.add_argument("--only", choices=["decode", "prefill", "chunk"], default=None,
+    ap.add_argument("--no-backward", action="store_true", help="skip the masked prefill backward")
+    ap.add_argument("--only", choices=["decode", "prefill", "chunk", "backward"], default=None,
                     help="run only one leg (for profiling); the JSON line then carries that leg only")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run one device-to-device copy of BYTES first (reference for HBM counter scaling)")
@@ -381,6 +382,41 @@ def run_prefill(ps, torch, reps=10, full_causal=True):
     return out
 
 
+def run_backward(ps, torch, reps=5):
+    """Backward of the truncated-backprop forward (8 x 8192 queries, W=2048, Hq=28, Hkv=4): dq, dk, dv from
+    the forward's output and LSE.  Useful work: the 5 products of attention backward (S recomputed, dP, dV,
+    dQ, dK), 2*D flops each per visible pair and head."""
+    import synth
+    cfg = synth.C4_PREFILL
+    attn = ps.AttnSpec(cfg.hq, cfg.hkv, cfg.dim, ps.PS_BF16, cfg.rope_theta, 1 / math.sqrt(cfg.dim))
+    g = torch.Generator(device="cuda").manual_seed(12)
+    q = torch.randn((cfg.batch, cfg.queries, cfg.hq, cfg.dim), generator=g, device="cuda").bfloat16()
+    k = torch.randn((cfg.batch, cfg.nk, cfg.hkv, cfg.dim), generator=g, device="cuda").bfloat16()
+    v = torch.randn((cfg.batch, cfg.nk, cfg.hkv, cfg.dim), generator=g, device="cuda").bfloat16()
+    do = torch.randn_like(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.batch, cfg.hq, cfg.queries), dtype=torch.float32, device="cuda")
+    ps.ps_prefill_attn(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, o, lse=lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ps.ps_prefill_backward_workspace_size(attn, cfg.batch, cfg.queries, cfg.nk),
+                     dtype=torch.uint8, device="cuda")
+
+    def call(n_):
+        for _ in range(n_):
+            ps.ps_prefill_attn_backward(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, o, do, lse, dq, dk, dv,
+                                        workspace=ws)
+    call(1)
+    t = timed(torch, call, reps) / reps
+    pairs = cfg.prefix * cfg.queries + sum(min(t_ + 1, cfg.window) for t_ in range(cfg.queries))
+    flops = 10.0 * cfg.dim * pairs * cfg.batch * cfg.hq
+    res = {"workload": cfg.name + "-backward", "ms": t * 1e3, "tflops": flops / t / 1e12,
+           "useful_tflop": flops / 1e12, "mfma_frac": flops / t / 1e12 / BF16_PEAK_TFLOPS,
+           "executed_products": 7}
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_chunk(ps, torch, reps=5):
     """Chunk continuing live traces (C6): 64 rings at 32768 (L=100, W=4096), a 2048-token chunk each.
     One call = chunk prep (ring gather + rotations), attention, append of the chunk into the rings."""
@@ -501,6 +537,9 @@ def main():
     if args.only == "chunk":
         print(json.dumps({"chunk_prefill": run_chunk(ps, torch)}))
         return
+    if args.only == "backward":
+        print(json.dumps({"prefill_backward": run_backward(ps, torch)}))
+        return
     dec = run_decode(ps, torch, args)
     print(f"[bench] decode done: {dec['tok_s']:.0f} tok/s, kernel {dec['kernel_s'] * 1e6:.1f} us",
           file=sys.stderr, flush=True)
@@ -508,6 +547,10 @@ def main():
     if not args.no_prefill and args.only is None:
         prefill = run_prefill(ps, torch)
         print(f"[bench] prefill done: {prefill}", file=sys.stderr, flush=True)
+    backward = None
+    if not args.no_backward and args.only is None:
+        backward = run_backward(ps, torch)
+        print(f"[bench] prefill backward done: {backward['tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
     chunk = None
     if not args.no_chunk and args.only is None:
         chunk = run_chunk(ps, torch)
@@ -548,6 +591,7 @@ def main():
                      "bytes_per_launch": dec["kernel_bytes"]},
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "prefill_backward": backward,
         "chunk_prefill": chunk,
         "full_attention": full,
     }

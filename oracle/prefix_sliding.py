@@ -299,6 +299,48 @@ def prefill_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, d_ou
     return dq, dk, dv
 
 
+def prefill_attention_backward_sampled(q: np.ndarray, k: np.ndarray, v: np.ndarray, d_out: np.ndarray,
+                                       prefix_len: int, window: int, kv_start: int, scale: float, theta: float,
+                                       kv_head: int, q_rows, k_rows, block: int = 512):
+    """Selected rows of ``prefill_attention_backward`` at sizes where the full
+    evaluation does not fit: dq rows ``q_rows`` of the query heads of KV head
+    ``kv_head``, and dk / dv rows ``k_rows`` of that KV head.  The same chain
+    rule, evaluated for those rows only; the per-query softmax statistics the
+    key rows need are formed ``block`` queries at a time (each query row still
+    over every key, masked).  Returns (dq [len(q_rows), G, D],
+    dk [len(k_rows), D], dv [len(k_rows), D])."""
+    q = np.asarray(q, dtype=np.float64)
+    t_q, hq, d = q.shape
+    nk, hkv, _ = k.shape
+    g = hq // hkv
+    heads = range(kv_head * g, (kv_head + 1) * g)
+    posk = key_positions(nk, prefix_len, kv_start)
+    posq = posk[nk - t_q:]
+    kr = rope(np.asarray(k[:, kv_head], dtype=np.float64), posk, theta)
+    vv = np.asarray(v[:, kv_head], dtype=np.float64)
+    do = np.asarray(d_out, dtype=np.float64)
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    dq = np.zeros((q_rows.size, g, d))
+    dkr = np.zeros((k_rows.size, d))
+    dv = np.zeros((k_rows.size, d))
+    for gi, h in enumerate(heads):
+        qr = rope(q[:, h], posq, theta)
+        for b0 in range(0, t_q, block):
+            rows = np.arange(b0, min(t_q, b0 + block))
+            mask = visible(posq[rows][:, None], posk[None, :], prefix_len, window)
+            p, _ = _masked_softmax_rows(scale * (qr[rows] @ kr.T), mask)
+            dp = do[rows, h] @ vv.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dv += p[:, k_rows].T @ do[rows, h]
+            dkr += scale * (ds[:, k_rows].T @ qr[rows])
+            sel = np.nonzero(np.isin(q_rows, rows))[0]
+            for i in sel:
+                dq[i, gi] = scale * (ds[q_rows[i] - b0] @ kr)
+        dq[:, gi] = rope(dq[:, gi], -posq[q_rows], theta)
+    return dq, rope(dkr, -posk[k_rows], theta), dv
+
+
 # --------------------------------------------------------------------------
 # prefill tile plan by element enumeration
 # --------------------------------------------------------------------------

@@ -181,3 +181,44 @@ def test_chunk_prefill_tool_output_64_sequences(ps):
                                                  1 / math.sqrt(cfg.dim), cfg.rope_theta, rows=rows)
         got = out[s].float().cpu().numpy()[rows]
         assert normwise_err(got, want) <= BF16_TOL, s
+
+
+def test_backward_truncated_backprop_chunk(ps):
+    # the 8 x 8192-query truncated-backprop shape, forward then backward on the GPU
+    # (bench launch configuration); sampled dq rows of one KV group's query heads
+    # and sampled dk / dv rows of that KV head of one batch row, against the oracle
+    cfg = synth.C4_PREFILL
+    attn = ps.AttnSpec(cfg.hq, cfg.hkv, cfg.dim, ps.PS_BF16, cfg.rope_theta, 1 / math.sqrt(cfg.dim))
+    B, T, nk = cfg.batch, cfg.queries, cfg.nk
+    print(f"backward full size: B={B} T={T} Nk={nk}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    q = torch.randn((B, T, cfg.hq, cfg.dim), generator=gen, device="cuda").bfloat16()
+    k = torch.randn((B, nk, cfg.hkv, cfg.dim), generator=gen, device="cuda").bfloat16()
+    v = torch.randn((B, nk, cfg.hkv, cfg.dim), generator=gen, device="cuda").bfloat16()
+    do = torch.randn((B, T, cfg.hq, cfg.dim), generator=gen, device="cuda").bfloat16()
+    sb, kvh = 3, 1
+    rs = lambda tensor, n, h: synth.round_to(synth.normal((n, h, cfg.dim), 0, cfg.cfg_id, tensor, sb), "bf16")
+    hq_, hk_, hv_, hd_ = rs(synth.T_Q, T, cfg.hq), rs(synth.T_K, nk, cfg.hkv), rs(synth.T_V, nk, cfg.hkv), \
+        rs(synth.T_MISC, T, cfg.hq)
+    q[sb], k[sb], v[sb], do[sb] = (to_dev(x, torch.bfloat16) for x in (hq_, hk_, hv_, hd_))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, cfg.hq, T), dtype=torch.float32, device="cuda")
+    ps.ps_prefill_attn(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, out, lse=lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ps.ps_prefill_attn_backward(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, out, do, lse, dq, dk, dv)
+    torch.cuda.synchronize()
+    q_rows = [0, 1, 2047, 2048, 5000, 8191]
+    k_rows = [0, 50, 99, 100, 101, 3000, 8291]
+    wq, wk, wv = oracle.prefill_attention_backward_sampled(hq_, hk_, hv_, hd_, cfg.prefix, cfg.window, cfg.kv_start,
+                                                           1 / math.sqrt(cfg.dim), cfg.rope_theta, kvh, q_rows,
+                                                           k_rows)
+    g = cfg.hq // cfg.hkv
+    got_q = dq[sb][q_rows][:, kvh * g:(kvh + 1) * g].float().cpu().numpy()
+    got_k = dk[sb][k_rows][:, kvh].float().cpu().numpy()
+    got_v = dv[sb][k_rows][:, kvh].float().cpu().numpy()
+    # the gradient tolerances of the small backward tests, per sampled set
+    for name, got, want in (("dq", got_q, wq), ("dk", got_k, wk), ("dv", got_v, wv)):
+        big = np.abs(want).max()
+        err = np.abs(got - want).max() / big
+        print(name, err, flush=True)
+        assert err <= 2e-2, (name, err)

@@ -414,6 +414,19 @@ def test_backward_invariants_and_loss_mask_structure():
     assert np.all(dq[:-r] == 0.0)
 
 
+def test_backward_sampled_rows_agree_with_full_evaluation():
+    q, k, v, do = _bwd_case(4, t_q=70, nk=90, hq=6, hkv=2, d=8)
+    L, W, ks = 7, 11, 33
+    dq, dk, dv = oracle.prefill_attention_backward(q, k, v, do, L, W, ks, 0.3, 10000.0)
+    qr, kr = [0, 5, 31, 69], [0, 6, 7, 40, 89]
+    for kv in range(2):
+        sq, sk, sv = oracle.prefill_attention_backward_sampled(q, k, v, do, L, W, ks, 0.3, 10000.0, kv, qr, kr,
+                                                               block=16)
+        np.testing.assert_allclose(sq, dq[qr][:, 3 * kv:3 * kv + 3], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sk, dk[kr, kv], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sv, dv[kr, kv], rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- tile plan
 def test_tile_plan_hand_worked_cases():
     for case in _golden("tile_plan_small.json")["cases"]:
