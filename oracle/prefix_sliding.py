@@ -40,6 +40,9 @@ the pages; no page is quoted):
 * Chunk continuing a trace (``chunk_prefill_attention``): queries at
   start..start+T-1 over the whole history; the ring supplies what the earlier
   trace left visible, so the result is again plain masked attention.
+* Reset PE (``decode_attention_reset_pe``; blog section "位置编码：Reset PE 还是
+  Continue PE？", the alternative the paper ablated): same visible set, visible
+  window tokens renumbered to follow the prefix, rotation at the new numbers.
 * Backward of the masked prefill (``prefill_attention_backward``): the chain
   rule of masked softmax attention, written out; gradients are taken with
   respect to the raw (un-rotated) inputs.
@@ -161,6 +164,43 @@ def decode_attention(q: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray, p: i
         s = scale * (kr[:, kv, :] @ qr[h])
         w, _ = _masked_softmax_rows(s[None, :], mask[None, :])
         out[h] = w[0] @ v[:, kv, :]
+    return out
+
+
+def reset_pe_positions(p: int, prefix_len: int, window: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Reset PE numbering for a query at ``p`` (blog section "位置编码：Reset PE 还是
+    Continue PE？"): the visible window tokens are renumbered so that they
+    directly follow the prefix, oldest first (0-indexed: the prefix keeps
+    0..L-1, the oldest visible window token becomes L).  Returns (visible
+    absolute positions, their new positions); the query's new position is the
+    last entry."""
+    vis = visible_positions(p, prefix_len, window)
+    pre = vis[vis < prefix_len]
+    win = vis[vis >= prefix_len]
+    return vis, np.concatenate([pre, prefix_len + np.arange(win.size, dtype=np.int64)])
+
+
+def decode_attention_reset_pe(q: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray, p: int,
+                              prefix_len: int, window: int, scale: float, theta: float) -> np.ndarray:
+    """Decode at ``p`` with Reset PE: the same visible set as Continue PE, but
+    every visible key and the query are rotated at their renumbered positions
+    (``reset_pe_positions``) instead of their absolute ones.  Raw inputs as in
+    ``decode_attention``; returns [Hq, D] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    hq, d = q.shape
+    hkv = k_hist.shape[1]
+    g = hq // hkv
+    vis, newpos = reset_pe_positions(p, prefix_len, window)
+    assert vis[-1] == p
+    qr = rope(q, newpos[-1], theta)
+    kr = rope(np.asarray(k_hist[vis], dtype=np.float64), newpos[:, None], theta)
+    v = np.asarray(v_hist[vis], dtype=np.float64)
+    out = np.empty((hq, d), dtype=np.float64)
+    for h in range(hq):
+        kv = h // g
+        s = scale * (kr[:, kv, :] @ qr[h])
+        e = np.exp(s - s.max())
+        out[h] = (e @ v[:, kv, :]) / e.sum()
     return out
 
 

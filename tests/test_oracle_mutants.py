@@ -26,6 +26,9 @@ PIN_CHECKS = [
     lambda: pins.test_backward_matches_central_differences(3, 4, 3, 10000.0),
     lambda: pins.test_backward_matches_torch_autograd(4, 5),
     lambda: pins.test_backward_invariants_and_loss_mask_structure(),
+    lambda: pins.test_reset_pe_numbering_hand_worked(),
+    lambda: pins.test_reset_pe_against_explicit_rotation(),
+    lambda: pins.test_reset_pe_reduces_to_continue_pe(3, 4, 20),
 ]
 
 
@@ -118,6 +121,16 @@ def _backward_with(bug):
     return f
 
 
+def _reset_pe_window_from_l_plus_one(p, L, W):
+    vis = ops.visible_positions(p, L, W)
+    pre, win = vis[vis < L], vis[vis >= L]
+    return vis, np.concatenate([pre, L + 1 + np.arange(win.size, dtype=np.int64)])
+
+
+def _reset_pe_not_renumbered(q, k_hist, v_hist, p, L, W, scale, theta):
+    return ORIG_DECODE(q, k_hist, v_hist, p, L, W, scale, theta)
+
+
 MUTANTS = {
     "window-off-by-one": ("visible", _window_off_by_one),
     "prefix-not-causal": ("visible", _prefix_not_causal),
@@ -129,6 +142,8 @@ MUTANTS = {
     "chunk-query-one-early": ("chunk_prefill_attention", _chunk_query_one_early),
     "backward-no-rowsum": ("prefill_attention_backward", _backward_with("no-rowsum")),
     "backward-no-unrotate": ("prefill_attention_backward", _backward_with("no-unrotate")),
+    "reset-pe-window-from-L+1": ("reset_pe_positions", _reset_pe_window_from_l_plus_one),
+    "reset-pe-not-renumbered": ("decode_attention_reset_pe", _reset_pe_not_renumbered),
 }
 
 

@@ -427,6 +427,58 @@ def test_backward_sampled_rows_agree_with_full_evaluation():
         np.testing.assert_allclose(sv, dv[kr, kv], rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- Reset PE
+def test_reset_pe_numbering_hand_worked():
+    # L = 3, W = 4, p = 20: visible {0, 1, 2, 17, 18, 19, 20} -> 0..6, query at 6
+    vis, new = oracle.reset_pe_positions(20, 3, 4)
+    assert vis.tolist() == [0, 1, 2, 17, 18, 19, 20] and new.tolist() == [0, 1, 2, 3, 4, 5, 6]
+    # warm-up: nothing is renumbered
+    vis, new = oracle.reset_pe_positions(5, 3, 4)
+    assert vis.tolist() == new.tolist() == [0, 1, 2, 3, 4, 5]
+    vis, new = oracle.reset_pe_positions(2, 10, 4)      # query inside the prefix
+    assert vis.tolist() == new.tolist() == [0, 1, 2]
+
+
+def test_reset_pe_against_explicit_rotation():
+    rs = np.random.default_rng(12)
+    k = rs.standard_normal((21, 2, 8))
+    v = rs.standard_normal((21, 2, 8))
+    q = rs.standard_normal((4, 8))
+    got = oracle.decode_attention_reset_pe(q, k, v, 20, 3, 4, 0.5, 100.0)
+    keys = [0, 1, 2, 17, 18, 19, 20]
+    # rotate each pair (i, i + D/2) by position * 100^(-2i/D) with complex numbers
+    def rot(x, pos):
+        f = 100.0 ** (-2.0 * np.arange(4) / 8)
+        z = (x[..., :4] + 1j * x[..., 4:]) * np.exp(1j * pos * f)
+        return np.concatenate([z.real, z.imag], axis=-1)
+    want = np.empty((4, 8))
+    for h in range(4):
+        qh = rot(q[h], 6)
+        s = np.array([0.5 * rot(k[j, h // 2], n) @ qh for n, j in enumerate(keys)])
+        w = np.exp(s - s.max())
+        want[h] = (w / w.sum()) @ v[keys, h // 2]
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("L,W,p", [(0, 8, 40), (0, 1, 9), (5, 6, 9), (5, 6, 10), (30, 6, 20), (4, 100, 50),
+                                   (3, 4, 20), (10, 8, 100)])
+def test_reset_pe_reduces_to_continue_pe(L, W, p):
+    # no prefix (only relative offsets inside the window matter), warm-up, or no
+    # rotation: Reset PE and Continue PE give the same attention
+    rs = np.random.default_rng(p)
+    k = rs.standard_normal((p + 1, 2, 16))
+    v = rs.standard_normal((p + 1, 2, 16))
+    q = rs.standard_normal((4, 16))
+    cont = oracle.decode_attention(q, k, v, p, L, W, 0.3, 10000.0)
+    reset = oracle.decode_attention_reset_pe(q, k, v, p, L, W, 0.3, 10000.0)
+    if L == 0 or p - W + 1 <= L:
+        np.testing.assert_allclose(reset, cont, rtol=0, atol=1e-12)
+    else:
+        assert np.abs(reset - cont).max() > 1e-6      # the prefix-window distance really changed
+    np.testing.assert_allclose(oracle.decode_attention_reset_pe(q, k, v, p, L, W, 0.3, 0.0),
+                               oracle.decode_attention(q, k, v, p, L, W, 0.3, 0.0), rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- tile plan
 def test_tile_plan_hand_worked_cases():
     for case in _golden("tile_plan_small.json")["cases"]:
