@@ -295,8 +295,9 @@ def run_sweep(ps, torch, num_seqs=256, layers=28, reps=10):
 def run_decode_extra(ps, torch, layers=28, reps=30):
     """Per-layer decode-kernel time of the other decode workloads (one layer's
     cache each; tok/s assumes `layers` layers of decode attention per token):
-    64 sequences at 32768 (W=4096), 256 at 131072 with W=8192, and the ragged
-    paged batch of 1024 sequences (positions 1024..262144, prefixes 50..2000)."""
+    64 sequences at 32768 (W=4096), 256 at 131072 with W=8192, the headline
+    workload with Continue PE and with Reset PE scoring, and the ragged paged
+    batch of 1024 sequences (positions 1024..262144, prefixes 50..2000)."""
     import numpy as np
     import synth
     out = {}
@@ -313,6 +314,21 @@ def run_decode_extra(ps, torch, layers=28, reps=30):
         b.release()
         del b
         torch.cuda.empty_cache()
+    # Reset PE at the headline workload: same cache, prefix slots scored with the renumbered query
+    import dataclasses
+    b = DecodeBench(ps, torch, 256, 1, 4096, 100, 131072, 0, pool=4)
+    pos = torch.full((256,), 131072, dtype=torch.int64, device="cuda")
+    for mode, key in ((ps.PS_PE_CONTINUE, "decode-131072-w4096-continue-pe"),
+                      (ps.PS_PE_RESET, "decode-131072-w4096-reset-pe")):
+        b.attn = dataclasses.replace(b.attn, pe_mode=mode)
+        b.decode_only(3, pos)
+        t = timed(torch, lambda k: b.decode_only(k, pos), reps) / reps
+        out[key] = {"us_per_layer": t * 1e6, "hbm_gbs": b.kernel_bytes(131072) / t / 1e9,
+                    "hbm_frac": b.kernel_bytes(131072) / t / 1e9 / HBM_PEAK_GBS,
+                    "tok_s_attention_only": 256 / (t * layers)}
+    b.release()
+    del b
+    torch.cuda.empty_cache()
     # ragged paged batch
     c = synth.C5_DECODE
     n = c.num_seqs

@@ -16,13 +16,14 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import PS_BF16, PS_F32, PSError
+from ._lib import PS_BF16, PS_F32, PS_PE_CONTINUE, PS_PE_RESET, PSError
 
 __all__ = ["AttnSpec", "CacheSpec", "PSError", "ps_kv_append", "ps_decode_attn", "ps_prefill_attn",
            "ps_chunk_prefill_attn", "ps_chunk_prefill_workspace_size", "ps_prefill_attn_backward",
            "ps_prefill_backward_workspace_size",
            "ps_prefill_plan", "ps_decode_workspace_size", "ps_decode_num_splits", "ps_prefill_workspace_size",
-           "ps_prefill_tile_shape", "ps_abi_version", "cache_shapes", "PS_BF16", "PS_F32"]
+           "ps_prefill_tile_shape", "ps_abi_version", "cache_shapes", "PS_BF16", "PS_F32", "PS_PE_CONTINUE",
+           "PS_PE_RESET"]
 
 _TORCH_DTYPE = {PS_BF16: torch.bfloat16, PS_F32: torch.float32}
 
@@ -35,11 +36,12 @@ class AttnSpec:
     dtype: int = PS_BF16
     rope_theta: float = 10000.0
     softmax_scale: Optional[float] = None  # default 1/sqrt(head_dim)
+    pe_mode: int = PS_PE_CONTINUE          # PS_PE_RESET: decode only
 
     def c(self) -> _lib.AttnDesc:
         scale = self.softmax_scale if self.softmax_scale is not None else 1.0 / math.sqrt(self.head_dim)
         return _lib.AttnDesc(self.num_q_heads, self.num_kv_heads, self.head_dim, self.dtype, float(self.rope_theta),
-                             float(scale))
+                             float(scale), int(self.pe_mode))
 
     @property
     def torch_dtype(self) -> torch.dtype:

@@ -12,11 +12,13 @@ LIB_PATH = os.path.join(HERE, "libprefix_sliding.so")
 
 PS_OK, PS_INVALID_ARGUMENT, PS_UNSUPPORTED, PS_WORKSPACE_TOO_SMALL, PS_HIP_ERROR = range(5)
 PS_BF16, PS_F32 = 0, 1
+PS_PE_CONTINUE, PS_PE_RESET = 0, 1
 
 
 class AttnDesc(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+                ("pe_mode", ctypes.c_int32)]
 
 
 class CacheDesc(ctypes.Structure):

@@ -50,6 +50,14 @@ ps_status check_attn(const ps_attn_desc* a) {
   if (!(a->rope_theta >= 0.0) || !isfinite(a->rope_theta))
     return fail(PS_INVALID_ARGUMENT, "rope_theta must be >= 0 and finite");
   if (a->rope_theta > 0.0 && a->rope_theta <= 1.0) return fail(PS_INVALID_ARGUMENT, "rope_theta must exceed 1");
+  if (a->pe_mode != PS_PE_CONTINUE && a->pe_mode != PS_PE_RESET)
+    return fail(PS_INVALID_ARGUMENT, "pe_mode %d (0 Continue PE, 1 Reset PE)", a->pe_mode);
+  return PS_OK;
+}
+
+// Reset PE is a decode-only scoring mode.
+ps_status continue_pe_only(const ps_attn_desc* a, const char* entry) {
+  if (a->pe_mode != PS_PE_CONTINUE) return fail(PS_UNSUPPORTED, "%s supports Continue PE only (pe_mode 0)", entry);
   return PS_OK;
 }
 
@@ -297,6 +305,7 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, c
   a.part_ml = splits > 1 ? ws + rows * attn->head_dim : nullptr;
   a.scale_log2 = attn->softmax_scale * 1.4426950408889634f;
   a.rope = make_rope(attn);
+  a.reset_pe = attn->pe_mode == PS_PE_RESET ? 1 : 0;
   return from_hip(ps::launch_decode(a, stream), "ps_decode_attn launch");
 }
 
@@ -319,6 +328,7 @@ ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t pref
                           hipStream_t stream) {
   ps_status st = check_attn(attn);
   if (st != PS_OK) return st;
+  if ((st = continue_pe_only(attn, "ps_prefill_attn")) != PS_OK) return st;
   if ((st = check_prefill_geom(window, prefix_len, kv_start, batch, num_queries, num_keys)) != PS_OK) return st;
   if (batch == 0 || num_queries == 0) return ok();
   if (!q || !k || !v || !out) return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
@@ -378,6 +388,7 @@ ps_status ps_prefill_attn_backward(const ps_attn_desc* attn, int32_t window, int
                                    void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   ps_status st = check_attn(attn);
   if (st != PS_OK) return st;
+  if ((st = continue_pe_only(attn, "ps_prefill_attn_backward")) != PS_OK) return st;
   if ((st = check_prefill_geom(window, prefix_len, kv_start, batch, num_queries, num_keys)) != PS_OK) return st;
   if (batch == 0 || num_queries == 0) return ok();
   if (!q || !k || !v || !out || !d_out || !lse || !dq || !dk || !dv)
@@ -443,6 +454,7 @@ ps_status ps_chunk_prefill_attn(const ps_attn_desc* attn, const ps_cache_desc* c
                                 size_t workspace_bytes, hipStream_t stream) {
   ps_status st = check_attn(attn);
   if (st != PS_OK) return st;
+  if ((st = continue_pe_only(attn, "ps_chunk_prefill_attn")) != PS_OK) return st;
   if ((st = check_cache(cache, block_table)) != PS_OK) return st;
   if (num_seqs < 0 || chunk_len < 0) return fail(PS_INVALID_ARGUMENT, "negative num_seqs or chunk_len");
   if (num_seqs == 0 || chunk_len == 0) return ok();

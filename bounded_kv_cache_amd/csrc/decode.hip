@@ -57,7 +57,7 @@ __device__ inline u32x4 stream_load(const uint16_t* p) {
 // ---------------------------------------------------------------------------
 // bf16 MFMA partial kernel
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NW, bool kReset>
 __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NC = D / 32;   // QK k-steps (32 dims each)
   constexpr int NDT = D / 16;  // PV d-tiles (16 dims each)
@@ -82,6 +82,10 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
   const int kb = split * a.split_keys;
   const int ke = kb + a.split_keys < nvis ? kb + a.split_keys : nvis;
   bf16x8 qop[NC];   // query operand, filled after the first chunk's loads are issued
+  // Reset PE: prefix slots [0, L) are scored with the query rotated at its
+  // renumbered position min(p, L+W-1); window keys keep their offsets to the
+  // query (the whole window shifts by one amount), so they use qop
+  bf16x8 qop_b[kReset ? NC : 1];
 
   // ---- per-lane load offsets inside a 32-key chunk (elements) ----
   // K tile t, row r -> key 8*(r/4) + 4t + r%4; k-step c covers dims 32c + 8g .. +8
@@ -156,16 +160,35 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
     for (int dt = 0; dt < NDT; ++dt) vr[dt] = stream_load(vp + voff + dt * 16 * 8);
   };
 
-  auto compute_chunk = [&](int ci, u32x4 (&kr)[2][NC], u32x4 (&vr)[NDT]) {
-    f32x4 st0 = f32x4{0.f, 0.f, 0.f, 0.f}, st1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto qk = [&](const bf16x8* qo, u32x4 (&kr)[2][NC], f32x4& st0, f32x4& st1) {
+    st0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    st1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
-      st0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[0][cc]), qop[cc], st0, 0, 0, 0);
-      st1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[1][cc]), qop[cc], st1, 0, 0, 0);
+      st0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[0][cc]), qo[cc], st0, 0, 0, 0);
+      st1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[1][cc]), qo[cc], st1, 0, 0, 0);
+    }
+  };
+
+  auto compute_chunk = [&](int ci, u32x4 (&kr)[2][NC], u32x4 (&vr)[NDT]) {
+    f32x4 st0, st1;
+    const int key0 = (ci << 5) + 8 * g;
+    if (kReset && (ci << 5) < L) {
+      qk(qop_b, kr, st0, st1);
+      if (((ci + 1) << 5) > L) {   // the chunk holding the end of the prefix: window keys from qop
+        f32x4 w0, w1;
+        qk(qop, kr, w0, w1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (key0 + i >= L) st0[i] = w0[i];
+          if (key0 + 4 + i >= L) st1[i] = w1[i];
+        }
+      }
+    } else {
+      qk(qop, kr, st0, st1);
     }
     // lane holds head r, keys 8g + i (i<4 from tile 0, i>=4 from tile 1)
     float sv[8] = {st0[0], st0[1], st0[2], st0[3], st1[0], st1[1], st1[2], st1[3]};
-    const int key0 = (ci << 5) + 8 * g;
     const bool tail = ((ci + 1) << 5) > ke || (ci << 5) < kb;
     if (tail) {
 #pragma unroll
@@ -227,6 +250,21 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
       for (int e = 0; e < 4; ++e) {
         qv[c][2 * e] = (r < G) ? lo_bf16(ww[e]) : 0.f;
         qv[c][2 * e + 1] = (r < G) ? hi_bf16(ww[e]) : 0.f;
+      }
+    }
+    if (kReset) {
+      const int64_t lw1 = (int64_t)L + geo.window - 1;
+      const int64_t pos_b = pos < lw1 ? pos : lw1;
+#pragma unroll
+      for (int c = 0; c < NC / 2; ++c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float cs = 1.f, sn = 0.f;
+          if (a.rope.enabled) rope_cos_sin(pos_b, a.rope.inv_freq[32 * c + 8 * g + i], cs, sn);
+          const float x1 = qv[c][i], x2 = qv[c + NC / 2][i];
+          qop_b[c][i] = (bf16)((x1 * cs - x2 * sn) * a.scale_log2);
+          qop_b[c + NC / 2][i] = (bf16)((x2 * cs + x1 * sn) * a.scale_log2);
+        }
       }
     }
     if (a.rope.enabled) {
@@ -319,6 +357,7 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
   constexpr int TK = 32;  // keys per tile
   __shared__ float qs[kMaxGroup][D];
+  __shared__ float qs_b[kMaxGroup][D];   // Reset PE: the query for prefix slots
   __shared__ float ks[TK][D + 1];
   __shared__ float vs[TK][D + 1];
   __shared__ float ps_[kMaxGroup][TK];
@@ -346,16 +385,23 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
   for (int idx = tid; idx < G * (D / 2); idx += 256) {
     const int n = idx / (D / 2), i = idx % (D / 2);
     const float* qr = q + ((int64_t)s * a.hq + h * G + n) * D;
-    float x1 = qr[i], x2 = qr[i + D / 2];
+    const float r1 = qr[i], r2 = qr[i + D / 2];
+    float x1 = r1, x2 = r2;
     if (a.rope.enabled) {
       float c, sn;
       rope_cos_sin(pos, a.rope.inv_freq[i], c, sn);
-      const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
-      x1 = y1;
-      x2 = y2;
+      x1 = r1 * c - r2 * sn;
+      x2 = r2 * c + r1 * sn;
     }
     qs[n][i] = x1 * a.scale_log2;
     qs[n][i + D / 2] = x2 * a.scale_log2;
+    if (a.reset_pe) {
+      const int64_t lw1 = (int64_t)L + geo.window - 1;
+      float c = 1.f, sn = 0.f;
+      if (a.rope.enabled) rope_cos_sin(pos < lw1 ? pos : lw1, a.rope.inv_freq[i], c, sn);
+      qs_b[n][i] = (r1 * c - r2 * sn) * a.scale_log2;
+      qs_b[n][i + D / 2] = (r2 * c + r1 * sn) * a.scale_log2;
+    }
   }
   if (tid < kMaxGroup) {
     m_s[tid] = -INFINITY;
@@ -387,8 +433,9 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     __syncthreads();
     for (int idx = tid; idx < G * TK; idx += 256) {
       const int n = idx / TK, j = idx % TK;
+      const float* qv = (a.reset_pe && t0 + j < L) ? qs_b[n] : qs[n];
       float sc = 0.f;
-      for (int d = 0; d < D; ++d) sc += qs[n][d] * ks[j][d];
+      for (int d = 0; d < D; ++d) sc += qv[d] * ks[j][d];
       ps_[n][j] = (t0 + j < ke) ? sc : -INFINITY;
     }
     __syncthreads();
@@ -474,7 +521,10 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((uint32_t)((int64_t)a.num_seqs * a.geom.hkv * a.num_splits));
   if (a.dtype == PS_BF16) {
     constexpr int NW = PS_DECODE_WAVES;
-    hipLaunchKernelGGL((decode_bf16_kernel<D, NW>), grid, dim3(NW * 64), 0, stream, a);
+    if (a.reset_pe)
+      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, true>), grid, dim3(NW * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false>), grid, dim3(NW * 64), 0, stream, a);
   } else {
     hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(256), 0, stream, a);
   }

@@ -44,6 +44,7 @@ struct DecodeArgs {
   float* part_ml;         // [num_seqs][hq][num_splits][2]  (running max in log2 units, sum)
   float scale_log2;       // softmax_scale * log2(e)
   RopeFreq rope;
+  int32_t reset_pe;       // 1: Reset PE scoring (prefix slots use the renumbered query)
 };
 
 struct PrefillArgs {

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 3
+#define PS_ABI_VERSION 4
 
 typedef enum {
   PS_OK = 0,
@@ -83,6 +83,19 @@ typedef enum {
 } ps_status;
 
 typedef enum { PS_BF16 = 0, PS_F32 = 1 } ps_dtype;
+
+/* Position encoding of the visible window (blog "Prefix Sliding 完全拆解",
+ * section "位置编码：Reset PE 还是 Continue PE？").  Continue PE: every token
+ * keeps its absolute position (the method's choice).  Reset PE (the ablated
+ * alternative): the visible window tokens are renumbered to follow the prefix
+ * directly, oldest first, and the query takes the last number,
+ * min(p, prefix_len + W - 1).  Only ps_decode_attn accepts PS_PE_RESET: the
+ * cache still holds keys rotated at their absolute positions, because
+ * renumbering shifts every window key and the query by the same amount, which
+ * leaves their rotary offsets unchanged -- so window keys are scored as under
+ * Continue PE and only the prefix keys are scored against the query rotated at
+ * its renumbered position (no key is re-rotated). */
+typedef enum { PS_PE_CONTINUE = 0, PS_PE_RESET = 1 } ps_pe_mode;
 
 /* Attention geometry.
  * num_q_heads % num_kv_heads == 0; query head h uses KV head
@@ -99,6 +112,7 @@ typedef struct {
   int32_t dtype;            /* ps_dtype: element type of q, k, v, caches, out */
   double rope_theta;
   float softmax_scale;
+  int32_t pe_mode;          /* ps_pe_mode; 0 = Continue PE */
 } ps_attn_desc;
 
 /* Cache geometry.  window = W >= 1.  page_size 0 (contiguous) or 64 (paged).

@@ -37,14 +37,15 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ps_abi_version() == 3
+    assert lib.ps_abi_version() == 4
     assert lib.ps_status_string(0) == b"ok"
     assert lib.ps_status_string(3) == b"workspace too small"
 
 
-def _descs(hq=16, hkv=2, d=128, dtype=0, theta=10000.0, scale=0.0884, window=4096, page=0, cap=4224, mp=0, npages=0):
+def _descs(hq=16, hkv=2, d=128, dtype=0, theta=10000.0, scale=0.0884, window=4096, page=0, cap=4224, mp=0, npages=0,
+           pe=0):
     from bounded_kv_cache_amd import _lib
-    return (_lib.AttnDesc(hq, hkv, d, dtype, theta, scale), _lib.CacheDesc(window, page, cap, mp, npages))
+    return (_lib.AttnDesc(hq, hkv, d, dtype, theta, scale, pe), _lib.CacheDesc(window, page, cap, mp, npages))
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
@@ -54,7 +55,7 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails val
     (dict(hq=15), 1), (dict(hkv=0), 1), (dict(hq=34, hkv=2), 2), (dict(d=96), 2), (dict(dtype=7), 2),
     (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(theta=-1.0), 1), (dict(theta=0.5), 1),
     (dict(window=0), 1), (dict(page=32), 2), (dict(cap=100), 1), (dict(page=64, cap=4224, mp=10, npages=5), 1),
-    (dict(page=64, cap=4224, mp=66, npages=0), 1),
+    (dict(page=64, cap=4224, mp=66, npages=0), 1), (dict(pe=2), 1), (dict(pe=-1), 1),
 ])
 def test_decode_validation(lib, mut, status):
     a, c = _descs(**mut)
@@ -237,3 +238,18 @@ def test_backward_validation_and_workspace(lib):
     assert call(nq=NK + 1) == 1             # more queries than keys
     assert call(nq=NK, ks=600) == 1         # queries reach into the prefix with a gap
     assert call(nq=0) == 0
+
+
+def test_reset_pe_is_decode_only(lib):
+    a, c = _descs(pe=1)
+    # prefill, backward and chunk prefill reject Reset PE before looking at anything else
+    assert lib.ps_prefill_attn(ctypes.byref(a), 64, 0, 0, FAKE, FAKE, FAKE, 1, 64, 64, FAKE, None, FAKE, 1 << 30,
+                               None) == 2
+    assert lib.ps_prefill_attn_backward(ctypes.byref(a), 64, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 64,
+                                        FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2
+    assert lib.ps_chunk_prefill_attn(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, 16, FAKE, FAKE,
+                                     FAKE, 1, FAKE, None, None, FAKE, 1 << 30, None) == 2
+    assert b"Continue PE" in lib.ps_last_error()
+    # decode accepts it (fails later only on the NULL cache pointer)
+    assert lib.ps_decode_attn(ctypes.byref(a), ctypes.byref(c), None, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 1,
+                              None, 0, None) == 1
