@@ -43,6 +43,10 @@ the pages; no page is quoted):
 * Reset PE (``decode_attention_reset_pe``; blog section "位置编码：Reset PE 还是
   Continue PE？", the alternative the paper ablated): same visible set, visible
   window tokens renumbered to follow the prefix, rotation at the new numbers.
+* Prefix + heavy hitters + window (``h2o_admit``, ``h2o_decode_trace``): the
+  combination the blog proposes when comparing with H2O; the admission rule
+  and the per-KV-head score (attention received, summed over the group's query
+  heads, accumulated while cached) are readings, stated in the docstrings.
 * Backward of the masked prefill (``prefill_attention_backward``): the chain
   rule of masked softmax attention, written out; gradients are taken with
   respect to the raw (un-rotated) inputs.
@@ -202,6 +206,83 @@ def decode_attention_reset_pe(q: np.ndarray, k_hist: np.ndarray, v_hist: np.ndar
         e = np.exp(s - s.max())
         out[h] = (e @ v[:, kv, :]) / e.sum()
     return out
+
+
+def h2o_admit(heavy_pos: Sequence[int], heavy_score: Sequence[float], cand_pos: int, cand_score: float,
+              capacity: int):
+    """Heavy-hitter admission for a token leaving the window (the prefix +
+    heavy-hitter + window combination the blog proposes in its comparison with
+    H2O: keep, besides prefix and window, the middle tokens that have drawn the
+    most attention so far).  Reading: the heavy set fills its ``capacity``
+    slots in order; once full, the candidate replaces the member with the
+    smallest accumulated score (ties: the oldest position) if its own score is
+    strictly larger, else the candidate is dropped.  Returns (slot index the
+    candidate is written to, or -1; evicted position, or -1)."""
+    n = sum(1 for x in heavy_pos if x >= 0)
+    if n < capacity:
+        return n, -1
+    m = min(range(capacity), key=lambda i: (heavy_score[i], heavy_pos[i]))
+    if cand_score > heavy_score[m]:
+        return m, int(heavy_pos[m])
+    return -1, int(cand_pos)
+
+
+def h2o_decode_trace(q: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray, prefix_len: int, window: int,
+                     heavy: int, scale: float, theta: float):
+    """Decode positions 0..N-1 of one sequence with prefix + heavy hitters +
+    window, per KV head (the cache is per KV head).  Step p: the token p - W
+    leaves the window and competes for the heavy set (``h2o_admit``) with its
+    accumulated score; the query at p attends, under plain masked softmax, to
+    the prefix, the heavy set and the window (p - W, p]; then every visible
+    non-prefix token adds the attention it received, summed over the query
+    heads of its KV head.  q: raw [N, Hq, D]; k_hist, v_hist: raw [N, Hkv, D].
+    Returns (out [N, Hq, D], heavy positions [Hkv, heavy] (-1 empty),
+    scores: list per KV head of dict position -> accumulated score)."""
+    q = np.asarray(q, dtype=np.float64)
+    n_steps, hq, d = q.shape
+    hkv = k_hist.shape[1]
+    g = hq // hkv
+    pos_all = np.arange(n_steps, dtype=np.int64)
+    kr = rope(np.asarray(k_hist, dtype=np.float64), pos_all[:, None], theta)
+    v = np.asarray(v_hist, dtype=np.float64)
+    out = np.empty((n_steps, hq, d), dtype=np.float64)
+    heavy_pos = np.full((hkv, heavy), -1, dtype=np.int64)
+    heavy_sc = np.zeros((hkv, heavy), dtype=np.float64)
+    scores = [dict() for _ in range(hkv)]
+    for p in range(n_steps):
+        e = p - window
+        for kv in range(hkv):
+            if e >= prefix_len and heavy > 0:
+                slot, dropped = h2o_admit(heavy_pos[kv], heavy_sc[kv], e, scores[kv][e], heavy)
+                if slot >= 0:
+                    heavy_pos[kv, slot] = e
+                    heavy_sc[kv, slot] = scores[kv][e]
+                if dropped >= 0:
+                    scores[kv].pop(dropped)
+            elif e >= prefix_len:
+                scores[kv].pop(e)
+            if p >= prefix_len:
+                scores[kv][p] = 0.0
+        qr = rope(q[p], p, theta)
+        for kv in range(hkv):
+            hp = heavy_pos[kv][heavy_pos[kv] >= 0]
+            win = np.arange(max(prefix_len, p - window + 1), p + 1, dtype=np.int64)
+            vis = np.concatenate([np.arange(min(prefix_len, p + 1), dtype=np.int64), hp, win])
+            assert np.unique(vis).size == vis.size
+            mass = np.zeros(vis.size)
+            for h in range(kv * g, (kv + 1) * g):
+                sc = scale * (kr[vis, kv, :] @ qr[h])
+                w = np.exp(sc - sc.max())
+                w /= w.sum()
+                out[p, h] = w @ v[vis, kv, :]
+                mass += w
+            for j, m in zip(vis, mass):
+                if j >= prefix_len:
+                    scores[kv][int(j)] += m
+            for i in range(heavy):
+                if heavy_pos[kv, i] >= 0:
+                    heavy_sc[kv, i] = scores[kv][int(heavy_pos[kv, i])]
+    return out, heavy_pos, scores
 
 
 def decode_from_slots(q: np.ndarray, p: int, k_rot: np.ndarray, v: np.ndarray, scale: float,

@@ -29,6 +29,10 @@ PIN_CHECKS = [
     lambda: pins.test_reset_pe_numbering_hand_worked(),
     lambda: pins.test_reset_pe_against_explicit_rotation(),
     lambda: pins.test_reset_pe_reduces_to_continue_pe(3, 4, 20),
+    lambda: pins.test_h2o_admission_hand_worked(),
+    lambda: pins.test_h2o_zero_query_trace_hand_worked(),
+    lambda: pins.test_h2o_reduces_to_prefix_sliding_and_full_attention(3, 5),
+    lambda: pins.test_h2o_trace_invariants(),
 ]
 
 
@@ -131,6 +135,26 @@ def _reset_pe_not_renumbered(q, k_hist, v_hist, p, L, W, scale, theta):
     return ORIG_DECODE(q, k_hist, v_hist, p, L, W, scale, theta)
 
 
+def _h2o_admit_on_tie(heavy_pos, heavy_score, cand_pos, cand_score, capacity):
+    n = sum(1 for x in heavy_pos if x >= 0)
+    if n < capacity:
+        return n, -1
+    m = min(range(capacity), key=lambda i: (heavy_score[i], heavy_pos[i]))
+    if cand_score >= heavy_score[m]:
+        return m, int(heavy_pos[m])
+    return -1, int(cand_pos)
+
+
+def _h2o_evict_newest(heavy_pos, heavy_score, cand_pos, cand_score, capacity):
+    n = sum(1 for x in heavy_pos if x >= 0)
+    if n < capacity:
+        return n, -1
+    m = min(range(capacity), key=lambda i: (heavy_score[i], -heavy_pos[i]))
+    if cand_score > heavy_score[m]:
+        return m, int(heavy_pos[m])
+    return -1, int(cand_pos)
+
+
 MUTANTS = {
     "window-off-by-one": ("visible", _window_off_by_one),
     "prefix-not-causal": ("visible", _prefix_not_causal),
@@ -144,6 +168,8 @@ MUTANTS = {
     "backward-no-unrotate": ("prefill_attention_backward", _backward_with("no-unrotate")),
     "reset-pe-window-from-L+1": ("reset_pe_positions", _reset_pe_window_from_l_plus_one),
     "reset-pe-not-renumbered": ("decode_attention_reset_pe", _reset_pe_not_renumbered),
+    "h2o-admit-on-tie": ("h2o_admit", _h2o_admit_on_tie),
+    "h2o-evict-newest": ("h2o_admit", _h2o_evict_newest),
 }
 
 

@@ -479,6 +479,71 @@ def test_reset_pe_reduces_to_continue_pe(L, W, p):
                                oracle.decode_attention(q, k, v, p, L, W, 0.3, 0.0), rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- prefix + heavy hitters + window
+def test_h2o_admission_hand_worked():
+    assert oracle.h2o_admit([-1, -1], [0.0, 0.0], 7, 0.1, 2) == (0, -1)          # free slot, filled in order
+    assert oracle.h2o_admit([5, -1], [3.0, 0.0], 7, 0.1, 2) == (1, -1)
+    assert oracle.h2o_admit([5, 6], [3.0, 1.0], 9, 2.0, 2) == (1, 6)             # beats the weakest member
+    assert oracle.h2o_admit([5, 6], [3.0, 1.0], 9, 1.0, 2) == (-1, 9)            # a tie keeps the member
+    assert oracle.h2o_admit([8, 6], [1.0, 1.0], 9, 1.5, 2) == (1, 6)             # equal members: oldest goes
+    assert oracle.h2o_admit([5], [1.0], 9, 0.5, 1) == (-1, 9)
+
+
+def test_h2o_zero_query_trace_hand_worked():
+    # q = 0 makes every visible token draw the same mass; with W = 1 and one heavy
+    # slot the first token enters the heavy set at step 1 and never leaves (each
+    # later candidate has drawn half a step's mass against its growing total), so
+    # the query at p averages v over {0, p}; features (1, j, j^2) expose the set
+    n, g = 12, 2
+    j = np.arange(n, dtype=np.float64)
+    v = np.zeros((n, 1, 4))
+    v[:, 0, 0], v[:, 0, 1], v[:, 0, 2] = 1.0, j, j * j
+    k = np.random.default_rng(0).standard_normal((n, 1, 4))
+    out, heavy, scores = oracle.h2o_decode_trace(np.zeros((n, g, 4)), k, v, 0, 1, 1, 1.0, 10000.0)
+    assert heavy.tolist() == [[0]]
+    np.testing.assert_allclose(out[0, :, :3], [[1.0, 0.0, 0.0]] * g, atol=1e-15)
+    for p in range(1, n):
+        np.testing.assert_allclose(out[p, 0, :3], [1.0, p / 2, p * p / 2], rtol=1e-13)
+    # token 0: G at step 0, then G/2 at each of steps 1..n-1
+    assert abs(scores[0][0] - (g + g * (n - 1) / 2)) < 1e-12
+    assert set(scores[0]) == {0, n - 1}
+
+
+@pytest.mark.parametrize("L,W", [(3, 5), (0, 4), (6, 1)])
+def test_h2o_reduces_to_prefix_sliding_and_full_attention(L, W):
+    rs = np.random.default_rng(L + W)
+    n = 40
+    q = rs.standard_normal((n, 4, 8))
+    k = rs.standard_normal((n, 2, 8))
+    v = rs.standard_normal((n, 2, 8))
+    none, _, _ = oracle.h2o_decode_trace(q, k, v, L, W, 0, 0.4, 10000.0)          # no heavy slots: Prefix Sliding
+    allk, heavy, _ = oracle.h2o_decode_trace(q, k, v, L, W, n, 0.4, 10000.0)      # room for every token: full
+    for p in range(n):
+        np.testing.assert_allclose(none[p], oracle.decode_attention(q[p], k, v, p, L, W, 0.4, 10000.0),
+                                   rtol=0, atol=1e-12)
+        np.testing.assert_allclose(allk[p], oracle.decode_attention(q[p], k, v, p, 0, 1 << 30, 0.4, 10000.0),
+                                   rtol=0, atol=1e-12)
+    assert sorted(heavy[0][heavy[0] >= 0].tolist()) == list(range(L, n - W))
+
+
+def test_h2o_trace_invariants():
+    # every step's attention sums to one per head, so the scores of the tokens
+    # still cached never exceed G * steps; heavy members always outscore the
+    # candidates they beat, and the heavy set is disjoint from prefix and window
+    rs = np.random.default_rng(3)
+    n, L, W, H = 80, 4, 6, 5
+    q = rs.standard_normal((n, 6, 8)) * 2
+    k = rs.standard_normal((n, 2, 8))
+    v = rs.standard_normal((n, 2, 8))
+    _, heavy, scores = oracle.h2o_decode_trace(q, k, v, L, W, H, 0.5, 10000.0)
+    for kv in range(2):
+        members = heavy[kv][heavy[kv] >= 0]
+        assert members.size == H
+        assert np.all(members >= L) and np.all(members <= n - 1 - W)
+        assert sum(scores[kv].values()) <= 3 * n + 1e-9
+        assert set(scores[kv]) == set(members.tolist()) | set(range(n - W, n))
+
+
 # ---------------------------------------------------------------- tile plan
 def test_tile_plan_hand_worked_cases():
     for case in _golden("tile_plan_small.json")["cases"]:
