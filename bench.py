@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the other decode workloads")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunk prefill that reads the ring")
     ap.add_argument("--no-backward", action="store_true", help="skip the masked prefill backward")
-    ap.add_argument("--only", choices=["decode", "prefill", "chunk", "backward"], default=None,
+    ap.add_argument("--no-heavy", action="store_true", help="skip prefix + heavy hitters + window decoding")
+    ap.add_argument("--only", choices=["decode", "prefill", "chunk", "backward", "heavy"], default=None,
                     help="run only one leg (for profiling); the JSON line then carries that leg only")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run one device-to-device copy of BYTES first (reference for HBM counter scaling)")
@@ -433,6 +434,59 @@ def run_backward(ps, torch, reps=5):
     return res
 
 
+def run_heavy(ps, torch, heavy=512, layers=28, reps=32):
+    """Prefix + heavy hitters + window decoding at the headline shape: 256 sequences at 131072, L=100, W=4096,
+    512 heavy slots per (sequence, KV head), steady state (heavy set full).  One step per layer = admission of
+    the token leaving the window, append, attention over L + W + H keys with the score side output, score
+    accumulation.  Reported per layer and as attention-only tok/s over `layers` layers, next to the plain
+    Prefix Sliding step (append + attention) on the same cache."""
+    n, L, W, p0 = 256, 100, 4096, 131072
+    attn = ps.AttnSpec(16, 2, 128, ps.PS_BF16, 10000.0, 1 / math.sqrt(128))
+    cap = -(-(L + W + heavy) // 64) * 64
+    cache = ps.CacheSpec(window=W, slot_capacity=cap)
+    g = torch.Generator(device="cuda").manual_seed(21)
+    ks, vs = ps.cache_shapes(attn, cache, n)
+    kc = (torch.randn(ks, generator=g, device="cuda") * 0.5).bfloat16()
+    vc = (torch.randn(vs, generator=g, device="cuda") * 0.5).bfloat16()
+    state = ps.HeavyState.new(attn, cache, n, heavy)
+    state.score.uniform_(0.0, 1.0, generator=g)
+    state.heavy_count.fill_(heavy)
+    state.heavy_pos.copy_(torch.arange(heavy, device="cuda").view(1, 1, heavy) * 37 + 500)
+    pl = torch.full((n,), L, dtype=torch.int32, device="cuda")
+    q = [torch.randn((n, 16, 128), generator=g, device="cuda").bfloat16() for _ in range(4)]
+    kn = (torch.randn((n, 1, 2, 128), generator=g, device="cuda") * 0.5).bfloat16()
+    vn = (torch.randn((n, 1, 2, 128), generator=g, device="cuda") * 0.5).bfloat16()
+    out = torch.empty((n, 16, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(ps.ps_heavy_workspace_size(attn, cache, n, 0), dtype=torch.uint8, device="cuda")
+    wsd = torch.empty(max(ps.ps_decode_workspace_size(attn, cache, n, 0), 1), dtype=torch.uint8, device="cuda")
+    positions = [torch.full((n,), p0 + i, dtype=torch.int64, device="cuda") for i in range(2 * reps + 8)]
+    cursor = [0]
+
+    def heavy_steps(k_):
+        for _ in range(k_):
+            ps.ps_heavy_decode_step(attn, cache, heavy, kc, vc, pl, positions[cursor[0]], q[cursor[0] % 4], kn, vn, out,
+                                    state, workspace=ws)
+            cursor[0] += 1
+
+    def plain_steps(k_):
+        for i in range(k_):
+            ps.ps_kv_append(attn, cache, kc, vc, pl, positions[i], kn, vn)
+            ps.ps_decode_attn(attn, cache, kc, vc, pl, positions[i], q[i % 4], out, workspace=wsd)
+    heavy_steps(4)
+    t_h = timed(torch, heavy_steps, reps) / reps
+    plain_steps(4)
+    t_p = timed(torch, plain_steps, reps) / reps
+    nvis = L + W + heavy
+    kv_bytes = n * nvis * 2 * 128 * 2 * 2
+    res = {"workload": f"decode-{p0}-w{W}-heavy{heavy}", "us_per_layer": t_h * 1e6,
+           "tok_s_attention_only": n / (t_h * layers), "keys_per_query": nvis,
+           "kv_gbs": kv_bytes / t_h / 1e9,
+           "plain_prefix_sliding_us_per_layer": t_p * 1e6, "plain_tok_s_attention_only": n / (t_p * layers)}
+    del kc, vc, state, ws, wsd
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_chunk(ps, torch, reps=5):
     """Chunk continuing live traces (C6): 64 rings at 32768 (L=100, W=4096), a 2048-token chunk each.
     One call = chunk prep (ring gather + rotations), attention, append of the chunk into the rings."""
@@ -556,6 +610,9 @@ def main():
     if args.only == "backward":
         print(json.dumps({"prefill_backward": run_backward(ps, torch)}))
         return
+    if args.only == "heavy":
+        print(json.dumps({"heavy_hitters": run_heavy(ps, torch)}))
+        return
     dec = run_decode(ps, torch, args)
     print(f"[bench] decode done: {dec['tok_s']:.0f} tok/s, kernel {dec['kernel_s'] * 1e6:.1f} us",
           file=sys.stderr, flush=True)
@@ -567,6 +624,10 @@ def main():
     if not args.no_backward and args.only is None:
         backward = run_backward(ps, torch)
         print(f"[bench] prefill backward done: {backward['tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    heavy = None
+    if not args.no_heavy and args.only is None:
+        heavy = run_heavy(ps, torch)
+        print(f"[bench] heavy hitters done: {heavy['us_per_layer']:.1f} us/layer", file=sys.stderr, flush=True)
     chunk = None
     if not args.no_chunk and args.only is None:
         chunk = run_chunk(ps, torch)
@@ -609,6 +670,7 @@ def main():
         "prefill": prefill,
         "prefill_backward": backward,
         "chunk_prefill": chunk,
+        "heavy_hitters": heavy,
         "full_attention": full,
     }
     if extra:

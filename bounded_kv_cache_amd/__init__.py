@@ -20,7 +20,7 @@ from ._lib import PS_BF16, PS_F32, PS_PE_CONTINUE, PS_PE_RESET, PSError
 
 __all__ = ["AttnSpec", "CacheSpec", "PSError", "ps_kv_append", "ps_decode_attn", "ps_prefill_attn",
            "ps_chunk_prefill_attn", "ps_chunk_prefill_workspace_size", "ps_prefill_attn_backward",
-           "ps_prefill_backward_workspace_size",
+           "ps_prefill_backward_workspace_size", "ps_heavy_decode_step", "ps_heavy_workspace_size", "HeavyState",
            "ps_prefill_plan", "ps_decode_workspace_size", "ps_decode_num_splits", "ps_prefill_workspace_size",
            "ps_prefill_tile_shape", "ps_abi_version", "cache_shapes", "PS_BF16", "PS_F32", "PS_PE_CONTINUE",
            "PS_PE_RESET"]
@@ -189,6 +189,63 @@ def ps_prefill_attn(attn: AttnSpec, window: int, prefix_len: int, kv_start: int,
     _lib.check(_lib.load().ps_prefill_attn(ctypes.byref(a), window, prefix_len, kv_start, _ptr(q), _ptr(k), _ptr(v),
                                            batch, num_q, num_k, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                            _stream(stream)))
+    return out
+
+
+def ps_heavy_workspace_size(attn: AttnSpec, cache: CacheSpec, num_seqs: int, num_splits: int = 0) -> int:
+    a, c = attn.c(), cache.c()
+    return _lib.load().ps_heavy_workspace_size(ctypes.byref(a), ctypes.byref(c), num_seqs, num_splits)
+
+
+@dataclasses.dataclass
+class HeavyState:
+    """Caller-owned state of prefix + heavy hitters + window decoding (zeros = new sequences)."""
+    score: torch.Tensor        # [num_seqs, Hkv, slot_capacity] float32
+    heavy_count: torch.Tensor  # [num_seqs, Hkv] int32
+    heavy_pos: torch.Tensor    # [num_seqs, Hkv, heavy_slots] int64
+
+    @staticmethod
+    def new(attn: AttnSpec, cache: CacheSpec, num_seqs: int, heavy_slots: int, device="cuda") -> "HeavyState":
+        h = attn.num_kv_heads
+        return HeavyState(torch.zeros((num_seqs, h, cache.slot_capacity), dtype=torch.float32, device=device),
+                          torch.zeros((num_seqs, h), dtype=torch.int32, device=device),
+                          torch.full((num_seqs, h, max(heavy_slots, 1)), -1, dtype=torch.int64, device=device))
+
+
+def ps_heavy_decode_step(attn: AttnSpec, cache: CacheSpec, heavy_slots: int, k_cache: torch.Tensor,
+                         v_cache: torch.Tensor, prefix_len: torch.Tensor, pos: torch.Tensor, q: torch.Tensor,
+                         k_new: torch.Tensor, v_new: torch.Tensor, out: torch.Tensor, state: HeavyState, *,
+                         block_table: Optional[torch.Tensor] = None, num_splits: int = 0,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step at positions pos with prefix + heavy hitters + window (see the header)."""
+    dt = attn.torch_dtype
+    num_seqs = q.shape[0]
+    _need(q, "q", dt, num_seqs * attn.num_q_heads * attn.head_dim)
+    _need(out, "out", dt, q.numel())
+    _need(k_new, "k_new", dt, num_seqs * attn.num_kv_heads * attn.head_dim)
+    _need(v_new, "v_new", dt, k_new.numel())
+    ks, vs = cache_shapes(attn, cache, num_seqs)
+    _need(k_cache, "k_cache", dt, math.prod(ks))
+    _need(v_cache, "v_cache", dt, math.prod(vs))
+    _need(prefix_len, "prefix_len", torch.int32, num_seqs)
+    _need(pos, "pos", torch.int64, num_seqs)
+    _need(state.score, "score", torch.float32, num_seqs * attn.num_kv_heads * cache.slot_capacity)
+    _need(state.heavy_count, "heavy_count", torch.int32, num_seqs * attn.num_kv_heads)
+    _need(state.heavy_pos, "heavy_pos", torch.int64)
+    if state.heavy_pos.numel() < num_seqs * attn.num_kv_heads * heavy_slots:
+        raise ValueError("heavy_pos too small")
+    if block_table is not None:
+        _need(block_table, "block_table", torch.int32, num_seqs * (cache.slot_capacity // 64))
+    need = ps_heavy_workspace_size(attn, cache, num_seqs, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    a, c = attn.c(), cache.c()
+    _lib.check(_lib.load().ps_heavy_decode_step(ctypes.byref(a), ctypes.byref(c), heavy_slots, _ptr(k_cache),
+                                                _ptr(v_cache), _ptr(block_table), _ptr(prefix_len), _ptr(pos),
+                                                _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), num_seqs,
+                                                _ptr(state.score), _ptr(state.heavy_count), _ptr(state.heavy_pos),
+                                                num_splits, _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

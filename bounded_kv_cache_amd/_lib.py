@@ -46,6 +46,9 @@ SIGNATURES = {
     "ps_prefill_attn_backward": (_i32, [_pA, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
                                         _vp, _vp, _vp, _sz, _vp]),
     "ps_prefill_backward_workspace_size": (_sz, [_pA, _i32, _i32, _i32]),
+    "ps_heavy_decode_step": (_i32, [_pA, _pC, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                    _i32, _vp, _sz, _vp]),
+    "ps_heavy_workspace_size": (_sz, [_pA, _pC, _i32, _i32]),
     "ps_prefill_tile_shape": (_i32, [_pA, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "ps_prefill_plan": (_i32, [_pA, _i32, _i32, _i64, _i32, _i32, _vp, _i32, _vp, _vp]),
     "ps_last_error": (ctypes.c_char_p, []),

@@ -306,7 +306,120 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, c
   a.scale_log2 = attn->softmax_scale * 1.4426950408889634f;
   a.rope = make_rope(attn);
   a.reset_pe = attn->pe_mode == PS_PE_RESET ? 1 : 0;
+  a.heavy_count = nullptr;
+  a.heavy_slots = 0;
+  a.stat_scores = nullptr;
+  a.stat_lse2 = nullptr;
   return from_hip(ps::launch_decode(a, stream), "ps_decode_attn launch");
+}
+
+size_t ps_heavy_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* cache, int32_t num_seqs,
+                               int32_t num_splits) {
+  if (check_attn(attn) != PS_OK || !cache || cache->slot_capacity <= 0 || num_seqs < 0 || num_splits < 0) return 0;
+  const int32_t sp = num_splits > 0 ? num_splits : auto_splits(attn, cache, num_seqs, device_cu_count());
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  return al(decode_ws_bytes(attn, num_seqs, sp)) +
+         al((size_t)num_seqs * attn->num_q_heads * cache->slot_capacity * sizeof(float)) +
+         al((size_t)num_seqs * attn->num_q_heads * sizeof(float));
+}
+
+ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* cache, int32_t heavy_slots,
+                               void* k_cache, void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
+                               const int64_t* pos, const void* q, const void* k_new, const void* v_new, void* out,
+                               int32_t num_seqs, float* score, int32_t* heavy_count, int64_t* heavy_pos,
+                               int32_t num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ps_status st = check_attn(attn);
+  if (st != PS_OK) return st;
+  if ((st = continue_pe_only(attn, "ps_heavy_decode_step")) != PS_OK) return st;
+  if ((st = check_cache(cache, block_table)) != PS_OK) return st;
+  if (num_seqs < 0 || num_splits < 0 || heavy_slots < 0)
+    return fail(PS_INVALID_ARGUMENT, "negative num_seqs, num_splits or heavy_slots");
+  if ((int64_t)cache->window + heavy_slots > cache->slot_capacity)
+    return fail(PS_INVALID_ARGUMENT, "W + heavy_slots exceeds slot_capacity");
+  if ((int64_t)(attn->num_q_heads / attn->num_kv_heads) * cache->slot_capacity * 4 >= ((int64_t)1 << 31))
+    return fail(PS_INVALID_ARGUMENT, "slot_capacity too large for heavy-hitter statistics");
+  if (num_seqs == 0) return ok();
+  if (!k_cache || !v_cache || !prefix_len || !pos || !q || !k_new || !v_new || !out || !score || !heavy_count ||
+      (heavy_slots > 0 && !heavy_pos))
+    return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if ((int64_t)num_seqs * attn->num_kv_heads * 64 > (int64_t)1 << 31)
+    return fail(PS_INVALID_ARGUMENT, "num_seqs too large for one launch");
+  const int32_t splits = num_splits > 0 ? num_splits : auto_splits(attn, cache, num_seqs, device_cu_count());
+  if (splits > 1024 || splits > cache->slot_capacity / 32)
+    return fail(PS_INVALID_ARGUMENT, "num_splits %d too large for slot_capacity %d", splits, cache->slot_capacity);
+  const size_t need = ps_heavy_workspace_size(attn, cache, num_seqs, splits);
+  if (!workspace || workspace_bytes < need)
+    return fail(PS_WORKSPACE_TOO_SMALL, "heavy decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* w = static_cast<char*>(workspace);
+  const size_t part = al(decode_ws_bytes(attn, num_seqs, splits));
+  float* stat_scores = reinterpret_cast<float*>(w + part);
+  float* stat_lse2 = reinterpret_cast<float*>(w + part +
+                                              al((size_t)num_seqs * attn->num_q_heads * cache->slot_capacity * 4));
+  const ps::CacheGeom geom = make_geom(attn, cache);
+  const ps::RopeFreq rope = make_rope(attn);
+  ps::HeavyArgs h;
+  h.geom = geom;
+  h.dtype = attn->dtype;
+  h.hq = attn->num_q_heads;
+  h.group = attn->num_q_heads / attn->num_kv_heads;
+  h.heavy_slots = heavy_slots;
+  h.k_cache = k_cache;
+  h.v_cache = v_cache;
+  h.block_table = block_table;
+  h.prefix_len = prefix_len;
+  h.pos = pos;
+  h.num_seqs = num_seqs;
+  h.score = score;
+  h.heavy_count = heavy_count;
+  h.heavy_pos = heavy_pos;
+  h.stat_scores = stat_scores;
+  h.stat_lse2 = stat_lse2;
+  hipError_t e = ps::launch_heavy_retire(h, stream);   // 1. the token leaving the window
+  if (e != hipSuccess) return from_hip(e, "ps_heavy_decode_step retire launch");
+  ps::AppendArgs ap;                                    // 2. the new token into the ring
+  ap.geom = geom;
+  ap.dtype = attn->dtype;
+  ap.k_cache = k_cache;
+  ap.v_cache = v_cache;
+  ap.block_table = block_table;
+  ap.prefix_len = prefix_len;
+  ap.start_pos = pos;
+  ap.seq_tokens = nullptr;
+  ap.tokens_per_seq = 1;
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.num_seqs = num_seqs;
+  ap.slot_pos = nullptr;
+  ap.rope = rope;
+  if ((e = ps::launch_append(ap, stream)) != hipSuccess) return from_hip(e, "ps_heavy_decode_step append launch");
+  ps::DecodeArgs a;                                     // 3. attention over prefix + window + heavy slots
+  a.geom = geom;
+  a.dtype = attn->dtype;
+  a.hq = attn->num_q_heads;
+  a.group = attn->num_q_heads / attn->num_kv_heads;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.prefix_len = prefix_len;
+  a.pos = pos;
+  a.q = q;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_splits = splits;
+  a.split_keys = split_keys_for(cache, splits);
+  const size_t rows = (size_t)num_seqs * attn->num_q_heads * splits;
+  a.part_o = splits > 1 ? reinterpret_cast<float*>(w) : nullptr;
+  a.part_ml = splits > 1 ? reinterpret_cast<float*>(w) + rows * attn->head_dim : nullptr;
+  a.scale_log2 = attn->softmax_scale * 1.4426950408889634f;
+  a.rope = rope;
+  a.reset_pe = 0;
+  a.heavy_count = heavy_count;
+  a.heavy_slots = heavy_slots;
+  a.stat_scores = stat_scores;
+  a.stat_lse2 = stat_lse2;
+  if ((e = ps::launch_decode(a, stream)) != hipSuccess) return from_hip(e, "ps_heavy_decode_step decode launch");
+  return from_hip(ps::launch_heavy_accumulate(h, stream), "ps_heavy_decode_step accumulate launch");  // 4.
 }
 
 size_t ps_prefill_workspace_size(const ps_attn_desc* attn, int32_t batch, int32_t num_queries, int32_t num_keys) {

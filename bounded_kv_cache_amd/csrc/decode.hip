@@ -57,7 +57,7 @@ __device__ inline u32x4 stream_load(const uint16_t* p) {
 // ---------------------------------------------------------------------------
 // bf16 MFMA partial kernel
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool kReset>
+template <int D, int NW, bool kReset, bool kStats>
 __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NC = D / 32;   // QK k-steps (32 dims each)
   constexpr int NDT = D / 16;  // PV d-tiles (16 dims each)
@@ -75,9 +75,16 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
 
   const int32_t L = a.prefix_len[s];
   const int64_t pos = a.pos[s];
-  // visible keys = ring slots [0, min(p+1, L+W)); every one must exist
-  const int64_t nvis64 = pos + 1 < (int64_t)L + geo.window ? pos + 1 : (int64_t)L + geo.window;
-  bool bad = L < 0 || pos < 0 || nvis64 > geo.slot_capacity;
+  // visible keys = ring slots [0, min(p+1, L+W)) (+ the occupied heavy slots
+  // right after the window); every one must exist
+  int64_t nvis64 = pos + 1 < (int64_t)L + geo.window ? pos + 1 : (int64_t)L + geo.window;
+  bool bad = L < 0 || pos < 0;
+  if (kStats) {
+    const int32_t hc = a.heavy_count[(int64_t)s * geo.hkv + h];
+    nvis64 += hc;
+    bad = bad || hc < 0 || hc > a.heavy_slots || (int64_t)L + geo.window + a.heavy_slots > geo.slot_capacity;
+  }
+  bad = bad || nvis64 > geo.slot_capacity;
   const int nvis = bad ? 0 : (int)nvis64;
   const int kb = split * a.split_keys;
   const int ke = kb + a.split_keys < nvis ? kb + a.split_keys : nvis;
@@ -103,6 +110,10 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+  // heavy-hitter statistics: the group's score rows of this (sequence, KV head)
+  const __amdgpu_buffer_rsrc_t stat_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      kStats ? a.stat_scores + ((int64_t)s * geo.hkv + h) * a.group * geo.slot_capacity : nullptr, (short)0,
+      kStats ? a.group * geo.slot_capacity * 4 : 0, 0x00020000);
 
   // chunk index list of this wave: first chunk kb/32 + wave, stride NW
   const int c_end = (ke + 31) >> 5;   // chunks touching [kb, ke)
@@ -207,6 +218,18 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
           if (k0 + 1 >= ke || k0 + 1 < kb) vr[dt][e] &= 0x0000ffffu;
         }
       }
+    }
+    if (kStats) {
+      // scores of this lane's head for the heavy-hitter statistics: every lane
+      // issues the same two stores (no branch, so the load pipeline's wait
+      // counts stay exact); lanes of padding heads aim past the buffer range and
+      // the hardware drops them.  Chunks never cross a split boundary, so the
+      // -inf of a final partial chunk only lands in slots past the visible range.
+      const int voff = (r < a.group ? r * geo.slot_capacity + key0 : a.group * geo.slot_capacity) * 4;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{sv[0], sv[1], sv[2], sv[3]}), stat_rsrc,
+                                             voff, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{sv[4], sv[5], sv[6], sv[7]}), stat_rsrc,
+                                             voff + 16, 0, 0);
     }
     float mx = sv[0];
 #pragma unroll
@@ -339,6 +362,7 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
     if (a.num_splits == 1) {
       const float val = any_bad ? __builtin_nanf("") : o / l;
       static_cast<uint16_t*>(a.out)[row * D + d] = f32_to_bf16_bits(val);
+      if (kStats && d == 0) a.stat_lse2[row] = any_bad ? __builtin_nanf("") : M + __log2f(l);
     } else {
       const int64_t prow = row * a.num_splits + split;
       a.part_o[prow * D + d] = any_bad ? __builtin_nanf("") : o;
@@ -375,8 +399,15 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 
   const int32_t L = a.prefix_len[s];
   const int64_t pos = a.pos[s];
-  const int64_t nvis64 = pos + 1 < (int64_t)L + geo.window ? pos + 1 : (int64_t)L + geo.window;
-  const bool seq_bad = L < 0 || pos < 0 || nvis64 > geo.slot_capacity;
+  int64_t nvis64 = pos + 1 < (int64_t)L + geo.window ? pos + 1 : (int64_t)L + geo.window;
+  bool seq_bad = L < 0 || pos < 0;
+  if (a.heavy_count) {
+    const int32_t hc = a.heavy_count[(int64_t)s * geo.hkv + h];
+    nvis64 += hc;
+    seq_bad = seq_bad || hc < 0 || hc > a.heavy_slots ||
+              (int64_t)L + geo.window + a.heavy_slots > geo.slot_capacity;
+  }
+  seq_bad = seq_bad || nvis64 > geo.slot_capacity;
   const int nvis = seq_bad ? 0 : (int)nvis64;
   const int kb = split * a.split_keys;
   const int ke = kb + a.split_keys < nvis ? kb + a.split_keys : nvis;
@@ -437,6 +468,8 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
       float sc = 0.f;
       for (int d = 0; d < D; ++d) sc += qv[d] * ks[j][d];
       ps_[n][j] = (t0 + j < ke) ? sc : -INFINITY;
+      if (a.stat_scores && t0 + j < ke)
+        a.stat_scores[(((int64_t)s * geo.hkv + h) * G + n) * geo.slot_capacity + t0 + j] = sc;
     }
     __syncthreads();
     if (tid < G) {
@@ -477,6 +510,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     const int64_t row = (int64_t)s * a.hq + h * G + n;
     if (a.num_splits == 1) {
       static_cast<float*>(a.out)[row * D + d] = any_bad ? __builtin_nanf("") : acc[k] / l_s[n];
+      if (a.stat_lse2 && d == 0) a.stat_lse2[row] = any_bad ? __builtin_nanf("") : m_s[n] + __log2f(l_s[n]);
     } else {
       const int64_t prow = row * a.num_splits + split;
       a.part_o[prow * D + d] = any_bad ? __builtin_nanf("") : acc[k];
@@ -514,6 +548,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   }
   const float val = nan ? __builtin_nanf("") : o / l;
   Elem<OutT>::store(static_cast<OutT*>(a.out) + row * D + d, val);
+  if (a.stat_lse2 && d == 0) a.stat_lse2[row] = nan ? __builtin_nanf("") : M + __log2f(l);
 }
 
 template <int D>
@@ -521,10 +556,12 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((uint32_t)((int64_t)a.num_seqs * a.geom.hkv * a.num_splits));
   if (a.dtype == PS_BF16) {
     constexpr int NW = PS_DECODE_WAVES;
-    if (a.reset_pe)
-      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, true>), grid, dim3(NW * 64), 0, stream, a);
+    if (a.heavy_count)
+      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, true>), grid, dim3(NW * 64), 0, stream, a);
+    else if (a.reset_pe)
+      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, true, false>), grid, dim3(NW * 64), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false>), grid, dim3(NW * 64), 0, stream, a);
+      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, false>), grid, dim3(NW * 64), 0, stream, a);
   } else {
     hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(256), 0, stream, a);
   }

@@ -1,0 +1,136 @@
+// Prefix + heavy hitters + window: the bookkeeping around a decode step.
+//
+// Blog "Prefix Sliding 完全拆解" (pinghaoyang.com.cn), section comparing the
+// method with H2O: H2O keeps the tokens that have drawn the most attention so
+// far, Prefix Sliding pins the prefix; the two can be stacked -- prefix,
+// heavily attended middle tokens and the window.  The pages give no algorithm,
+// so the rule here is the plain reading (stated with the C ABI):
+//   * per (sequence, KV head) up to H heavy slots right after the window's W
+//     ring slots, so the visible slots stay one range [0, L + W + count);
+//   * a token's score is the attention it has received while cached, summed
+//     over the query heads of its KV head;
+//   * when a token leaves the window it joins the heavy set if a slot is
+//     free, or replaces the weakest member (smallest score, oldest on ties) if
+//     its own score is strictly larger; otherwise it is dropped.
+// Kernels: retire (before the step's append, one wave per (sequence, KV head):
+// admission and the K/V copy into the heavy slot) and accumulate (after the
+// decode kernel has written the step's scores and each row's log2-sum-exp2).
+#include "ps_internal.h"
+
+namespace ps {
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(64) void heavy_retire_kernel(HeavyArgs a) {
+  const CacheGeom& g = a.geom;
+  const int32_t h = (int32_t)(blockIdx.x % g.hkv);
+  const int32_t s = (int32_t)(blockIdx.x / g.hkv);
+  const int lane = threadIdx.x;
+  const int32_t L = a.prefix_len[s];
+  const int64_t p = a.pos[s];
+  const int32_t H = a.heavy_slots;
+  if (L < 0 || p < 0 || (int64_t)L + g.window + H > g.slot_capacity) return;
+  const int64_t e = p - g.window;   // the token leaving the window at this step
+  if (e < L) return;
+  const int32_t se = ring_slot(e, L, g.window);
+  const int64_t sh = (int64_t)s * g.hkv + h;
+  float* score = a.score + sh * g.slot_capacity;
+  int64_t* hpos = a.heavy_pos + sh * H;
+  const float cand = score[se];
+  const int32_t base = L + g.window;
+  const int32_t cnt = a.heavy_count[sh];
+  int32_t dst = -1;
+  if (H > 0) {
+    if (cnt < H) {
+      dst = cnt;
+    } else {
+      // the weakest member: smallest score, then oldest position
+      float best = INFINITY;
+      int64_t bpos = INT64_MAX;
+      int32_t bidx = -1;
+      for (int32_t i = lane; i < H; i += 64) {
+        const float sc = score[base + i];
+        const int64_t hp = hpos[i];
+        if (sc < best || (sc == best && hp < bpos)) {
+          best = sc;
+          bpos = hp;
+          bidx = i;
+        }
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ob = __shfl_xor(best, off);
+        const int64_t op = __shfl_xor(bpos, off);
+        const int32_t oi = __shfl_xor(bidx, off);
+        if (ob < best || (ob == best && op < bpos)) {
+          best = ob;
+          bpos = op;
+          bidx = oi;
+        }
+      }
+      if (cand > best) dst = bidx;
+    }
+  }
+  if (dst >= 0) {
+    const int32_t sd = base + dst;
+    const int64_t re = region_offset(g, a.block_table, s, h, se);
+    const int64_t rd = region_offset(g, a.block_table, s, h, sd);
+    if (re >= 0 && rd >= 0) {
+      T* kc = static_cast<T*>(a.k_cache);
+      T* vc = static_cast<T*>(a.v_cache);
+      for (int32_t d = lane; d < g.head_dim; d += 64) {
+        kc[rd + k_in_region(sd, d, g.head_dim)] = kc[re + k_in_region(se, d, g.head_dim)];
+        vc[rd + v_in_region(sd, d, g.head_dim)] = vc[re + v_in_region(se, d, g.head_dim)];
+      }
+    }
+    if (lane == 0) {
+      score[sd] = cand;
+      hpos[dst] = e;
+      if (dst == cnt) a.heavy_count[sh] = cnt + 1;
+    }
+  }
+  if (lane == 0) score[se] = 0.f;   // the slot receives position p next
+}
+
+// score[j] += sum over the group's query heads of exp2(s_j - lse2), j in [L, n_vis)
+__global__ __launch_bounds__(256) void heavy_accumulate_kernel(HeavyArgs a) {
+  const CacheGeom& g = a.geom;
+  const int32_t h = (int32_t)(blockIdx.x % g.hkv);
+  const int32_t s = (int32_t)(blockIdx.x / g.hkv);
+  const int32_t L = a.prefix_len[s];
+  const int64_t p = a.pos[s];
+  if (L < 0 || p < 0 || (int64_t)L + g.window + a.heavy_slots > g.slot_capacity) return;
+  const int64_t sh = (int64_t)s * g.hkv + h;
+  const int64_t lw = (int64_t)L + g.window;
+  const int64_t nvis = (p + 1 < lw ? p + 1 : lw) + a.heavy_count[sh];
+  if (nvis > g.slot_capacity) return;
+  float lse2[kMaxGroup];
+  for (int n = 0; n < a.group; ++n) lse2[n] = a.stat_lse2[(int64_t)s * a.hq + h * a.group + n];
+  float* score = a.score + sh * g.slot_capacity;
+  const float* st = a.stat_scores + sh * a.group * g.slot_capacity;
+  for (int64_t j = L + threadIdx.x; j < nvis; j += 256) {
+    float m = 0.f;
+    for (int n = 0; n < a.group; ++n) m += __builtin_amdgcn_exp2f(st[(int64_t)n * g.slot_capacity + j] - lse2[n]);
+    score[j] += m;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_heavy_retire(const HeavyArgs& a, hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  const dim3 grid((uint32_t)((int64_t)a.num_seqs * a.geom.hkv));
+  if (a.dtype == PS_BF16)
+    hipLaunchKernelGGL(heavy_retire_kernel<uint16_t>, grid, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(heavy_retire_kernel<float>, grid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_heavy_accumulate(const HeavyArgs& a, hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  const dim3 grid((uint32_t)((int64_t)a.num_seqs * a.geom.hkv));
+  hipLaunchKernelGGL(heavy_accumulate_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ps

@@ -45,6 +45,30 @@ struct DecodeArgs {
   float scale_log2;       // softmax_scale * log2(e)
   RopeFreq rope;
   int32_t reset_pe;       // 1: Reset PE scoring (prefix slots use the renumbered query)
+  // heavy-hitter mode (NULL / 0 otherwise): visible slots are [0, min(p+1, L+W) + heavy_count)
+  const int32_t* heavy_count;  // [num_seqs][hkv]
+  int32_t heavy_slots;         // H: heavy slots after the window, L + W + H <= slot_capacity
+  float* stat_scores;          // [num_seqs][hkv][group][slot_capacity] scores (log2 units) of the visible slots
+  float* stat_lse2;            // [num_seqs][hq] log2-sum-exp2 of each query row
+};
+
+// Heavy-hitter bookkeeping around a decode step.
+struct HeavyArgs {
+  CacheGeom geom;
+  int32_t dtype;
+  int32_t hq, group;
+  int32_t heavy_slots;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const int32_t* prefix_len;
+  const int64_t* pos;
+  int32_t num_seqs;
+  float* score;                // [num_seqs][hkv][slot_capacity] accumulated attention per slot
+  int32_t* heavy_count;        // [num_seqs][hkv]
+  int64_t* heavy_pos;          // [num_seqs][hkv][heavy_slots]
+  const float* stat_scores;
+  const float* stat_lse2;
 };
 
 struct PrefillArgs {
@@ -111,6 +135,8 @@ struct BackwardArgs {
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_heavy_retire(const HeavyArgs& a, hipStream_t stream);
+hipError_t launch_heavy_accumulate(const HeavyArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_chunk_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_plan(int32_t num_q, int32_t num_k, int32_t prefix_len, int32_t window,

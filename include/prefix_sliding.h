@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 4
+#define PS_ABI_VERSION 5
 
 typedef enum {
   PS_OK = 0,
@@ -206,6 +206,43 @@ ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t pref
 
 size_t ps_prefill_workspace_size(const ps_attn_desc* attn, int32_t batch, int32_t num_queries,
                                  int32_t num_keys);
+
+/* ps_heavy_decode_step -- one decode step with prefix + heavy hitters +
+ * window.  Blog "Prefix Sliding 完全拆解", section comparing the method with
+ * H2O: H2O keeps the tokens that have drawn the most attention (it looks
+ * back), Prefix Sliding pins the prefix (it looks ahead); the two can be
+ * stacked.  The pages give no algorithm; the rule implemented:
+ *   - per (sequence, KV head), heavy_slots = H cache slots right after the
+ *     window's ring slots: slots [0, L) prefix, [L, L+W) window, [L+W, L+W+H)
+ *     heavy hitters, so L + W + H <= slot_capacity for every sequence;
+ *   - a token's score is the softmax attention it has received while cached,
+ *     summed over the query heads of its KV head;
+ *   - at step p the token p - W leaves the window; it takes the next free
+ *     heavy slot, or replaces the member with the smallest score (ties: the
+ *     oldest position) if its own score is strictly larger, else it is dropped;
+ *   - then the token p is appended (as ps_kv_append), the query at p attends
+ *     to prefix + heavy set + window, and every visible non-prefix token adds
+ *     the attention it just received to its score.
+ * Arguments as ps_kv_append (k_new, v_new: [num_seqs][1][Hkv][D], the token
+ * at pos) and ps_decode_attn (q, out, pos, num_splits, workspace), plus the
+ * caller-owned state, zeroed when a sequence starts:
+ *   score       : [num_seqs][Hkv][slot_capacity] float, 0 initially;
+ *   heavy_count : [num_seqs][Hkv] int32, 0 initially;
+ *   heavy_pos   : [num_seqs][Hkv][heavy_slots] int64 positions of the heavy
+ *                 members (entries past heavy_count are unspecified).
+ * Steps must be issued for consecutive positions of a sequence (the
+ * admission at p needs the scores accumulated up to p - 1).  workspace:
+ * >= ps_heavy_workspace_size(...) bytes.  Continue PE only. */
+ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* cache,
+                               int32_t heavy_slots, void* k_cache, void* v_cache,
+                               const int32_t* block_table, const int32_t* prefix_len,
+                               const int64_t* pos, const void* q, const void* k_new,
+                               const void* v_new, void* out, int32_t num_seqs, float* score,
+                               int32_t* heavy_count, int64_t* heavy_pos, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t ps_heavy_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* cache,
+                               int32_t num_seqs, int32_t num_splits);
 
 /* ps_prefill_attn_backward -- gradients of ps_prefill_attn for the raw
  * inputs: dq, dk, dv from the upstream gradient d_out.  Blog "Prefix Sliding

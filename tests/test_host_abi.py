@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ps_abi_version() == 4
+    assert lib.ps_abi_version() == 5
     assert lib.ps_status_string(0) == b"ok"
     assert lib.ps_status_string(3) == b"workspace too small"
 
@@ -253,3 +253,25 @@ def test_reset_pe_is_decode_only(lib):
     # decode accepts it (fails later only on the NULL cache pointer)
     assert lib.ps_decode_attn(ctypes.byref(a), ctypes.byref(c), None, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 1,
                               None, 0, None) == 1
+
+
+def test_heavy_decode_validation_and_workspace(lib):
+    a, c = _descs(cap=4352)
+    need = lib.ps_heavy_workspace_size(ctypes.byref(a), ctypes.byref(c), 4, 1)
+    al = lambda x: (x + 255) // 256 * 256
+    assert need == al(0) + al(4 * 16 * 4352 * 4) + al(4 * 16 * 4)
+    need3 = lib.ps_heavy_workspace_size(ctypes.byref(a), ctypes.byref(c), 4, 3)
+    assert need3 == al(4 * 16 * 3 * (128 + 2) * 4) + al(4 * 16 * 4352 * 4) + al(4 * 16 * 4)
+
+    def call(attn=a, cache=c, H=128, score=FAKE, hpos=FAKE, ws=FAKE, wsb=need, splits=1, seqs=4):
+        return lib.ps_heavy_decode_step(ctypes.byref(attn), ctypes.byref(cache), H, FAKE, FAKE, None, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, FAKE, seqs, score, FAKE, hpos, splits, ws, wsb, None)
+    assert call(wsb=need - 1) == 3
+    assert call(score=None) == 1
+    assert call(hpos=None) == 1
+    assert call(hpos=None, H=0) != 1 or lib.ps_last_error()      # no heavy slots: heavy_pos may be NULL
+    assert call(H=-1) == 1
+    assert call(H=4352 - 4096 + 1) == 1                          # W + H beyond the capacity
+    assert call(seqs=0) == 0
+    r, _ = _descs(pe=1)
+    assert call(attn=r) == 2
