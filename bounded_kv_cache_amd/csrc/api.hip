@@ -13,6 +13,10 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// the bf16 attention kernel addresses eight V^T rows of one load with 32-bit
+// byte offsets: 7 * padded keys * 2 bytes must stay below 2^32
+constexpr size_t kMaxBf16PrefillKeys = (size_t)1 << 28;
+
 ps_status fail(ps_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 ps_status fail(ps_status st, const char* fmt, ...) {
   char buf[512];
@@ -473,6 +477,8 @@ ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t pref
   a.lse = lse;
   const size_t elem = attn->dtype == PS_BF16 ? 2 : 4;
   const size_t nkp = ((size_t)num_keys + bn - 1) / bn * bn;
+  if (attn->dtype == PS_BF16 && nkp > kMaxBf16PrefillKeys)
+    return fail(PS_INVALID_ARGUMENT, "bf16 prefill takes at most 2^28 keys, got %d", num_keys);
   const size_t kv = 2 * (size_t)batch * attn->num_kv_heads * nkp * attn->head_dim * elem;
   a.k_rot = workspace;
   a.rope_cs = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((kv + 255) / 256) * 256);
@@ -586,6 +592,8 @@ ps_status ps_chunk_prefill_attn(const ps_attn_desc* attn, const ps_cache_desc* c
     return fail(PS_WORKSPACE_TOO_SMALL, "chunk prefill needs %zu workspace bytes, got %zu", need, workspace_bytes);
   const size_t elem = attn->dtype == PS_BF16 ? 2 : 4;
   const size_t nkp = chunk_nkp(cache, chunk_len);
+  if (attn->dtype == PS_BF16 && nkp > kMaxBf16PrefillKeys)
+    return fail(PS_INVALID_ARGUMENT, "bf16 chunk prefill takes at most 2^28 keys per sequence");
   const size_t kv = 2 * (size_t)num_seqs * attn->num_kv_heads * nkp * attn->head_dim * elem;
   ps::PrefillArgs a;
   a.dtype = attn->dtype;

@@ -431,24 +431,55 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 // Softmax bookkeeping per query column: `ref` is the reference max (log2
 // units); the S accumulator starts at -ref, so the MFMA itself yields s - ref
 // and the fast path is just max / exp2 / sum / convert.
+//
+// Software pipeline: while tile j's probabilities are formed (VALU) and
+// multiplied into O (MFMA), the scores of tile j+1 are computed (MFMA), so each
+// wave always has independent matrix work to issue next to its vector work.
+// K and V^T tiles go global -> LDS directly (global_load_lds_dwordx4, no
+// staging registers) into two-deep rings: at step j the loads of K(j+2) and
+// V(j+1) are in flight.  Inside a tile the 16-byte chunks of a row are
+// XOR-swizzled by row so that the operand reads (16 consecutive rows, one chunk
+// column) fall in distinct LDS banks.  The four buffers are separate LDS
+// objects and the loop is unrolled by two, so every access names its buffer:
+// the compiler can then see that a load in flight into one buffer does not
+// alias reads of another and does not wait for it.
+template <int CH>
+__device__ inline int chunk_swizzle(int row) {   // CH 16-byte chunks per row (8 or 16)
+  return (row / (16 / CH)) & (CH - 1);
+}
+
+// Workgroup barrier that orders LDS only: global loads in flight stay in
+// flight (__syncthreads would wait for them too).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// one wave load of 64 x 16 bytes into 1 KB of LDS at `lds` (lane i -> lds + 16 i)
+__device__ inline void load_to_lds(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 template <int D, bool kPerSeq>
 __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int BM = 128, BN = 64;
   constexpr int KS = D / 16;        // QK k-steps
   constexpr int MT = D / 32;        // PV output d-tiles
-  constexpr int KPAD = D + 8;       // K row stride in LDS (bf16 elements)
-  constexpr int VPAD = BN + 8;      // V^T row stride in LDS
-  constexpr int KPIECES = BN * D / 8 / 256;   // 16-byte pieces per thread per tile
-  constexpr int VPIECES = D * BN / 8 / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VPAD];
+  constexpr int KCH = D / 8;        // 16-byte chunks per K row
+  constexpr int VCH = BN / 8;       // 16-byte chunks per V^T row
+  constexpr int DMA = BN * D / 8 / 256;   // 1 KB wave loads per wave per tile (same for K and V^T)
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[D * BN];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[D * BN];
 
   PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, BM, BN};
   const int32_t n_qt = pf_num_qtiles(geo);
   const Item it = decode_item(a, n_qt);
   if (!it.valid) return;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
   if (kPerSeq && !chunk_geom(a, it.b, BM, BN, geo)) {   // sequence cannot be served: NaN rows
     const int32_t tn = it.qt * BM + wave * 32 + col;
@@ -465,44 +496,67 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
   const uint16_t* vt = static_cast<const uint16_t*>(a.k_rot) + (int64_t)a.batch * a.hkv * nkp * D +
                        ((int64_t)it.b * a.hkv + kvh) * D * nkp;
 
-  u32x4 kreg[KPIECES], vreg[VPIECES];
-  // global -> registers (next tile) and registers -> LDS; plain code so that the
-  // staging arrays stay in registers
-#define PS_PF_GLOAD(KT)                                                                              \
-  do {                                                                                              \
-    _Pragma("unroll") for (int p = 0; p < KPIECES; ++p) {                                           \
-      const int piece = tid + 256 * p;                                                              \
-      kreg[p] = *reinterpret_cast<const u32x4*>(kr + ((int64_t)(KT) * BN + piece / (D / 8)) * D +   \
-                                                (piece % (D / 8)) * 8);                             \
-    }                                                                                               \
-    _Pragma("unroll") for (int p = 0; p < VPIECES; ++p) {                                           \
-      const int piece = tid + 256 * p;                                                              \
-      vreg[p] = *reinterpret_cast<const u32x4*>(vt + (int64_t)(piece / (BN / 8)) * nkp +            \
-                                                (int64_t)(KT) * BN + (piece % (BN / 8)) * 8);       \
-    }                                                                                               \
-  } while (0)
-#define PS_PF_LSTORE(BUF)                                                                            \
-  do {                                                                                              \
-    _Pragma("unroll") for (int p = 0; p < KPIECES; ++p) {                                           \
-      const int piece = tid + 256 * p;                                                              \
-      *reinterpret_cast<u32x4*>(&k_lds[BUF][(piece / (D / 8)) * KPAD + (piece % (D / 8)) * 8]) =    \
-          kreg[p];                                                                                  \
-    }                                                                                               \
-    _Pragma("unroll") for (int p = 0; p < VPIECES; ++p) {                                           \
-      const int piece = tid + 256 * p;                                                              \
-      *reinterpret_cast<u32x4*>(&v_lds[BUF][(piece / (BN / 8)) * VPAD + (piece % (BN / 8)) * 8]) =  \
-          vreg[p];                                                                                  \
-    }                                                                                               \
-  } while (0)
+  // Wave load p of wave w fills LDS chunks (4p + w)*64 + lane, i.e. rows
+  // (4p + w)*64/CH + lane/CH; the row's swizzle depends on (w, lane) only (the
+  // rows of one load step by a multiple of the swizzle period), so one source
+  // offset per lane serves every p.
+  const uint32_t koff = (uint32_t)((wave * (64 / KCH) + lane / KCH) * D +
+                                   ((lane % KCH) ^ chunk_swizzle<KCH>(wave * (64 / KCH) + lane / KCH)) * 8);
+  const uint32_t voff = (uint32_t)(lane / VCH) * (uint32_t)nkp +
+                        (uint32_t)(((lane % VCH) ^ chunk_swizzle<VCH>(wave * (64 / VCH) + lane / VCH)) * 8);
+  auto load_k = [&](int32_t kt, uint16_t* dst) {
+    const uint16_t* src = kr + (int64_t)kt * BN * D + koff;
+#pragma unroll
+    for (int p = 0; p < DMA; ++p) load_to_lds(src + p * 4 * (64 / KCH) * D, dst + (p * 4 + wave) * 512);
+  };
+  auto load_v = [&](int32_t kt, uint16_t* dst) {
+    const uint16_t* src = vt + (int64_t)kt * BN + voff;
+#pragma unroll
+    for (int p = 0; p < DMA; ++p)   // wave load p covers V^T rows (p*4 + wave) * 64/VCH + [0, 64/VCH)
+      load_to_lds(src + (int64_t)((p * 4 + wave) * (64 / VCH)) * nkp, dst + (p * 4 + wave) * 512);
+  };
+  // Inside the loop the tiles are staged through registers instead: a wave's
+  // LDS reads issued after a direct-to-LDS load wait for that load to land,
+  // which would serialise the prefetch with the tile being computed.
+  auto gload_k = [&](int32_t kt, u32x4* r) {
+    const uint16_t* src = kr + (int64_t)kt * BN * D + koff;
+#pragma unroll
+    for (int p = 0; p < DMA; ++p) r[p] = *reinterpret_cast<const u32x4*>(src + p * 4 * (64 / KCH) * D);
+  };
+  auto gload_v = [&](int32_t kt, u32x4* r) {
+    const uint16_t* src = vt + (int64_t)kt * BN + voff;
+#pragma unroll
+    for (int p = 0; p < DMA; ++p)
+      r[p] = *reinterpret_cast<const u32x4*>(src + (int64_t)((p * 4 + wave) * (64 / VCH)) * nkp);
+  };
+  auto lstore = [&](uint16_t* dst, const u32x4* r) {
+#pragma unroll
+    for (int p = 0; p < DMA; ++p) *reinterpret_cast<u32x4*>(dst + (p * 4 + wave) * 512 + lane * 8) = r[p];
+  };
 
   const TileRange tr = pf_tile_range(geo, it.qt);
   const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
   auto cand_tile = [&](int32_t ci) { return ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix); };
+  // Every candidate is walked: a candidate with no visible pair (rare: the
+  // prefix and band ranges are exact except at their ends) is treated as a
+  // partly visible tile whose mask hides everything, which keeps the walk free
+  // of data-dependent loops.  Loads past the last candidate repeat it.
+  auto kind_at = [&](int32_t ci) {
+    const int k = pf_classify(geo, it.qt, cand_tile(ci));
+    return k == 0 ? 2 : k;
+  };
+  auto tile_at = [&](int32_t ci) { return cand_tile(ci < n_cand ? ci : n_cand - 1); };
 
-  int32_t ci = 0;
-  int kind = 0;
-  while (ci < n_cand && (kind = pf_classify(geo, it.qt, cand_tile(ci))) == 0) ++ci;
-  if (ci < n_cand) PS_PF_GLOAD(cand_tile(ci));   // in flight while the query prologue runs
+  // tiles c0, c0 + 1 of the walk (candidate indices); K(0), V(0), K(1) load
+  // while the query prologue runs, K(2) is staged in registers one step ahead
+  // of its LDS store
+  u32x4 kst[DMA];
+  if (n_cand > 0) {
+    load_k(tile_at(0), k_lds0);
+    load_v(tile_at(0), v_lds0);
+    load_k(tile_at(1), k_lds1);
+    gload_k(tile_at(2), kst);
+  }
 
   // ---- query operand (B of S^T = K Q^T): query row t, dims 16*ks + 8*hf + e ----
   const int32_t t = it.qt * BM + wave * 32 + col;
@@ -569,73 +623,87 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
 #pragma unroll
   for (int i = 0; i < 16; ++i) negref[i] = 0.f;
 
-  if (ci < n_cand) PS_PF_LSTORE(0);
-  __syncthreads();
-  int buf = 0;
-  while (ci < n_cand) {
-    const int32_t kt = cand_tile(ci);
-    const int cur_kind = kind;
-    int32_t cn = ci + 1;
-    int nkind = 0;
-    while (cn < n_cand && (nkind = pf_classify(geo, it.qt, cand_tile(cn))) == 0) ++cn;
-    if (cn < n_cand) PS_PF_GLOAD(cand_tile(cn));  // next tile's loads are in flight during this tile's math
+  // LDS operand addresses (elements): row 32*m + col, logical chunk c -> c ^ swizzle(col)
+  // Byte offsets (inside a tile) of this lane's first K and V^T operand
+  // chunks.  Logical chunk 2s + hf lives at physical chunk (2s + hf) ^ swizzle,
+  // i.e. at byte offset off ^ 32s: the chunk bits sit below the row bits, so
+  // one XOR per k-step addresses every operand; the 32-row M-tiles are
+  // immediate offsets.
+  const uint32_t k_off = (uint32_t)(col * D + (hf ^ chunk_swizzle<KCH>(col)) * 8) * 2;
+  const uint32_t v_off = (uint32_t)(col * BN + (hf ^ chunk_swizzle<VCH>(col)) * 8) * 2;
+  auto frag = [](const uint16_t* buf, uint32_t byte_off) {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(buf) + byte_off);
+  };
 
-    // ---- S^T - ref = K Q^T + (-ref): two 32-key M-tiles; the operands of
-    // k-step ks+1 are read from LDS while the MFMAs of k-step ks run ----
-    f32x16 st[2];
-    {
-      const uint16_t* k0row = &k_lds[buf][col * KPAD + 8 * hf];
-      const uint16_t* k1row = k0row + 32 * KPAD;
-      bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(k0row);
-      bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(k1row);
+  // S^T - ref = K Q^T + (-ref) for the K tile in `kb`: two 32-key M-tiles; the
+  // operands of k-step ks+1 are read while the MFMAs of k-step ks run
+  auto qk = [&](const uint16_t* kb, f32x16* st) {
+    bf16x8 k0 = frag(kb, k_off);
+    bf16x8 k1 = frag(kb, k_off + 64 * D);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 kb0 = ka0, kb1 = ka1;
-        if (ks + 1 < KS) {
-          kb0 = *reinterpret_cast<const bf16x8*>(k0row + 16 * (ks + 1));
-          kb1 = *reinterpret_cast<const bf16x8*>(k1row + 16 * (ks + 1));
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 n0 = k0, n1 = k1;
+      if (ks + 1 < KS) {
+        const uint32_t c = k_off ^ (32 * (ks + 1));
+        n0 = frag(kb, c);
+        n1 = frag(kb, c + 64 * D);
+      }
+      st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], ks == 0 ? negref : st[0], 0, 0, 0);
+      st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], ks == 0 ? negref : st[1], 0, 0, 0);
+      k0 = n0;
+      k1 = n1;
+    }
+  };
+  // element masks of a partly visible tile; key of register i of M-tile m2:
+  // kt*BN + 32*m2 + 8*(i/4) + 4*hf + i%4
+  auto mask = [&](int32_t kt, f32x16* st) {
+    const int32_t kbase = kt * BN + 4 * hf;
+    if (kt * BN >= prefix_len && kt * BN + BN <= num_k) {
+      // chunk keys only, all in range: visible iff 0 <= u - key < W, one unsigned compare
+      const uint32_t rel = (uint32_t)(row_ok ? u - kbase : -1 - a.window);
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t off = 32 * m2 + 8 * (i >> 2) + (i & 3);
+          if (rel - off >= (uint32_t)a.window) st[m2][i] = -INFINITY;
         }
-        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qop[ks], ks == 0 ? negref : st[0], 0, 0, 0);
-        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qop[ks], ks == 0 ? negref : st[1], 0, 0, 0);
-        ka0 = kb0;
-        ka1 = kb1;
-      }
+    } else {
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t key = kbase + 32 * m2 + 8 * (i >> 2) + (i & 3);
+          const bool vis = key < pre_end || (uint32_t)(key - band_lo) <= band_w;
+          if (!vis) st[m2][i] = -INFINITY;
+        }
     }
-    // key of register i of tile m2: kt*BN + 32*m2 + 8*(i/4) + 4*hf + i%4
-    if (cur_kind == 2) {
-      const int32_t kbase = kt * BN + 4 * hf;
-      if (kt * BN >= prefix_len && kt * BN + BN <= num_k) {
-        // chunk keys only, all in range: visible iff 0 <= u - key < W, one unsigned compare
-        const uint32_t rel = (uint32_t)(row_ok ? u - kbase : -1 - a.window);
+  };
+  // row max of a fresh S tile
+  auto tile_max = [&](const f32x16* st) {
+    float m0 = fmaxf(st[0][0], st[1][0]), m1 = fmaxf(st[0][1], st[1][1]);
 #pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t off = 32 * m2 + 8 * (i >> 2) + (i & 3);
-            if (rel - off >= (uint32_t)a.window) st[m2][i] = -INFINITY;
-          }
-      } else {
-#pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int32_t key = kbase + 32 * m2 + 8 * (i >> 2) + (i & 3);
-            const bool vis = key < pre_end || (uint32_t)(key - band_lo) <= band_w;
-            if (!vis) st[m2][i] = -INFINITY;
-          }
-      }
+    for (int i = 2; i < 16; i += 2) {
+      m0 = fmaxf(m0, fmaxf(st[0][i], st[1][i]));
+      m1 = fmaxf(m1, fmaxf(st[0][i + 1], st[1][i + 1]));
     }
-    float mx = st[0][0];
-#pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-      for (int i = (m2 == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, st[m2][i]);
-    mx = max_xor32(mx);
-    // rare path (wave-uniform branch): this tile's max exceeds the reference by
-    // more than kRebase -> move the reference up and rescale what is accumulated
-    if (__any(mx > kRebase)) {
-      const float shift = mx > kRebase ? mx : 0.f;
-      const float alpha = __builtin_amdgcn_exp2f(-shift);
+    return max_xor32(fmaxf(m0, m1));
+  };
+  // the reference moves for a fresh S tile with row max mx (one rare,
+  // wave-uniform branch):
+  //  * the tile's max exceeds the reference by more than kRebase: move the
+  //    reference up to it and rescale what is accumulated;
+  //  * nothing accumulated yet and every score far below the reference: move
+  //    it down so the first probabilities do not underflow (no rescale needed)
+  auto rebase = [&](f32x16* st, float mx) {
+    // per-lane (divergent) branch: both halves of a query column see the same
+    // mx and ltot, so they take the same decision
+    const float ltot = sum_xor32(l_run);
+    const bool up = mx > kRebase;
+    const bool down = !up && mx < -kRebaseLow && ltot == 0.f && mx != -INFINITY;
+    if (up || down) {
+      const float shift = mx;
+      const float alpha = up ? __builtin_amdgcn_exp2f(-shift) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
@@ -644,57 +712,109 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
 #pragma unroll
       for (int m2 = 0; m2 < 2; ++m2) st[m2] -= shift;
     }
-    // nothing accumulated yet and every score far below the reference: move it
-    // down so the first probabilities do not underflow (no rescale needed)
-    if (__any(mx < -kRebaseLow)) {
-      const float ltot = sum_xor32(l_run);
-      const float shift = (ltot == 0.f && mx < -kRebaseLow && mx != -INFINITY) ? mx : 0.f;
-      ref += shift;
-      negref -= shift;
-#pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) st[m2] -= shift;
-    }
+  };
+
+  __syncthreads();
+  f32x16 sa[2], sb[2];   // scores of tiles c0 / c0 + 1, alternating between steps
+  if (n_cand > 0) {
+    qk(k_lds0, sa);
+    if (kind_at(0) == 2) mask(cand_tile(0), sa);
+    rebase(sa, tile_max(sa));
+  }
+  int32_t c0 = 0;
+  // one step of the walk: tile c0 (scores in sc, V in vcur) and tile c0 + 1
+  // (K in knext, scores into sn); the staged K(c0 + 2) goes into kfree, V(c0 + 1)
+  // into vnext
+  auto step = [&](uint16_t* kfree, const uint16_t* knext, const uint16_t* vcur, uint16_t* vnext, f32x16* sc,
+                  f32x16* sn) {
+    lstore(kfree, kst);   // K(c0 + 2); K(c0), its previous content, was consumed last step
+    gload_k(tile_at(c0 + 3), kst);
+    u32x4 vst[DMA];
+    gload_v(tile_at(c0 + 1), vst);
+
+    // Straight-line sections, each fenced against the scheduler: one MFMA
+    // step, the LDS operand reads of the next one, and a share of the vector
+    // work.  QK sections: scores of the next tile (past the last tile its K
+    // buffer holds stale data: computed and discarded) and this tile's
+    // probabilities (bf16 B operand of PV).  PV sections: O^T += V^T P^T (PV
+    // k-step j covers keys 16j + 8*(e/4) + 4*hf + e%4) and the next tile's
+    // row max.
+    constexpr int EPS = 32 / KS;   // probabilities formed per QK section
     bf16x8 pop[4];
-    float psum = 0.f;
+    float ps[2] = {0.f, 0.f};
+    uint32_t ko = k_off, vo = v_off;
+    asm volatile("" : "+v"(ko), "+v"(vo));   // keep the per-step XORs from being hoisted into registers
+    bf16x8 k0 = frag(knext, ko);
+    bf16x8 k1 = frag(knext, ko + 64 * D);
+    bf16x8 va[MT];
 #pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2)
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 n0 = k0, n1 = k1;
+      if (ks + 1 < KS) {
+        const uint32_t c = ko ^ (32 * (ks + 1));
+        n0 = frag(knext, c);
+        n1 = frag(knext, c + 64 * D);
+      }
+      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], ks == 0 ? negref : sn[0], 0, 0, 0);
+      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], ks == 0 ? negref : sn[1], 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(st[m2][i]);
-        psum += p;
+      for (int e = 0; e < EPS; ++e) {
+        const int idx = ks * EPS + e, m2 = idx >> 4, i = idx & 15;
+        const float p = __builtin_amdgcn_exp2f(sc[m2][i]);
+        ps[i & 1] += p;
         pop[2 * m2 + (i >> 3)][i & 7] = (bf16)p;
       }
-    l_run += psum;
-
-    // ---- O^T += V^T P^T: PV k-step j covers keys 16j + 8*(e/4) + 4*hf + e%4;
-    // the V^T operands of step j+1 are read while step j's MFMAs run ----
-    {
-      const uint16_t* vrow = &v_lds[buf][col * VPAD + 8 * hf];
-      bf16x8 va[MT];
+      k0 = n0;
+      k1 = n1;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // the next k-step's operand reads first,
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // then this k-step's MFMAs,
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // then the vector work
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += ps[0] + ps[1];
+    float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) va[mt] = *reinterpret_cast<const bf16x8*>(vrow + 32 * mt * VPAD);
+    for (int mt = 0; mt < MT; ++mt) va[mt] = frag(vcur, vo + 64 * BN * mt);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8 vb[MT];
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 vn[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          vb[mt] = (j + 1 < 4) ? *reinterpret_cast<const bf16x8*>(vrow + 32 * mt * VPAD + 16 * (j + 1)) : va[mt];
+      for (int mt = 0; mt < MT; ++mt)
+        vn[mt] = j + 1 < 4 ? frag(vcur, (vo ^ (32 * (j + 1))) + 64 * BN * mt) : va[mt];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mt], pop[j], acc[mt], 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mt], pop[j], acc[mt], 0, 0, 0);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) va[mt] = vb[mt];
+      for (int e = 0; e < 8; e += 2) {
+        const int idx = 8 * j + e, m2 = idx >> 4, i = idx & 15;
+        mx0 = fmaxf(mx0, sn[m2][i]);
+        mx1 = fmaxf(mx1, sn[m2][i + 1]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) va[mt] = vn[mt];
+      __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("" ::"v"(mx0), "v"(mx1));   // the max is formed in the PV sections above
+    lstore(vnext, vst);   // V of the previous tile, consumed
+    if (c0 + 1 < n_cand) {
+      if (kind_at(c0 + 1) == 2) {
+        mask(cand_tile(c0 + 1), sn);
+        rebase(sn, tile_max(sn));
+      } else {
+        rebase(sn, max_xor32(fmaxf(mx0, mx1)));
       }
     }
-    if (cn < n_cand) PS_PF_LSTORE(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    ci = cn;
-    kind = nkind;
+    lds_barrier();   // this step's LDS stores are visible and its LDS reads done; K(c0 + 3) stays in flight
+    ++c0;
+  };
+  while (c0 < n_cand) {
+    step(k_lds0, k_lds1, v_lds0, v_lds1, sa, sb);
+    if (c0 >= n_cand) break;
+    step(k_lds1, k_lds0, v_lds1, v_lds0, sb, sa);
   }
-
-#undef PS_PF_GLOAD
-#undef PS_PF_LSTORE
 
   // ---- epilogue: l across the two halves, normalise, store ----
   l_run = sum_xor32(l_run);

@@ -129,6 +129,11 @@ def test_prefill_workspace_and_tiles(lib):
     assert need == (2 * 8 * 4 * nkp * 128 * 2 + 255) // 256 * 256 + 8192 * 64 * 2 * 4
     assert lib.ps_prefill_attn(ctypes.byref(a), 2048, 100, 98304, FAKE, FAKE, FAKE, 8, 8192, 8292, FAKE, None,
                                FAKE, need - 1, None) == 3
+    # the bf16 kernel addresses V^T rows with 32-bit offsets: at most 2^28 keys
+    nk = (1 << 28) + 1
+    assert lib.ps_prefill_attn(ctypes.byref(a), 2048, 100, nk - 64, FAKE, FAKE, FAKE, 1, 64, nk, FAKE, None,
+                               FAKE, 1 << 62, None) == 1
+    assert "2^28" in lib.ps_last_error().decode()
 
 
 # ---------------------------------------------------------------- scheduler (host build) vs oracle
