@@ -561,6 +561,52 @@ def run_cpu_baseline(args):
             "cpu_seconds": sum(r[1] for r in res)}
 
 
+def _oracle_prefill_worker(args):
+    """Full query rows of the C4 prefill (W=2048 behind a 100-token prefix)
+    for one slice of rows of each sampled (batch, head) pair."""
+    idx, n_pairs, row0, n_rows = args
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    import synth
+    cfg = synth.C4_PREFILL
+    rows = np.arange(row0, row0 + n_rows)
+    el = 0.0
+    for pair in range(n_pairs):
+        q = synth.round_to(synth.normal((cfg.queries, 1, cfg.dim), 0, 4, 100 + pair, 0), "bf16")
+        k = synth.round_to(synth.normal((cfg.nk, 1, cfg.dim), 0, 4, 200 + pair, 0), "bf16")
+        v = synth.round_to(synth.normal((cfg.nk, 1, cfg.dim), 0, 4, 300 + pair, 0), "bf16")
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            oracle.prefill_attention(q, k, v, cfg.prefix, cfg.window, cfg.kv_start, 1 / math.sqrt(cfg.dim),
+                                     cfg.rope_theta, rows=rows)
+            el += time.perf_counter() - t0
+    pairs = sum(cfg.prefix + min(t + 1, cfg.window) for t in rows) * n_pairs
+    return pairs, el
+
+
+def run_cpu_prefill_baseline(cores):
+    """The oracle on 4 (batch, head) pairs of the C4 prefill, every query row,
+    the rows split evenly over the worker processes."""
+    import concurrent.futures
+    import multiprocessing
+    import synth
+    cfg = synth.C4_PREFILL
+    n_pairs = 4
+    per = -(-cfg.queries // cores)
+    jobs = [(i, n_pairs, i * per, min(per, cfg.queries - i * per)) for i in range(cores) if i * per < cfg.queries]
+    ctx = multiprocessing.get_context("spawn")
+    with concurrent.futures.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
+        res = list(ex.map(_oracle_prefill_worker, jobs))
+    pairs = sum(r[0] for r in res)
+    slowest = max(r[1] for r in res)
+    return {"value": float(4.0 * cfg.dim * pairs / slowest / 1e12), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_pairs} (batch, head) pairs of the 8 x 8192-query prefill (W=2048, prefix 100), all "
+                      f"{cfg.queries} query rows, split over {len(jobs)} worker processes x 1 BLAS thread; "
+                      f"TFLOP/s = 4 D x visible pairs / slowest worker's oracle time",
+            "cpu_seconds": sum(r[1] for r in res)}
+
+
 def load_traffic(kernel_bytes):
     """HBM traffic per launch from the committed counter summary, if it was
     taken on the current kernel source."""
@@ -581,11 +627,15 @@ def main():
                                    "described in DESIGN.md, not implemented)"}))
         sys.exit(2)
     # the CPU oracle's worker processes start before anything initialises the GPU
-    cpu = None
+    cpu = cpu_prefill = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(args)
         print(f"[bench] cpu oracle done: {cpu['value']:.3f} tok/s on {cpu['cores']} cores", file=sys.stderr,
               flush=True)
+        if not args.no_prefill:
+            cpu_prefill = run_cpu_prefill_baseline(cpu["cores"])
+            print(f"[bench] cpu oracle prefill done: {cpu_prefill['value'] * 1e3:.3f} GFLOP/s", file=sys.stderr,
+                  flush=True)
     import torch
     import bounded_kv_cache_amd as ps
     if not torch.cuda.is_available():
@@ -667,6 +717,7 @@ def main():
                      "kernel_launches_timed": dec["kernel_launches"],
                      "bytes_per_launch": dec["kernel_bytes"]},
         "cpu_baseline": cpu,
+        "cpu_baseline_prefill": cpu_prefill,
         "prefill": prefill,
         "prefill_backward": backward,
         "chunk_prefill": chunk,
