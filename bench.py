@@ -297,7 +297,9 @@ def run_decode_extra(ps, torch, layers=28, reps=30):
     """Per-layer decode-kernel time of the other decode workloads (one layer's
     cache each; tok/s assumes `layers` layers of decode attention per token):
     64 sequences at 32768 (W=4096), 256 at 131072 with W=8192, the headline
-    workload with Continue PE and with Reset PE scoring, and the ragged paged
+    workload with Continue PE, with Reset PE scoring and with Reset PE re-rotating
+    every visible key before each call (what the scoring identity avoids; the
+    cache content is immaterial to the cost), and the ragged paged
     batch of 1024 sequences (positions 1024..262144, prefixes 50..2000)."""
     import numpy as np
     import synth
@@ -320,8 +322,12 @@ def run_decode_extra(ps, torch, layers=28, reps=30):
     b = DecodeBench(ps, torch, 256, 1, 4096, 100, 131072, 0, pool=4)
     pos = torch.full((256,), 131072, dtype=torch.int64, device="cuda")
     for mode, key in ((ps.PS_PE_CONTINUE, "decode-131072-w4096-continue-pe"),
-                      (ps.PS_PE_RESET, "decode-131072-w4096-reset-pe")):
+                      (ps.PS_PE_RESET, "decode-131072-w4096-reset-pe"),
+                      (ps.PS_PE_RESET_RECOMPUTE, "decode-131072-w4096-reset-pe-recompute")):
         b.attn = dataclasses.replace(b.attn, pe_mode=mode)
+        if mode == ps.PS_PE_RESET_RECOMPUTE:   # the re-rotated key copy lives in the workspace
+            b.ws = torch.empty(ps.ps_decode_workspace_size(b.attn, b.cache, 256, 0), dtype=torch.uint8,
+                               device="cuda")
         b.decode_only(3, pos)
         t = timed(torch, lambda k: b.decode_only(k, pos), reps) / reps
         out[key] = {"us_per_layer": t * 1e6, "hbm_gbs": b.kernel_bytes(131072) / t / 1e9,

@@ -16,14 +16,14 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import PS_BF16, PS_F32, PS_PE_CONTINUE, PS_PE_RESET, PSError
+from ._lib import PS_BF16, PS_F32, PS_PE_CONTINUE, PS_PE_RESET, PS_PE_RESET_RECOMPUTE, PSError
 
 __all__ = ["AttnSpec", "CacheSpec", "PSError", "ps_kv_append", "ps_decode_attn", "ps_prefill_attn",
            "ps_chunk_prefill_attn", "ps_chunk_prefill_workspace_size", "ps_prefill_attn_backward",
            "ps_prefill_backward_workspace_size", "ps_heavy_decode_step", "ps_heavy_workspace_size", "HeavyState",
            "ps_prefill_plan", "ps_decode_workspace_size", "ps_decode_num_splits", "ps_prefill_workspace_size",
            "ps_prefill_tile_shape", "ps_abi_version", "cache_shapes", "PS_BF16", "PS_F32", "PS_PE_CONTINUE",
-           "PS_PE_RESET"]
+           "PS_PE_RESET", "PS_PE_RESET_RECOMPUTE"]
 
 _TORCH_DTYPE = {PS_BF16: torch.bfloat16, PS_F32: torch.float32}
 
@@ -36,7 +36,7 @@ class AttnSpec:
     dtype: int = PS_BF16
     rope_theta: float = 10000.0
     softmax_scale: Optional[float] = None  # default 1/sqrt(head_dim)
-    pe_mode: int = PS_PE_CONTINUE          # PS_PE_RESET: decode only
+    pe_mode: int = PS_PE_CONTINUE          # PS_PE_RESET / PS_PE_RESET_RECOMPUTE: decode only
 
     def c(self) -> _lib.AttnDesc:
         scale = self.softmax_scale if self.softmax_scale is not None else 1.0 / math.sqrt(self.head_dim)

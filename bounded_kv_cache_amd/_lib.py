@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(HERE, "libprefix_sliding.so")
 
 PS_OK, PS_INVALID_ARGUMENT, PS_UNSUPPORTED, PS_WORKSPACE_TOO_SMALL, PS_HIP_ERROR = range(5)
 PS_BF16, PS_F32 = 0, 1
-PS_PE_CONTINUE, PS_PE_RESET = 0, 1
+PS_PE_CONTINUE, PS_PE_RESET, PS_PE_RESET_RECOMPUTE = 0, 1, 2
 
 
 class AttnDesc(ctypes.Structure):

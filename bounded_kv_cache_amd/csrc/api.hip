@@ -7,6 +7,7 @@
 #include <string>
 
 #include "ps_internal.h"
+#include "ps_reset.h"
 #include "ps_sched.h"
 
 namespace {
@@ -54,8 +55,9 @@ ps_status check_attn(const ps_attn_desc* a) {
   if (!(a->rope_theta >= 0.0) || !isfinite(a->rope_theta))
     return fail(PS_INVALID_ARGUMENT, "rope_theta must be >= 0 and finite");
   if (a->rope_theta > 0.0 && a->rope_theta <= 1.0) return fail(PS_INVALID_ARGUMENT, "rope_theta must exceed 1");
-  if (a->pe_mode != PS_PE_CONTINUE && a->pe_mode != PS_PE_RESET)
-    return fail(PS_INVALID_ARGUMENT, "pe_mode %d (0 Continue PE, 1 Reset PE)", a->pe_mode);
+  if (a->pe_mode != PS_PE_CONTINUE && a->pe_mode != PS_PE_RESET && a->pe_mode != PS_PE_RESET_RECOMPUTE)
+    return fail(PS_INVALID_ARGUMENT, "pe_mode %d (0 Continue PE, 1 Reset PE, 2 Reset PE re-rotating keys)",
+                a->pe_mode);
   return PS_OK;
 }
 
@@ -138,6 +140,22 @@ size_t decode_ws_bytes(const ps_attn_desc* a, int32_t num_seqs, int32_t splits) 
   if (splits <= 1) return 0;
   const size_t rows = (size_t)num_seqs * a->num_q_heads * splits;
   return rows * a->head_dim * sizeof(float) + rows * 2 * sizeof(float);
+}
+
+// Reset PE re-rotating keys: after the split partials (256-aligned), the
+// renumbered query positions, the cos/sin table and the rotated key copy.
+struct RecomputeLayout {
+  size_t pos, table, keys, total;
+};
+RecomputeLayout recompute_layout(const ps_attn_desc* a, const ps_cache_desc* c, int32_t num_seqs, int32_t splits) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  RecomputeLayout l;
+  l.pos = al(decode_ws_bytes(a, num_seqs, splits));
+  l.table = l.pos + al((size_t)num_seqs * sizeof(int64_t));
+  const size_t elem = a->dtype == PS_BF16 ? 2 : 4;
+  l.keys = l.table + al((size_t)c->slot_capacity * (a->head_dim / 2) * 2 * elem);   // fp16 / fp32 (cos, sin)
+  l.total = l.keys + al((size_t)num_seqs * a->num_kv_heads * c->slot_capacity * a->head_dim * elem);
+  return l;
 }
 
 ps_status check_prefill_geom(int32_t window, int32_t prefix_len, int64_t kv_start, int32_t batch, int32_t num_q,
@@ -254,6 +272,7 @@ ps_status ps_kv_append(const ps_attn_desc* attn, const ps_cache_desc* cache, voi
   a.num_seqs = num_seqs;
   a.slot_pos = slot_pos;
   a.rope = make_rope(attn);
+  if (attn->pe_mode == PS_PE_RESET_RECOMPUTE) a.rope.enabled = 0;   // keys are rotated at every read
   return from_hip(ps::launch_append(a, stream), "ps_kv_append launch");
 }
 
@@ -266,6 +285,7 @@ size_t ps_decode_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* c
                                 int32_t num_splits) {
   if (check_attn(attn) != PS_OK || !cache || cache->slot_capacity <= 0 || num_seqs < 0 || num_splits < 0) return 0;
   const int32_t s = num_splits > 0 ? num_splits : auto_splits(attn, cache, num_seqs, device_cu_count());
+  if (attn->pe_mode == PS_PE_RESET_RECOMPUTE) return recompute_layout(attn, cache, num_seqs, s).total;
   return decode_ws_bytes(attn, num_seqs, s);
 }
 
@@ -285,7 +305,11 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, c
   const int32_t splits = num_splits > 0 ? num_splits : auto_splits(attn, cache, num_seqs, device_cu_count());
   if (splits > 1024 || splits > cache->slot_capacity / 32)
     return fail(PS_INVALID_ARGUMENT, "num_splits %d too large for slot_capacity %d", splits, cache->slot_capacity);
-  const size_t need = decode_ws_bytes(attn, num_seqs, splits);
+  const bool recompute = attn->pe_mode == PS_PE_RESET_RECOMPUTE;
+  if (recompute && cache->page_size != 0)
+    return fail(PS_UNSUPPORTED, "pe_mode 2 (Reset PE re-rotating keys) needs a contiguous cache");
+  const size_t need = recompute ? recompute_layout(attn, cache, num_seqs, splits).total
+                                : decode_ws_bytes(attn, num_seqs, splits);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PS_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
   ps::DecodeArgs a;
@@ -314,6 +338,26 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, c
   a.heavy_slots = 0;
   a.stat_scores = nullptr;
   a.stat_lse2 = nullptr;
+  if (recompute) {   // rotate the visible keys at their renumbered positions, then decode the copy
+    const RecomputeLayout l = recompute_layout(attn, cache, num_seqs, splits);
+    char* w = static_cast<char*>(workspace);
+    ps::ResetArgs r;
+    r.geom = a.geom;
+    r.dtype = attn->dtype;
+    r.num_seqs = num_seqs;
+    r.k_cache = k_cache;
+    r.prefix_len = prefix_len;
+    r.pos = pos;
+    r.rope = a.rope;
+    r.table = w + l.table;
+    r.k_out = w + l.keys;
+    r.pos_out = reinterpret_cast<int64_t*>(w + l.pos);
+    const ps_status rs = from_hip(ps::launch_reset_rerotate(r, stream), "ps_decode_attn key rotation launch");
+    if (rs != PS_OK) return rs;
+    a.k_cache = r.k_out;
+    a.pos = r.pos_out;
+    a.reset_pe = 0;
+  }
   return from_hip(ps::launch_decode(a, stream), "ps_decode_attn launch");
 }
 

@@ -17,12 +17,14 @@ __host__ __device__ inline int32_t vt_slot(int32_t k) {
   return (k & ~15) | (((kl >> 2) & 1) << 3) | ((kl >> 3) << 2) | (kl & 3);
 }
 
-// n contiguous elements <-> floats, 16-byte loads / stores
-template <typename T>
+// n contiguous elements <-> floats, 16-byte loads / stores (kNT: non-temporal,
+// for data streamed once that should not displace cached data)
+template <typename T, bool kNT = false>
 __device__ inline void load_vec(const T* p, float* x, int n) {
   constexpr int E = 16 / sizeof(T);
   for (int c = 0; c < n; c += E) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(p + c);
+    const u32x4 w = kNT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + c))
+                        : *reinterpret_cast<const u32x4*>(p + c);
     if (sizeof(T) == 2) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -35,7 +37,7 @@ __device__ inline void load_vec(const T* p, float* x, int n) {
     }
   }
 }
-template <typename T>
+template <typename T, bool kNT = false>
 __device__ inline void store_vec(T* p, const float* x, int n) {
   constexpr int E = 16 / sizeof(T);
   for (int c = 0; c < n; c += E) {
@@ -47,7 +49,10 @@ __device__ inline void store_vec(T* p, const float* x, int n) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(x[c + e]);
     }
-    *reinterpret_cast<u32x4*>(p + c) = w;
+    if (kNT)
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p + c));
+    else
+      *reinterpret_cast<u32x4*>(p + c) = w;
   }
 }
 

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 5
+#define PS_ABI_VERSION 6
 
 typedef enum {
   PS_OK = 0,
@@ -95,7 +95,15 @@ typedef enum { PS_BF16 = 0, PS_F32 = 1 } ps_dtype;
  * leaves their rotary offsets unchanged -- so window keys are scored as under
  * Continue PE and only the prefix keys are scored against the query rotated at
  * its renumbered position (no key is re-rotated). */
-typedef enum { PS_PE_CONTINUE = 0, PS_PE_RESET = 1 } ps_pe_mode;
+/* PS_PE_RESET_RECOMPUTE computes the same Reset-PE attention the way the blog
+ * describes its cost: ps_kv_append stores K un-rotated, and every
+ * ps_decode_attn call first rotates each visible key at its renumbered
+ * position (prefix slot j keeps j; the window token at absolute position n
+ * becomes L + n - max(L, p - W + 1)) into a scratch copy in the workspace,
+ * then runs the ordinary decode with the query at min(p, L + W - 1).
+ * Contiguous caches only; decode only (other entry points return
+ * PS_UNSUPPORTED).  It exists to measure what PS_PE_RESET avoids. */
+typedef enum { PS_PE_CONTINUE = 0, PS_PE_RESET = 1, PS_PE_RESET_RECOMPUTE = 2 } ps_pe_mode;
 
 /* Attention geometry.
  * num_q_heads % num_kv_heads == 0; query head h uses KV head
@@ -142,7 +150,8 @@ typedef struct {
  * Within one call a token at position j is written only if j < L or
  * j > p_last - W (p_last = the sequence's last position in the call): tokens
  * that the same call would already evict are skipped, so no two writes of a
- * call hit the same slot.  tokens_per_seq == 0 or num_seqs == 0 is a no-op. */
+ * call hit the same slot.  tokens_per_seq == 0 or num_seqs == 0 is a no-op.
+ * With pe_mode PS_PE_RESET_RECOMPUTE the keys are stored un-rotated. */
 ps_status ps_kv_append(const ps_attn_desc* attn, const ps_cache_desc* cache,
                        void* k_cache, void* v_cache, const int32_t* block_table,
                        const int32_t* prefix_len, const int64_t* start_pos,
@@ -176,7 +185,9 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache,
  * invalid arguments. */
 int32_t ps_decode_num_splits(const ps_attn_desc* attn, const ps_cache_desc* cache, int32_t num_seqs);
 
-/* Workspace bytes ps_decode_attn needs (num_splits 0: automatic). */
+/* Workspace bytes ps_decode_attn needs (num_splits 0: automatic).  With
+ * pe_mode PS_PE_RESET_RECOMPUTE this includes the rotated copy of the keys
+ * (num_seqs * Hkv * slot_capacity * head_dim elements) and a cos/sin table. */
 size_t ps_decode_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* cache,
                                 int32_t num_seqs, int32_t num_splits);
 

@@ -1,8 +1,10 @@
-"""GPU parity of Reset-PE decode (ps_decode_attn with pe_mode = PS_PE_RESET)
-against oracle.decode_attention_reset_pe, through the C ABI.  The cache is
-filled exactly as for Continue PE; only the scoring of prefix slots changes.
+"""GPU parity of Reset-PE decode against oracle.decode_attention_reset_pe,
+through the C ABI, in both implementations: pe_mode PS_PE_RESET (cache filled
+exactly as for Continue PE; only the scoring of prefix slots changes) and
+PS_PE_RESET_RECOMPUTE (keys cached un-rotated and re-rotated at their
+renumbered positions before every decode call; contiguous caches only).
 Prefix lengths that are not multiples of 32 put the prefix end inside a key
-chunk (scored with both query rotations)."""
+chunk (scored with both query rotations in the first mode)."""
 import math
 
 import numpy as np
@@ -29,10 +31,18 @@ def _hist(seed, cfg_id, seq, n, hkv, d, std, dtype):
             synth.history(seed, cfg_id, synth.T_V, seq, 0, 0, n, hkv, d, std, dtype))
 
 
+MODES = ["reset", "recompute"]
+
+
+def _mode(ps, name):
+    return ps.PS_PE_RESET if name == "reset" else ps.PS_PE_RESET_RECOMPUTE
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("splits", [1, 3])
-def test_reset_pe_tiny_fp32_autoregressive(ps, splits):
+def test_reset_pe_tiny_fp32_autoregressive(ps, splits, mode):
     c = synth.C1_DECODE
-    attn = ps.AttnSpec(c.hq, c.hkv, c.dim, ps.PS_F32, c.rope_theta, 1 / math.sqrt(c.dim), pe_mode=ps.PS_PE_RESET)
+    attn = ps.AttnSpec(c.hq, c.hkv, c.dim, ps.PS_F32, c.rope_theta, 1 / math.sqrt(c.dim), pe_mode=_mode(ps, mode))
     cache = ps.CacheSpec(window=c.window, slot_capacity=128)
     steps = 400
     k, v = _hist(0, c.cfg_id, 0, steps, c.hkv, c.dim, c.kv_std, "f32")
@@ -67,14 +77,17 @@ CASES = [  # (prefix, window, query positions)
 ]
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("case", range(len(CASES)))
-def test_reset_pe_bf16_small(ps, case, paged):
+def test_reset_pe_bf16_small(ps, case, paged, mode):
+    if paged and mode == "recompute":
+        pytest.skip("the re-rotating mode takes contiguous caches only (PS_UNSUPPORTED, checked on the host)")
     L, W, positions = CASES[case]
     hq, hkv, d = 16, 2, 128
     n = len(positions)
     cap = -(-(L + W) // 64) * 64
-    attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16, 10000.0, 1 / math.sqrt(d), pe_mode=ps.PS_PE_RESET)
+    attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16, 10000.0, 1 / math.sqrt(d), pe_mode=_mode(ps, mode))
     bt, num_pages = (None, 0)
     if paged:
         bt, num_pages = paged_table(n, cap // 64, seed=case)

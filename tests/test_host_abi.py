@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ps_abi_version() == 5
+    assert lib.ps_abi_version() == 6
     assert lib.ps_status_string(0) == b"ok"
     assert lib.ps_status_string(3) == b"workspace too small"
 
@@ -55,7 +55,7 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails val
     (dict(hq=15), 1), (dict(hkv=0), 1), (dict(hq=34, hkv=2), 2), (dict(d=96), 2), (dict(dtype=7), 2),
     (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(theta=-1.0), 1), (dict(theta=0.5), 1),
     (dict(window=0), 1), (dict(page=32), 2), (dict(cap=100), 1), (dict(page=64, cap=4224, mp=10, npages=5), 1),
-    (dict(page=64, cap=4224, mp=66, npages=0), 1), (dict(pe=2), 1), (dict(pe=-1), 1),
+    (dict(page=64, cap=4224, mp=66, npages=0), 1), (dict(pe=3), 1), (dict(pe=-1), 1),
 ])
 def test_decode_validation(lib, mut, status):
     a, c = _descs(**mut)
@@ -245,8 +245,9 @@ def test_backward_validation_and_workspace(lib):
     assert call(nq=0) == 0
 
 
-def test_reset_pe_is_decode_only(lib):
-    a, c = _descs(pe=1)
+@pytest.mark.parametrize("pe", [1, 2])
+def test_reset_pe_is_decode_only(lib, pe):
+    a, c = _descs(pe=pe)
     # prefill, backward and chunk prefill reject Reset PE before looking at anything else
     assert lib.ps_prefill_attn(ctypes.byref(a), 64, 0, 0, FAKE, FAKE, FAKE, 1, 64, 64, FAKE, None, FAKE, 1 << 30,
                                None) == 2
@@ -255,9 +256,28 @@ def test_reset_pe_is_decode_only(lib):
     assert lib.ps_chunk_prefill_attn(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, 16, FAKE, FAKE,
                                      FAKE, 1, FAKE, None, None, FAKE, 1 << 30, None) == 2
     assert b"Continue PE" in lib.ps_last_error()
+    assert lib.ps_heavy_decode_step(ctypes.byref(a), ctypes.byref(c), 8, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, 4, FAKE, FAKE, FAKE, 1, FAKE, 1 << 30, None) == 2
     # decode accepts it (fails later only on the NULL cache pointer)
     assert lib.ps_decode_attn(ctypes.byref(a), ctypes.byref(c), None, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 1,
                               None, 0, None) == 1
+
+
+def test_reset_pe_recompute_workspace_and_layout(lib):
+    al = lambda x: (x + 255) // 256 * 256
+    for dtype, elem in ((0, 2), (1, 4)):
+        a, c = _descs(pe=2, dtype=dtype, cap=4224)
+        for splits, part in ((1, 0), (3, 4 * 16 * 3 * (128 + 2) * 4)):
+            need = lib.ps_decode_workspace_size(ctypes.byref(a), ctypes.byref(c), 4, splits)
+            assert need == al(part) + al(4 * 8) + al(4224 * 64 * 2 * elem) + al(4 * 2 * 4224 * 128 * elem)
+            # too small a workspace is reported before anything runs
+            assert lib.ps_decode_attn(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4,
+                                      splits, FAKE, need - 1, None) == 3
+    # contiguous caches only
+    a, c = _descs(pe=2, page=64, mp=66, npages=1000)
+    assert lib.ps_decode_attn(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1,
+                              FAKE, 1 << 40, None) == 2
+    assert b"contiguous" in lib.ps_last_error()
 
 
 def test_heavy_decode_validation_and_workspace(lib):
