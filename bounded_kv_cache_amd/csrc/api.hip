@@ -190,8 +190,8 @@ size_t chunk_nkp(const ps_cache_desc* c, int32_t chunk_len) {
 size_t chunk_ws_bytes(const ps_attn_desc* a, const ps_cache_desc* c, int32_t num_seqs, int32_t chunk_len) {
   const size_t elem = a->dtype == PS_BF16 ? 2 : 4;
   const size_t kv = 2 * (size_t)num_seqs * a->num_kv_heads * chunk_nkp(c, chunk_len) * a->head_dim * elem;
-  const size_t qr = (size_t)num_seqs * chunk_len * a->num_q_heads * a->head_dim * elem;
-  return ((kv + 255) / 256) * 256 + ((qr + 255) / 256) * 256;
+  const size_t cs = (size_t)num_seqs * chunk_len * (a->head_dim / 2) * 2 * sizeof(float);   // query cos/sin
+  return ((kv + 255) / 256) * 256 + ((cs + 255) / 256) * 256;
 }
 
 // Backward workspace layout (each piece 256-byte aligned).
@@ -535,7 +535,6 @@ ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t pref
   a.v_cache = nullptr;
   a.block_table = nullptr;
   a.cg = ps::CacheGeom{};
-  a.q_rot = nullptr;
   return from_hip(ps::launch_prefill(a, stream), "ps_prefill_attn launch");
 }
 
@@ -659,7 +658,7 @@ ps_status ps_chunk_prefill_attn(const ps_attn_desc* attn, const ps_cache_desc* c
   a.out = out;
   a.lse = lse;
   a.k_rot = workspace;
-  a.rope_cs = nullptr;
+  a.rope_cs = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((kv + 255) / 256) * 256);
   a.scale_log2 = attn->softmax_scale * 1.4426950408889634f;
   a.rope = make_rope(attn);
   a.nkp = (int32_t)nkp;
@@ -669,7 +668,6 @@ ps_status ps_chunk_prefill_attn(const ps_attn_desc* attn, const ps_cache_desc* c
   a.v_cache = v_cache;
   a.block_table = block_table;
   a.cg = make_geom(attn, cache);
-  a.q_rot = static_cast<char*>(workspace) + ((kv + 255) / 256) * 256;
   hipError_t e = ps::launch_chunk_prefill(a, stream);
   if (e != hipSuccess) return from_hip(e, "ps_chunk_prefill_attn launch");
   // the chunk joins the ring only after every chunk query has read the ring

@@ -310,23 +310,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a) {
       __syncthreads();
     }
   }
-  // chunk queries: rotated at P + t, scaled; one thread per (sequence, query, pair)
+  // cos/sin of every chunk query position P + t (one row per sequence and query)
   const int64_t pairs = (int64_t)a.batch * a.num_q * HALF;
-  const T* q = static_cast<const T*>(a.q);
-  T* qr = static_cast<T*>(a.q_rot);
   for (int64_t idx = blockIdx.x * 256ll + tid; idx < pairs; idx += (int64_t)gridDim.x * 256) {
     const int32_t i = (int32_t)(idx % HALF);
     const int64_t bt = idx / HALF;          // b * T + t
-    const int32_t b = (int32_t)(bt / a.num_q);
-    const int64_t P = a.seq_start[b];
+    const int64_t P = a.seq_start[bt / a.num_q];
     float c = 1.f, sn = 0.f;
     if (a.rope.enabled && P >= 0) rope_cos_sin(P + bt % a.num_q, a.rope.inv_freq[i], c, sn);
-    for (int32_t h = 0; h < a.hq; ++h) {
-      const int64_t row = (bt * a.hq + h) * D;
-      const float x1 = Elem<T>::load(q + row + i), x2 = Elem<T>::load(q + row + i + HALF);
-      Elem<T>::store(qr + row + i, (x1 * c - x2 * sn) * a.scale_log2);
-      Elem<T>::store(qr + row + i + HALF, (x2 * c + x1 * sn) * a.scale_log2);
-    }
+    a.rope_cs[idx * 2 + 0] = c;
+    a.rope_cs[idx * 2 + 1] = sn;
   }
 }
 
@@ -360,13 +353,11 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   const float* kr = static_cast<const float*>(a.k_rot) + ((int64_t)it.b * a.hkv + kvh) * nkp * D;
   const float* vt = static_cast<const float*>(a.k_rot) + (int64_t)a.batch * a.hkv * nkp * D +
                     ((int64_t)it.b * a.hkv + kvh) * D * nkp;
-  if (row_ok && kPerSeq) {   // rotated and scaled by the chunk prep
-    const float* qrow = static_cast<const float*>(a.q_rot) + (((int64_t)it.b * a.num_q + t) * a.hq + it.hq) * D;
-    for (int d = 0; d < D; ++d) qs[tid][d] = qrow[d];
-  } else if (row_ok) {
+  if (row_ok) {
     const float* qrow = q + (((int64_t)it.b * a.num_q + t) * a.hq + it.hq) * D;
+    const float* cs = a.rope_cs + ((kPerSeq ? (int64_t)it.b * a.num_q : 0) + t) * (D / 2) * 2;
     for (int i = 0; i < D / 2; ++i) {
-      const float c = a.rope_cs[((int64_t)t * (D / 2) + i) * 2], s = a.rope_cs[((int64_t)t * (D / 2) + i) * 2 + 1];
+      const float c = cs[2 * i], s = cs[2 * i + 1];
       const float x1 = qrow[i], x2 = qrow[i + D / 2];
       qs[tid][i] = (x1 * c - x2 * s) * a.scale_log2;
       qs[tid][i + D / 2] = (x2 * c + x1 * s) * a.scale_log2;
@@ -563,15 +554,7 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
   const bool row_ok = t < a.num_q;
   const int32_t u = num_k - a.num_q + t;  // key index of this lane's query
   bf16x8 qop[KS];
-  if (kPerSeq) {   // rotated and scaled by the chunk prep
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q_rot) +
-                           (((int64_t)it.b * a.num_q + (row_ok ? t : 0)) * a.hq + it.hq) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qop[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hf);
-      if (!row_ok) qop[ks] = bf16x8{};
-    }
-  } else {
+  {
     float qv[KS][8];
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            (((int64_t)it.b * a.num_q + (row_ok ? t : 0)) * a.hq + it.hq) * D;
@@ -585,7 +568,9 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
         qv[ks][2 * e + 1] = hi_bf16(ww[e]);
       }
     }
-    const float* cs = a.rope_cs + (int64_t)(row_ok ? t : 0) * (D / 2) * 2;
+    // cos/sin of the query position: one table row per query (uniform
+    // geometry) or per (sequence, query) (chunks continuing a ring)
+    const float* cs = a.rope_cs + ((kPerSeq ? (int64_t)it.b * a.num_q : 0) + (row_ok ? t : 0)) * (D / 2) * 2;
 #pragma unroll
     for (int ks = 0; ks < KS / 2; ++ks) {
 #pragma unroll

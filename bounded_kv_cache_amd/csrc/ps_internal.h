@@ -84,7 +84,7 @@ struct PrefillArgs {
   void* out;
   float* lse;
   void* k_rot;            // workspace: rotated keys [batch][num_k][hkv][D]
-  float* rope_cs;         // workspace: [num_q][D/2][2] cos/sin of query positions
+  float* rope_cs;         // workspace: [num_q][D/2][2] cos/sin of query positions (chunks: [batch][num_q][D/2][2])
   float scale_log2;
   RopeFreq rope;
   int32_t nkp;            // key stride of the K / V^T copies (multiple of 64)
@@ -95,7 +95,6 @@ struct PrefillArgs {
   const void* v_cache;
   const int32_t* block_table;
   CacheGeom cg;
-  void* q_rot;            // workspace: rotated, scaled queries [batch][num_q][hq][D]
 };
 
 // Backward of the masked prefill (dq, dk, dv for the raw inputs).

@@ -198,10 +198,10 @@ def test_chunk_prefill_validation_and_workspace(lib):
     nkp = (4224 + T + 63) // 64 * 64
     align = lambda x: (x + 255) // 256 * 256
     need = lib.ps_chunk_prefill_workspace_size(ctypes.byref(a), ctypes.byref(c), S, T)
-    assert need == align(2 * S * 2 * nkp * 128 * 2) + align(S * T * 16 * 128 * 2)
+    assert need == align(2 * S * 2 * nkp * 128 * 2) + align(S * T * 64 * 2 * 4)
     a32, _ = _descs(dtype=1)
     assert lib.ps_chunk_prefill_workspace_size(ctypes.byref(a32), ctypes.byref(c), S, T) == \
-        align(2 * S * 2 * nkp * 128 * 4) + align(S * T * 16 * 128 * 4)
+        align(2 * S * 2 * nkp * 128 * 4) + align(S * T * 64 * 2 * 4)
 
     def call(attn=a, cache=c, kc=FAKE, q=FAKE, chunk=T, seqs=S, ws=FAKE, wsb=need, bt=None):
         return lib.ps_chunk_prefill_attn(ctypes.byref(attn), ctypes.byref(cache), kc, FAKE, bt, FAKE, FAKE, chunk,
