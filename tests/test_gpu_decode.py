@@ -134,6 +134,49 @@ def test_bf16_decode_small(ps, case, paged):
             assert err <= BF16_TOL, (splits, s, positions[s], err)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_large_score_swings(ps, dtype):
+    """Softmax maxima that move by over a hundred log2 units (power-of-two
+    scalings, exact in bf16; no rotation, so alignments hold at every
+    position): the pinned keys are 8 k0, even sequences query with -k0
+    (pinned scores about -90 natural units, then ordinary window scores) and
+    odd ones with -k0 / 16 (about -6 against window scores near 0); W = 1 in
+    the second geometry (prefix + self)."""
+    hq, hkv, d = 16, 2, 128
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16 if dtype == "bf16" else ps.PS_F32, 0.0, 1 / math.sqrt(d))
+    for L, W, positions in ((40, 300, [45, 339, 340, 2000, 5000, 77]), (40, 1, [39, 40, 41, 900])):
+        n = len(positions)
+        cap = -(-(L + W) // 64) * 64
+        cache = ps.CacheSpec(window=W, slot_capacity=cap)
+        kc, vc = new_cache(ps, attn, cache, n)
+        hist = []
+        for s_ in range(n):
+            k, v = _hist(6, 120 + W, s_, positions[s_] + 1, hkv, d, 1.0, dtype)
+            k0 = k[:1, :1, :].copy()
+            k[:L] = 8.0 * k0
+            hist.append((k, v, k0))
+        fill_ring(ps, attn, cache, kc, vc, [L] * n, [p - 1 for p in positions], [h[0] for h in hist],
+                  [h[1] for h in hist])
+        kn = np.stack([h[0][p] for h, p in zip(hist, positions)])[:, None]
+        vn = np.stack([h[1][p] for h, p in zip(hist, positions)])[:, None]
+        pl = torch.full((n,), L, dtype=torch.int32, device="cuda")
+        pos = torch.tensor(positions, dtype=torch.int64, device="cuda")
+        ps.ps_kv_append(attn, cache, kc, vc, pl, pos, to_dev(kn, dt), to_dev(vn, dt))
+        q = np.stack([-hist[s_][2][0] * (1.0 if s_ % 2 == 0 else 1.0 / 16.0) for s_ in range(n)])
+        q = np.broadcast_to(q, (n, hq, d)).copy()
+        qd = to_dev(q, dt)
+        for splits in sorted({sp for sp in (1, 2, 3, 0) if sp <= cap // 32}):
+            out = torch.empty((n, hq, d), dtype=dt, device="cuda")
+            ps.ps_decode_attn(attn, cache, kc, vc, pl, pos, qd, out, num_splits=splits)
+            got = out.float().cpu().numpy()
+            for s_ in range(n):
+                want = oracle.decode_attention(q[s_], hist[s_][0], hist[s_][1], positions[s_], L, W,
+                                               1 / math.sqrt(d), 0.0)
+                err = normwise_err(got[s_], want)
+                assert err <= (BF16_TOL if dtype == "bf16" else F32_TOL), (W, splits, s_, positions[s_], err)
+
+
 def test_bf16_decode_deterministic(ps):
     L, W, hq, hkv, d, n = 7, 300, 16, 2, 128, 5
     positions = [0, 100, 306, 307, 5000]

@@ -52,9 +52,10 @@ def test_plan_bit_exact(ps, dtype):
             (W, L, start, T, nk)
 
 
-def _prefill_case(ps, dtype, batch, hq, hkv, d, L, W, start, chunk, T, seed, rows=None, tol=None):
+def _prefill_case(ps, dtype, batch, hq, hkv, d, L, W, start, chunk, T, seed, rows=None, tol=None, theta=10000.0,
+                  transform=None):
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16 if dtype == "bf16" else ps.PS_F32, 10000.0, 1 / math.sqrt(d))
+    attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16 if dtype == "bf16" else ps.PS_F32, theta, 1 / math.sqrt(d))
     nk = L + chunk
     qs, ks, vs = [], [], []
     for b in range(batch):
@@ -62,6 +63,8 @@ def _prefill_case(ps, dtype, batch, hq, hkv, d, L, W, start, chunk, T, seed, row
         ks.append(synth.history(seed, 40, synth.T_K, b, 0, 0, nk, hkv, d, 1.0, dtype))
         vs.append(synth.history(seed, 40, synth.T_V, b, 0, 0, nk, hkv, d, 1.0, dtype))
     q, k, v = np.stack(qs), np.stack(ks), np.stack(vs)
+    if transform is not None:
+        q, k, v = transform(q, k, v)
     out = torch.empty((batch, T, hq, d), dtype=dt, device="cuda")
     lse = torch.empty((batch, hq, T), dtype=torch.float32, device="cuda")
     ps.ps_prefill_attn(attn, W, L, start, to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), out, lse=lse)
@@ -69,7 +72,7 @@ def _prefill_case(ps, dtype, batch, hq, hkv, d, L, W, start, chunk, T, seed, row
     got_lse = lse.cpu().numpy()
     tol = tol if tol is not None else (BF16_TOL if dtype == "bf16" else F32_TOL)
     for b in range(batch):
-        want, want_lse = oracle.prefill_attention(q[b], k[b], v[b], L, W, start, 1 / math.sqrt(d), 10000.0,
+        want, want_lse = oracle.prefill_attention(q[b], k[b], v[b], L, W, start, 1 / math.sqrt(d), theta,
                                                   rows=rows)
         sel = got[b] if rows is None else got[b][rows]
         err = normwise_err(sel, want)
@@ -101,3 +104,29 @@ def test_bf16_prefill_small(ps, args):
 ])
 def test_fp32_prefill_small(ps, args):
     _prefill_case(ps, "f32", *args, seed=2)
+
+
+def _score_swings(L):
+    """Reference moves of the softmax (power-of-two scalings, exact in bf16;
+    no rotation, so the alignments hold at every position).  Every pinned key
+    is 8 k0.  Even query rows are -k0: their pinned scores are about -90
+    natural units (-130 in log2), so the kernel's reference must move down
+    before anything is accumulated, and the window keys' ordinary scores then
+    move it up by ~130 log2 units, rescaling the pinned contributions already
+    accumulated.  Odd rows are -k0 / 16: pinned scores about -6 against
+    window scores near 0 (a mix with no reference move).  The scores that
+    carry weight stay O(1), within the dtype's ordinary accuracy."""
+    def tf(q, k, v):
+        q, k = q.copy(), k.copy()
+        k0 = k[:, :1, :1, :].copy()
+        k[:, :L] = 8.0 * k0
+        q[:, 0::2] = -k0
+        q[:, 1::2] = -k0 / 16.0
+        return q, k, v
+    return tf
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_large_score_swings(ps, dtype):
+    L, W, start, chunk, T = 40, 300, 1000, 700, 700
+    _prefill_case(ps, dtype, 1, 4, 2, 128, L, W, start, chunk, T, seed=5, theta=0.0, transform=_score_swings(L))
