@@ -269,6 +269,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   for (int ks = 0; ks < KS; ++ks) {
     kop[ks] = *reinterpret_cast<const bf16x8*>(kr + (int64_t)kw * D + 16 * ks + 8 * hf);
     vop[ks] = *reinterpret_cast<const bf16x8*>(vr + (int64_t)kw * D + 16 * ks + 8 * hf);
+    // keep them in registers: left as plain loads of read-only memory, the
+    // compiler re-issues them inside the loop and waits on them every step
+    asm volatile("" : "+v"(kop[ks]), "+v"(vop[ks]));
   }
 
   // query blocks that can see the tile: from the first query at or after k0 to
@@ -531,6 +534,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
     for (int ks = 0; ks < KS; ++ks) {
       qop[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hf);
       dop[ks] = *reinterpret_cast<const bf16x8*>(drow + 16 * ks + 8 * hf);
+      asm volatile("" : "+v"(qop[ks]), "+v"(dop[ks]));   // registers, not re-issued loads
     }
   }
   const float lse2 = row_ok ? a.lse2[bh * a.tqp + t] : INFINITY;
