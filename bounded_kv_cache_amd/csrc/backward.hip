@@ -482,43 +482,67 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
   const uint16_t* vr = static_cast<const uint16_t*>(a.vr) + bkv * a.nkp * D;
   const uint16_t* ktr = static_cast<const uint16_t*>(a.krt) + bkv * D * a.nkp;
 
-  u32x4 kreg[RP], vreg[RP], treg[TP];
-#define PS_BQ_GLOAD(KT)                                                                              \
-  do {                                                                                              \
-    _Pragma("unroll") for (int pc_ = 0; pc_ < RP; ++pc_) {                                          \
-      const int piece_ = tid + 256 * pc_;                                                           \
-      const int64_t o_ = ((int64_t)(KT) * BN + piece_ / (D / 8)) * D + (piece_ % (D / 8)) * 8;     \
-      kreg[pc_] = *reinterpret_cast<const u32x4*>(kr + o_);                                         \
-      vreg[pc_] = *reinterpret_cast<const u32x4*>(vr + o_);                                         \
-    }                                                                                               \
-    _Pragma("unroll") for (int pc_ = 0; pc_ < TP; ++pc_) {                                          \
-      const int piece_ = tid + 256 * pc_;                                                           \
-      treg[pc_] = *reinterpret_cast<const u32x4*>(ktr + (int64_t)(piece_ / (BN / 8)) * a.nkp +     \
-                                                  (int64_t)(KT) * BN + (piece_ % (BN / 8)) * 8);    \
-    }                                                                                               \
-  } while (0)
-#define PS_BQ_LSTORE(BUF)                                                                            \
-  do {                                                                                              \
-    _Pragma("unroll") for (int pc_ = 0; pc_ < RP; ++pc_) {                                          \
-      const int piece_ = tid + 256 * pc_;                                                           \
-      const int o_ = (piece_ / (D / 8)) * KPAD + (piece_ % (D / 8)) * 8;                            \
-      *reinterpret_cast<u32x4*>(&k_lds[BUF][o_]) = kreg[pc_];                                       \
-      *reinterpret_cast<u32x4*>(&v_lds[BUF][o_]) = vreg[pc_];                                       \
-    }                                                                                               \
-    _Pragma("unroll") for (int pc_ = 0; pc_ < TP; ++pc_) {                                          \
-      const int piece_ = tid + 256 * pc_;                                                           \
-      *reinterpret_cast<u32x4*>(&t_lds[BUF][(piece_ / (BN / 8)) * TPAD + (piece_ % (BN / 8)) * 8]) = \
-          treg[pc_];                                                                                \
-    }                                                                                               \
-  } while (0)
+  // staging: K' and V rows (row-major) and the d-major K' copy, 16-byte pieces
+  auto gload_kv = [&](int32_t kt, u32x4* kreg, u32x4* vreg) {
+#pragma unroll
+    for (int pc = 0; pc < RP; ++pc) {
+      const int piece = tid + 256 * pc;
+      const int64_t o = ((int64_t)kt * BN + piece / (D / 8)) * D + (piece % (D / 8)) * 8;
+      kreg[pc] = *reinterpret_cast<const u32x4*>(kr + o);
+      vreg[pc] = *reinterpret_cast<const u32x4*>(vr + o);
+    }
+  };
+  auto gload_t = [&](int32_t kt, u32x4* treg) {
+#pragma unroll
+    for (int pc = 0; pc < TP; ++pc) {
+      const int piece = tid + 256 * pc;
+      treg[pc] = *reinterpret_cast<const u32x4*>(ktr + (int64_t)(piece / (BN / 8)) * a.nkp + (int64_t)kt * BN +
+                                                  (piece % (BN / 8)) * 8);
+    }
+  };
+  auto lstore_kv = [&](int b_, const u32x4* kreg, const u32x4* vreg) {
+#pragma unroll
+    for (int pc = 0; pc < RP; ++pc) {
+      const int piece = tid + 256 * pc;
+      const int o = (piece / (D / 8)) * KPAD + (piece % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&k_lds[b_][o]) = kreg[pc];
+      *reinterpret_cast<u32x4*>(&v_lds[b_][o]) = vreg[pc];
+    }
+  };
+  auto lstore_t = [&](int b_, const u32x4* treg) {
+#pragma unroll
+    for (int pc = 0; pc < TP; ++pc) {
+      const int piece = tid + 256 * pc;
+      *reinterpret_cast<u32x4*>(&t_lds[b_][(piece / (BN / 8)) * TPAD + (piece % (BN / 8)) * 8]) = treg[pc];
+    }
+  };
 
   const TileRange tr = pf_tile_range(geo, qt);
   const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
   auto cand_tile = [&](int32_t ci) { return ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix); };
-  int32_t ci = 0;
-  int kind = 0;
-  while (ci < n_cand && (kind = pf_classify(geo, qt, cand_tile(ci))) == 0) ++ci;
-  if (ci < n_cand) PS_BQ_GLOAD(cand_tile(ci));
+  auto next_live = [&](int32_t ci, int& kind) {   // first candidate >= ci that is not skipped
+    kind = 0;
+#pragma clang loop vectorize(disable) interleave(disable) unroll(disable)
+    while (ci < n_cand && (kind = pf_classify(geo, qt, cand_tile(ci))) == 0) ++ci;
+    return ci;
+  };
+  // tiles c0 (j) and c1 (j+1) of the walk
+  int kind0 = 0, kind1 = 0;
+  int32_t c0 = next_live(0, kind0);
+  int32_t c1 = c0 < n_cand ? next_live(c0 + 1, kind1) : n_cand;
+  {
+    u32x4 kreg[RP], vreg[RP], treg[TP];
+    if (c0 < n_cand) {
+      gload_kv(cand_tile(c0), kreg, vreg);
+      gload_t(cand_tile(c0), treg);
+      lstore_kv(0, kreg, vreg);
+      lstore_t(0, treg);
+    }
+    if (c1 < n_cand) {
+      gload_kv(cand_tile(c1), kreg, vreg);
+      lstore_kv(1, kreg, vreg);
+    }
+  }
 
   // this lane's query: B operands of S^T = K' Q''^T and dP^T = V dO^T
   const int32_t t = qt * BM + wave * 32 + col;
@@ -552,65 +576,134 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
-  f32x16 zero;
+  // initial value of the S^T accumulators: the MFMAs then yield s - lse2
+  f32x16 neg_lse2, zero;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) zero[i] = 0.f;
+  for (int i = 0; i < 16; ++i) {
+    neg_lse2[i] = -lse2;
+    zero[i] = 0.f;
+  }
 
-  if (ci < n_cand) PS_BQ_LSTORE(0);
-  __syncthreads();
-  int buf = 0;
-  while (ci < n_cand) {
-    const int32_t kt = cand_tile(ci);
-    const int cur_kind = kind;
-    int32_t cn = ci + 1;
-    int nkind = 0;
-    while (cn < n_cand && (nkind = pf_classify(geo, qt, cand_tile(cn))) == 0) ++cn;
-    if (cn < n_cand) PS_BQ_GLOAD(cand_tile(cn));
-
-    f32x16 st[2], dpt[2];
-#pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-      const uint16_t* krow = &k_lds[buf][(32 * m2 + col) * KPAD + 8 * hf];
-      const uint16_t* vrow = &v_lds[buf][(32 * m2 + col) * KPAD + 8 * hf];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + 16 * ks);
-        st[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[ks], ks == 0 ? zero : st[m2], 0, 0, 0);
-        dpt[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dop[ks], ks == 0 ? zero : dpt[m2], 0, 0, 0);
-      }
-    }
-    // register i of tile m2 <-> key kt*BN + 32*m2 + 8*(i/4) + 4*hf + i%4
-    bf16x8 sb[4];
+  // register i of tile m2 <-> key kt*BN + 32*m2 + 8*(i/4) + 4*hf + i%4; keys
+  // a partly visible tile hides get S - lse2 = -inf, so their P and dS are zero
+  auto mask = [&](int32_t kt, f32x16* st) {
     const int32_t kbase = kt * BN + 4 * hf;
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = __builtin_amdgcn_exp2f(st[m2][i] - lse2);
-        if (cur_kind == 2) {
-          const int32_t key = kbase + 32 * m2 + 8 * (i >> 2) + (i & 3);
-          const bool vis = key < pre_end || (uint32_t)(key - band_lo) <= band_w;
-          if (!vis) p = 0.f;
-        }
-        sb[2 * m2 + (i >> 3)][i & 7] = (bf16)(p * (dpt[m2][i] - di));
+        const int32_t key = kbase + 32 * m2 + 8 * (i >> 2) + (i & 3);
+        const bool vis = key < pre_end || (uint32_t)(key - band_lo) <= band_w;
+        if (!vis) st[m2][i] = -INFINITY;
       }
-    // dQ''^T += K'^T dS^T: k-step j covers keys 16j + 8*(e/4) + 4*hf + e%4
+  };
+  // S^T and dP^T of the K'/V tile in buffer b_ (not pipelined: the first tile)
+  auto sdp = [&](int b_, f32x16* st, f32x16* dpt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int m2 = 0; m2 < 2; ++m2) {
+      const uint16_t* krow = &k_lds[b_][(32 * m2 + col) * KPAD + 8 * hf];
+      const uint16_t* vrow = &v_lds[b_][(32 * m2 + col) * KPAD + 8 * hf];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&t_lds[buf][(32 * mt + col) * TPAD + 16 * j + 8 * hf]);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, sb[j], acc[mt], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + 16 * ks);
+        st[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[ks], ks == 0 ? neg_lse2 : st[m2], 0, 0, 0);
+        dpt[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dop[ks], ks == 0 ? zero : dpt[m2], 0, 0, 0);
       }
-    if (cn < n_cand) PS_BQ_LSTORE(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    ci = cn;
-    kind = nkind;
+    }
+  };
+
+  __syncthreads();
+  f32x16 sa[2], pa[2], sb_[2], pb[2];   // S^T, dP^T of tiles c0 / c1, alternating between steps
+  if (c0 < n_cand) {
+    sdp(0, sa, pa);
+    if (kind0 == 2) mask(cand_tile(c0), sa);
   }
-#undef PS_BQ_GLOAD
-#undef PS_BQ_LSTORE
+  // One step, software-pipelined inside the wave (one wave per SIMD, so the
+  // wave's own matrix and vector work must overlap): the S^T / dP^T products
+  // of tile c1 run while tile c0's dS is formed, then dQ^T += K'^T dS^T for
+  // tile c0.  K'/V of c1 sit in kv buffer kvb ^ 1, K'^T of c0 in t buffer tb;
+  // the next tiles' data are staged in registers and stored after the LDS
+  // reads of the step.
+  int kvb = 0, tb = 0;
+  auto step = [&](f32x16* sc, f32x16* pc, f32x16* sn, f32x16* pn) {
+    int kind2 = 0;
+    const int32_t c2 = c1 < n_cand ? next_live(c1 + 1, kind2) : n_cand;
+    u32x4 kreg[RP], vreg[RP], treg[TP];
+    if (c2 < n_cand) gload_kv(cand_tile(c2), kreg, vreg);
+    if (c1 < n_cand) gload_t(cand_tile(c1), treg);
+
+    // sections: one k-step of the four S^T / dP^T products of tile c1 (its
+    // operands read one k-step ahead) and a quarter-eighth of tile c0's dS
+    constexpr int EPS = 32 / KS;
+    bf16x8 sbv[4];
+    const uint16_t* krow = &k_lds[kvb ^ 1][col * KPAD + 8 * hf];
+    const uint16_t* vrow = &v_lds[kvb ^ 1][col * KPAD + 8 * hf];
+    bf16x8 k0 = *reinterpret_cast<const bf16x8*>(krow), k1 = *reinterpret_cast<const bf16x8*>(krow + 32 * KPAD);
+    bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vrow), v1 = *reinterpret_cast<const bf16x8*>(vrow + 32 * KPAD);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 nk0 = k0, nk1 = k1, nv0 = v0, nv1 = v1;
+      if (ks + 1 < KS) {
+        nk0 = *reinterpret_cast<const bf16x8*>(krow + 16 * (ks + 1));
+        nk1 = *reinterpret_cast<const bf16x8*>(krow + 32 * KPAD + 16 * (ks + 1));
+        nv0 = *reinterpret_cast<const bf16x8*>(vrow + 16 * (ks + 1));
+        nv1 = *reinterpret_cast<const bf16x8*>(vrow + 32 * KPAD + 16 * (ks + 1));
+      }
+      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], ks == 0 ? neg_lse2 : sn[0], 0, 0, 0);
+      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], ks == 0 ? neg_lse2 : sn[1], 0, 0, 0);
+      pn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, dop[ks], ks == 0 ? zero : pn[0], 0, 0, 0);
+      pn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, dop[ks], ks == 0 ? zero : pn[1], 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) {
+        const int idx = ks * EPS + e, m2 = idx >> 4, i = idx & 15;
+        sbv[2 * m2 + (i >> 3)][i & 7] = (bf16)(__builtin_amdgcn_exp2f(sc[m2][i]) * (pc[m2][i] - di));
+      }
+      k0 = nk0;
+      k1 = nk1;
+      v0 = nv0;
+      v1 = nv1;
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // the next k-step's operand reads,
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // this k-step's MFMAs,
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // the vector work
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dQ''^T += K'^T dS^T for tile c0: k-step j covers keys 16j + 8*(e/4) + 4*hf + e%4
+    {
+      const uint16_t* trow = &t_lds[tb][col * TPAD + 8 * hf];
+      bf16x8 ta[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) ta[mt] = *reinterpret_cast<const bf16x8*>(trow + 32 * mt * TPAD);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 tn[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          tn[mt] = j + 1 < 4 ? *reinterpret_cast<const bf16x8*>(trow + 32 * mt * TPAD + 16 * (j + 1)) : ta[mt];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[mt], sbv[j], acc[mt], 0, 0, 0);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) ta[mt] = tn[mt];
+        __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (__builtin_expect(c1 < n_cand && kind1 == 2, 0)) mask(cand_tile(c1), sn);   // partial tiles are few
+    if (c2 < n_cand) lstore_kv(kvb, kreg, vreg);   // K'/V of c0, its previous content, were consumed last step
+    if (c1 < n_cand) lstore_t(tb ^ 1, treg);       // K'^T of the tile before c0, consumed last step
+    __syncthreads();
+    kvb ^= 1;
+    tb ^= 1;
+    c0 = c1;
+    c1 = c2;
+    kind1 = kind2;
+  };
+  while (c0 < n_cand) {
+    step(sa, pa, sb_, pb);
+    if (c0 >= n_cand) break;
+    step(sb_, pb, sa, pa);
+  }
 
   if (!row_ok) return;
   // dQ' = scale * acc, rotated back by -position
