@@ -357,10 +357,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     if (nx < n_it) PS_BW_GLOAD(kvh * a.group + nx / n_qb, qb_lo + nx % n_qb);
     (void)h;
 
-    // S = Q'' K'^T and dP = dO V^T: two 32-query M-tiles
+    // S = Q'' K'^T and dP = dO V^T (two 32-query M-tiles), then
+    // dV^T += dO^T P and dK^T += Q''^T dS over the block's 64 queries.  One
+    // wave per SIMD, so the wave overlaps its own matrix and vector work:
+    // M-tile 1's products run while M-tile 0's P and dS are formed, and the
+    // first half of the dV / dK k-steps (queries of M-tile 0) runs while
+    // M-tile 1's are formed.  Register r of tile m2 <-> query
+    // 32*m2 + 8*(r/4) + 4*hf + r%4 of the block; PV k-step j covers queries
+    // 16j + 8*(e/4) + 4*hf + e%4 (M-tile j/2).
     f32x16 s[2], dp[2];
-#pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
+    bf16x8 pb[4], sb[4];
+    auto products = [&](int m2) {
       const uint16_t* qrow = &q_lds[buf][(32 * m2 + col) * RPAD + 8 * hf];
       const uint16_t* orow = &o_lds[buf][(32 * m2 + col) * RPAD + 8 * hf];
 #pragma unroll
@@ -370,11 +377,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
         s[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[ks], ks == 0 ? zero : s[m2], 0, 0, 0);
         dp[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vop[ks], ks == 0 ? zero : dp[m2], 0, 0, 0);
       }
-    }
-    // register r of tile m2 <-> query 32*m2 + 8*(r/4) + 4*hf + r%4 of the block
-    bf16x8 pb[4], sb[4];
-#pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2)
+    };
+    auto softmax_ds = [&](int m2) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int ql = 32 * m2 + 8 * r4 + 4 * hf;
@@ -383,19 +387,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          float p = __builtin_amdgcn_exp2f(s[m2][r] - l4[e]);
-          if (cur_kind == 2) {
-            const int32_t u = off + qb * BQ + ql + e;
-            if (!pf_visible(cg, u, kw) || kw >= a.num_k) p = 0.f;
-          }
+          const float p = __builtin_amdgcn_exp2f(s[m2][r] - l4[e]);
           const float ds = p * (dp[m2][r] - d4[e]);
           pb[2 * m2 + (r >> 3)][r & 7] = (bf16)p;
           sb[2 * m2 + (r >> 3)][r & 7] = (bf16)ds;
         }
       }
-    // dV^T += dO^T P and dK^T += Q''^T dS over the block's 64 queries (4 k-steps)
+    };
+    // a partly visible block: queries that do not see this lane's key get S = -inf
+    auto mask = [&](int m2) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int r = 0; r < 16; ++r) {
+        const int32_t uq = off + qb * BQ + 32 * m2 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (!pf_visible(cg, uq, kw) || kw >= a.num_k) s[m2][r] = -INFINITY;
+      }
+    };
+    auto dvdk = [&](int j) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&ot_lds[buf][(32 * mt + col) * TPAD + 16 * j + 8 * hf]);
@@ -403,6 +410,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
         dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pb[j], dv[mt], 0, 0, 0);
         dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb[j], dk[mt], 0, 0, 0);
       }
+    };
+    const bool partial = __builtin_expect(cur_kind == 2, 0);   // partly visible blocks are few
+    products(0);
+    if (partial) mask(0);
+    __builtin_amdgcn_sched_barrier(0);
+    products(1);
+    softmax_ds(0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {   // each MFMA with an operand read and a share of the vector work
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (partial) mask(1);
+    __builtin_amdgcn_sched_barrier(0);
+    dvdk(0);
+    dvdk(1);
+    softmax_ds(1);
+#pragma unroll
+    for (int i = 0; i < 4 * MT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dvdk(2);
+    dvdk(3);
     if (nx < n_it) PS_BW_LSTORE(buf ^ 1);
     __syncthreads();
     buf ^= 1;
