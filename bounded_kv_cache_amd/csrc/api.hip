@@ -142,6 +142,23 @@ size_t decode_ws_bytes(const ps_attn_desc* a, int32_t num_seqs, int32_t splits) 
   return rows * a->head_dim * sizeof(float) + rows * 2 * sizeof(float);
 }
 
+// Heavy-hitter step: after the split partials (256-aligned), the per-slot
+// statistics (fp16 s - m for bf16, fp32 s for fp32), the bf16 path's per-chunk
+// maxima and each row's log2-sum-exp2.
+struct HeavyLayout {
+  size_t scores, max, lse2, total;
+};
+HeavyLayout heavy_layout(const ps_attn_desc* a, const ps_cache_desc* c, int32_t num_seqs, int32_t splits) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const bool bf16 = a->dtype == PS_BF16;
+  HeavyLayout l;
+  l.scores = al(decode_ws_bytes(a, num_seqs, splits));
+  l.max = l.scores + al((size_t)num_seqs * a->num_q_heads * c->slot_capacity * (bf16 ? 2 : 4));
+  l.lse2 = l.max + (bf16 ? al((size_t)num_seqs * a->num_q_heads * (c->slot_capacity / 32) * sizeof(float)) : 0);
+  l.total = l.lse2 + al((size_t)num_seqs * a->num_q_heads * sizeof(float));
+  return l;
+}
+
 // Reset PE re-rotating keys: after the split partials (256-aligned), the
 // renumbered query positions, the cos/sin table and the rotated key copy.
 struct RecomputeLayout {
@@ -337,6 +354,7 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, c
   a.heavy_count = nullptr;
   a.heavy_slots = 0;
   a.stat_scores = nullptr;
+  a.stat_max = nullptr;
   a.stat_lse2 = nullptr;
   if (recompute) {   // rotate the visible keys at their renumbered positions, then decode the copy
     const RecomputeLayout l = recompute_layout(attn, cache, num_seqs, splits);
@@ -365,10 +383,7 @@ size_t ps_heavy_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* ca
                                int32_t num_splits) {
   if (check_attn(attn) != PS_OK || !cache || cache->slot_capacity <= 0 || num_seqs < 0 || num_splits < 0) return 0;
   const int32_t sp = num_splits > 0 ? num_splits : auto_splits(attn, cache, num_seqs, device_cu_count());
-  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  return al(decode_ws_bytes(attn, num_seqs, sp)) +
-         al((size_t)num_seqs * attn->num_q_heads * cache->slot_capacity * sizeof(float)) +
-         al((size_t)num_seqs * attn->num_q_heads * sizeof(float));
+  return heavy_layout(attn, cache, num_seqs, sp).total;
 }
 
 ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* cache, int32_t heavy_slots,
@@ -398,12 +413,11 @@ ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* ca
   const size_t need = ps_heavy_workspace_size(attn, cache, num_seqs, splits);
   if (!workspace || workspace_bytes < need)
     return fail(PS_WORKSPACE_TOO_SMALL, "heavy decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
-  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   char* w = static_cast<char*>(workspace);
-  const size_t part = al(decode_ws_bytes(attn, num_seqs, splits));
-  float* stat_scores = reinterpret_cast<float*>(w + part);
-  float* stat_lse2 = reinterpret_cast<float*>(w + part +
-                                              al((size_t)num_seqs * attn->num_q_heads * cache->slot_capacity * 4));
+  const HeavyLayout hl = heavy_layout(attn, cache, num_seqs, splits);
+  void* stat_scores = w + hl.scores;
+  float* stat_max = attn->dtype == PS_BF16 ? reinterpret_cast<float*>(w + hl.max) : nullptr;
+  float* stat_lse2 = reinterpret_cast<float*>(w + hl.lse2);
   const ps::CacheGeom geom = make_geom(attn, cache);
   const ps::RopeFreq rope = make_rope(attn);
   ps::HeavyArgs h;
@@ -422,6 +436,7 @@ ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* ca
   h.heavy_count = heavy_count;
   h.heavy_pos = heavy_pos;
   h.stat_scores = stat_scores;
+  h.stat_max = stat_max;
   h.stat_lse2 = stat_lse2;
   hipError_t e = ps::launch_heavy_retire(h, stream);   // 1. the token leaving the window
   if (e != hipSuccess) return from_hip(e, "ps_heavy_decode_step retire launch");
@@ -465,6 +480,7 @@ ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* ca
   a.heavy_count = heavy_count;
   a.heavy_slots = heavy_slots;
   a.stat_scores = stat_scores;
+  a.stat_max = stat_max;
   a.stat_lse2 = stat_lse2;
   if ((e = ps::launch_decode(a, stream)) != hipSuccess) return from_hip(e, "ps_heavy_decode_step decode launch");
   return from_hip(ps::launch_heavy_accumulate(h, stream), "ps_heavy_decode_step accumulate launch");  // 4.

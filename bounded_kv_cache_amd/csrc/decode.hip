@@ -110,10 +110,17 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
-  // heavy-hitter statistics: the group's score rows of this (sequence, KV head)
+  // heavy-hitter statistics of this (sequence, KV head), chunk-major so that a
+  // chunk's rows land as whole cache lines: [chunk][head of the group][32 keys]
+  // fp16 s - m, and [chunk][head] fp32 m, the running max after that chunk
+  const int nch = geo.slot_capacity / 32;
   const __amdgpu_buffer_rsrc_t stat_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      kStats ? a.stat_scores + ((int64_t)s * geo.hkv + h) * a.group * geo.slot_capacity : nullptr, (short)0,
-      kStats ? a.group * geo.slot_capacity * 4 : 0, 0x00020000);
+      kStats ? static_cast<uint16_t*>(a.stat_scores) + ((int64_t)s * geo.hkv + h) * a.group * geo.slot_capacity
+             : nullptr,
+      (short)0, kStats ? a.group * geo.slot_capacity * 2 : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t max_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      kStats ? a.stat_max + ((int64_t)s * geo.hkv + h) * a.group * nch : nullptr, (short)0,
+      kStats ? a.group * nch * 4 : 0, 0x00020000);
 
   // chunk index list of this wave: first chunk kb/32 + wave, stride NW
   const int c_end = (ke + 31) >> 5;   // chunks touching [kb, ke)
@@ -181,6 +188,23 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
     }
   };
 
+  // statistics of the last computed chunk, awaiting their store
+  u32x4 st_x = {0u, 0u, 0u, 0u};
+  float st_m = 0.f;
+  int st_ci = -1;
+  auto store_stats = [&]() {
+    // every lane issues the same two stores (no branch, so the load pipeline's
+    // wait counts stay exact); lanes of padding heads, for the max all but lane
+    // group 0, and everything before the first chunk aim past the buffer range
+    // and the hardware drops them.  Chunks never cross a split boundary, so the
+    // -inf of a final partial chunk only lands in slots past the visible range.
+    const bool live = st_ci >= 0 && r < a.group;
+    const int xoff = (live ? (st_ci * a.group + r) * 32 + 8 * g : a.group * geo.slot_capacity) * 2;
+    __builtin_amdgcn_raw_buffer_store_b128(st_x, stat_rsrc, xoff, 0, 0);
+    const int moff = (live && g == 0 ? st_ci * a.group + r : a.group * nch) * 4;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, st_m), max_rsrc, moff, 0, 0);
+  };
+
   auto compute_chunk = [&](int ci, u32x4 (&kr)[2][NC], u32x4 (&vr)[NDT]) {
     f32x4 st0, st1;
     const int key0 = (ci << 5) + 8 * g;
@@ -219,18 +243,6 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
         }
       }
     }
-    if (kStats) {
-      // scores of this lane's head for the heavy-hitter statistics: every lane
-      // issues the same two stores (no branch, so the load pipeline's wait
-      // counts stay exact); lanes of padding heads aim past the buffer range and
-      // the hardware drops them.  Chunks never cross a split boundary, so the
-      // -inf of a final partial chunk only lands in slots past the visible range.
-      const int voff = (r < a.group ? r * geo.slot_capacity + key0 : a.group * geo.slot_capacity) * 4;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{sv[0], sv[1], sv[2], sv[3]}), stat_rsrc,
-                                             voff, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{sv[4], sv[5], sv[6], sv[7]}), stat_rsrc,
-                                             voff + 16, 0, 0);
-    }
     float mx = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
@@ -239,12 +251,23 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-    float pv[8];
+    float pv[8], xv[8];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
+      xv[i] = sv[i] - m_new;
+      pv[i] = __builtin_amdgcn_exp2f(xv[i]);
       psum += pv[i];
+    }
+    if (kStats) {
+      // heavy-hitter statistics, stored with the next chunk's loads (a store
+      // issued amid the math would hold the wave until the memory pipeline
+      // takes it).  fp16 keeps s - m to 2^-11 near 0, where the mass is.
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st_x[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xv[2 * i], xv[2 * i + 1]));
+      st_m = m_new;
+      st_ci = ci;
     }
     l_run = l_run * alpha + psum;
     if (__any(alpha != 1.f)) {
@@ -310,14 +333,17 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
   }
 
   while (c < c_end) {
+    if (kStats) store_stats();
     if (c + NW < c_end) load_chunk(c + NW, kB, vB);
     compute_chunk(c, kA, vA);
     c += NW;
     if (c >= c_end) break;
+    if (kStats) store_stats();
     if (c + NW < c_end) load_chunk(c + NW, kA, vA);
     compute_chunk(c, kB, vB);
     c += NW;
   }
+  if (kStats) store_stats();
 
   // ---- finish the wave: sum the lane-local partial sums of each head ----
   l_run = sum_xor16(l_run);
@@ -469,7 +495,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
       for (int d = 0; d < D; ++d) sc += qv[d] * ks[j][d];
       ps_[n][j] = (t0 + j < ke) ? sc : -INFINITY;
       if (a.stat_scores && t0 + j < ke)
-        a.stat_scores[(((int64_t)s * geo.hkv + h) * G + n) * geo.slot_capacity + t0 + j] = sc;
+        static_cast<float*>(a.stat_scores)[(((int64_t)s * geo.hkv + h) * G + n) * geo.slot_capacity + t0 + j] = sc;
     }
     __syncthreads();
     if (tid < G) {

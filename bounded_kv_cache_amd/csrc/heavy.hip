@@ -92,6 +92,7 @@ __global__ __launch_bounds__(64) void heavy_retire_kernel(HeavyArgs a) {
 }
 
 // score[j] += sum over the group's query heads of exp2(s_j - lse2), j in [L, n_vis)
+// (bf16 path: s_j = (s_j - m) + m from the fp16 slot value and its chunk's max)
 __global__ __launch_bounds__(256) void heavy_accumulate_kernel(HeavyArgs a) {
   const CacheGeom& g = a.geom;
   const int32_t h = (int32_t)(blockIdx.x % g.hkv);
@@ -106,11 +107,41 @@ __global__ __launch_bounds__(256) void heavy_accumulate_kernel(HeavyArgs a) {
   float lse2[kMaxGroup];
   for (int n = 0; n < a.group; ++n) lse2[n] = a.stat_lse2[(int64_t)s * a.hq + h * a.group + n];
   float* score = a.score + sh * g.slot_capacity;
-  const float* st = a.stat_scores + sh * a.group * g.slot_capacity;
-  for (int64_t j = L + threadIdx.x; j < nvis; j += 256) {
-    float m = 0.f;
-    for (int n = 0; n < a.group; ++n) m += __builtin_amdgcn_exp2f(st[(int64_t)n * g.slot_capacity + j] - lse2[n]);
-    score[j] += m;
+  if (a.stat_max) {   // bf16 path: fp16 s - m per slot, m per 32-key chunk, chunk-major
+    // 8 consecutive slots per thread (16-byte loads of each head's row; the
+    // capacity is a multiple of 64, so a group never crosses a chunk or the end)
+    const _Float16* st = static_cast<const _Float16*>(a.stat_scores) + sh * a.group * g.slot_capacity;
+    const float* mx = a.stat_max + sh * a.group * (g.slot_capacity / 32);
+    for (int64_t j0 = (L & ~7) + 8 * threadIdx.x; j0 < nvis; j0 += 8 * 256) {
+      const int64_t c = j0 >> 5;
+      float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < a.group; ++n) {
+        const uint4 w = *reinterpret_cast<const uint4*>(st + (c * a.group + n) * 32 + (j0 & 31));
+        const float off = mx[c * a.group + n] - lse2[n];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const auto x = __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), ww[e]);
+          m[2 * e] += __builtin_amdgcn_exp2f((float)x[0] + off);
+          m[2 * e + 1] += __builtin_amdgcn_exp2f((float)x[1] + off);
+        }
+      }
+      float4* sp = reinterpret_cast<float4*>(score + j0);
+      float4 s0 = sp[0], s1 = sp[1];
+      float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (j0 + i >= L && j0 + i < nvis) sv[i] += m[i];
+      sp[0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      sp[1] = make_float4(sv[4], sv[5], sv[6], sv[7]);
+    }
+  } else {            // fp32 path: the scores themselves
+    const float* st = static_cast<const float*>(a.stat_scores) + sh * a.group * g.slot_capacity;
+    for (int64_t j = L + threadIdx.x; j < nvis; j += 256) {
+      float m = 0.f;
+      for (int n = 0; n < a.group; ++n) m += __builtin_amdgcn_exp2f(st[(int64_t)n * g.slot_capacity + j] - lse2[n]);
+      score[j] += m;
+    }
   }
 }
 

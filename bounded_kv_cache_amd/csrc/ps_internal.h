@@ -48,7 +48,11 @@ struct DecodeArgs {
   // heavy-hitter mode (NULL / 0 otherwise): visible slots are [0, min(p+1, L+W) + heavy_count)
   const int32_t* heavy_count;  // [num_seqs][hkv]
   int32_t heavy_slots;         // H: heavy slots after the window, L + W + H <= slot_capacity
-  float* stat_scores;          // [num_seqs][hkv][group][slot_capacity] scores (log2 units) of the visible slots
+  // per visible slot and head, in log2 units: bf16 path, [num_seqs][hkv][slot_capacity / 32][group][32]
+  // fp16 s - m with m the running max after the slot's 32-key chunk (in stat_max); fp32 path,
+  // [num_seqs][hkv][group][slot_capacity] the score s itself
+  void* stat_scores;
+  float* stat_max;             // bf16 path: [num_seqs][hkv][slot_capacity / 32][group]; else NULL
   float* stat_lse2;            // [num_seqs][hq] log2-sum-exp2 of each query row
 };
 
@@ -67,7 +71,8 @@ struct HeavyArgs {
   float* score;                // [num_seqs][hkv][slot_capacity] accumulated attention per slot
   int32_t* heavy_count;        // [num_seqs][hkv]
   int64_t* heavy_pos;          // [num_seqs][hkv][heavy_slots]
-  const float* stat_scores;
+  const void* stat_scores;     // as DecodeArgs
+  const float* stat_max;
   const float* stat_lse2;
 };
 

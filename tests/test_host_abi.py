@@ -284,9 +284,15 @@ def test_heavy_decode_validation_and_workspace(lib):
     a, c = _descs(cap=4352)
     need = lib.ps_heavy_workspace_size(ctypes.byref(a), ctypes.byref(c), 4, 1)
     al = lambda x: (x + 255) // 256 * 256
-    assert need == al(0) + al(4 * 16 * 4352 * 4) + al(4 * 16 * 4)
+    # bf16: fp16 s - m per slot and head, one fp32 max per 32-slot chunk, the row sums
+    stats = al(4 * 16 * 4352 * 2) + al(4 * 16 * (4352 // 32) * 4) + al(4 * 16 * 4)
+    assert need == al(0) + stats
     need3 = lib.ps_heavy_workspace_size(ctypes.byref(a), ctypes.byref(c), 4, 3)
-    assert need3 == al(4 * 16 * 3 * (128 + 2) * 4) + al(4 * 16 * 4352 * 4) + al(4 * 16 * 4)
+    assert need3 == al(4 * 16 * 3 * (128 + 2) * 4) + stats
+    # fp32: the scores themselves, no maxima
+    a32, c32 = _descs(cap=4352, dtype=1)
+    assert lib.ps_heavy_workspace_size(ctypes.byref(a32), ctypes.byref(c32), 4, 1) == \
+        al(4 * 16 * 4352 * 4) + al(4 * 16 * 4)
 
     def call(attn=a, cache=c, H=128, score=FAKE, hpos=FAKE, ws=FAKE, wsb=need, splits=1, seqs=4):
         return lib.ps_heavy_decode_step(ctypes.byref(attn), ctypes.byref(cache), H, FAKE, FAKE, None, FAKE, FAKE,
