@@ -142,9 +142,16 @@ size_t decode_ws_bytes(const ps_attn_desc* a, int32_t num_seqs, int32_t splits) 
   return rows * a->head_dim * sizeof(float) + rows * 2 * sizeof(float);
 }
 
+// Heavy-hitter step in bf16 with one split: when a sequence's statistics fit
+// in LDS the decode kernel keeps them there and accumulates the scores itself.
+bool heavy_fused(const ps_attn_desc* a, const ps_cache_desc* c, int32_t splits) {
+  return a->dtype == PS_BF16 && splits == 1 &&
+         ps::fused_stats_bytes(c->slot_capacity, a->num_q_heads / a->num_kv_heads) <= (size_t)ps::kFusedStatsLds;
+}
+
 // Heavy-hitter step: after the split partials (256-aligned), the per-slot
 // statistics (fp16 s - m for bf16, fp32 s for fp32), the bf16 path's per-chunk
-// maxima and each row's log2-sum-exp2.
+// maxima and each row's log2-sum-exp2; nothing for the fused step.
 struct HeavyLayout {
   size_t scores, max, lse2, total;
 };
@@ -153,6 +160,10 @@ HeavyLayout heavy_layout(const ps_attn_desc* a, const ps_cache_desc* c, int32_t 
   const bool bf16 = a->dtype == PS_BF16;
   HeavyLayout l;
   l.scores = al(decode_ws_bytes(a, num_seqs, splits));
+  if (heavy_fused(a, c, splits)) {
+    l.max = l.lse2 = l.total = l.scores;
+    return l;
+  }
   l.max = l.scores + al((size_t)num_seqs * a->num_q_heads * c->slot_capacity * (bf16 ? 2 : 4));
   l.lse2 = l.max + (bf16 ? al((size_t)num_seqs * a->num_q_heads * (c->slot_capacity / 32) * sizeof(float)) : 0);
   l.total = l.lse2 + al((size_t)num_seqs * a->num_q_heads * sizeof(float));
@@ -352,6 +363,7 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, c
   a.rope = make_rope(attn);
   a.reset_pe = attn->pe_mode == PS_PE_RESET ? 1 : 0;
   a.heavy_count = nullptr;
+  a.heavy_score = nullptr;
   a.heavy_slots = 0;
   a.stat_scores = nullptr;
   a.stat_max = nullptr;
@@ -411,7 +423,7 @@ ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* ca
   if (splits > 1024 || splits > cache->slot_capacity / 32)
     return fail(PS_INVALID_ARGUMENT, "num_splits %d too large for slot_capacity %d", splits, cache->slot_capacity);
   const size_t need = ps_heavy_workspace_size(attn, cache, num_seqs, splits);
-  if (!workspace || workspace_bytes < need)
+  if ((need > 0 && !workspace) || workspace_bytes < need)
     return fail(PS_WORKSPACE_TOO_SMALL, "heavy decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
   char* w = static_cast<char*>(workspace);
   const HeavyLayout hl = heavy_layout(attn, cache, num_seqs, splits);
@@ -479,10 +491,13 @@ ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* ca
   a.reset_pe = 0;
   a.heavy_count = heavy_count;
   a.heavy_slots = heavy_slots;
-  a.stat_scores = stat_scores;
-  a.stat_max = stat_max;
-  a.stat_lse2 = stat_lse2;
+  const bool fused = heavy_fused(attn, cache, splits);
+  a.stat_scores = fused ? nullptr : stat_scores;
+  a.stat_max = fused ? nullptr : stat_max;
+  a.stat_lse2 = fused ? nullptr : stat_lse2;
+  a.heavy_score = fused ? score : nullptr;   // fused: the decode kernel also does step 4
   if ((e = ps::launch_decode(a, stream)) != hipSuccess) return from_hip(e, "ps_heavy_decode_step decode launch");
+  if (fused) return ok();
   return from_hip(ps::launch_heavy_accumulate(h, stream), "ps_heavy_decode_step accumulate launch");  // 4.
 }
 

@@ -57,8 +57,11 @@ __device__ inline u32x4 stream_load(const uint16_t* p) {
 // ---------------------------------------------------------------------------
 // bf16 MFMA partial kernel
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool kReset, bool kStats>
-__global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_kernel(DecodeArgs a) {
+// kStats (heavy-hitter mode): 0 off; 1 per-slot statistics to HBM for the
+// accumulate kernel; 2 statistics kept in LDS and the scores accumulated here
+// (one workgroup per CU, the whole sequence in one split).
+template <int D, int NW, bool kReset, int kStats>
+__global__ __launch_bounds__(NW * 64, kStats == 2 ? 1 : PS_DECODE_MIN_BLOCKS) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NC = D / 32;   // QK k-steps (32 dims each)
   constexpr int NDT = D / 16;  // PV d-tiles (16 dims each)
   const int lane = threadIdx.x & 63;
@@ -115,12 +118,16 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
   // fp16 s - m, and [chunk][head] fp32 m, the running max after that chunk
   const int nch = geo.slot_capacity / 32;
   const __amdgpu_buffer_rsrc_t stat_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      kStats ? static_cast<uint16_t*>(a.stat_scores) + ((int64_t)s * geo.hkv + h) * a.group * geo.slot_capacity
+      kStats == 1 ? static_cast<uint16_t*>(a.stat_scores) + ((int64_t)s * geo.hkv + h) * a.group * geo.slot_capacity
              : nullptr,
-      (short)0, kStats ? a.group * geo.slot_capacity * 2 : 0, 0x00020000);
+      (short)0, kStats == 1 ? a.group * geo.slot_capacity * 2 : 0, 0x00020000);
   const __amdgpu_buffer_rsrc_t max_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      kStats ? a.stat_max + ((int64_t)s * geo.hkv + h) * a.group * nch : nullptr, (short)0,
-      kStats ? a.group * nch * 4 : 0, 0x00020000);
+      kStats == 1 ? a.stat_max + ((int64_t)s * geo.hkv + h) * a.group * nch : nullptr, (short)0,
+      kStats == 1 ? a.group * nch * 4 : 0, 0x00020000);
+  // kStats 2: the same two arrays in LDS (the wave merge reuses the space later)
+  __shared__ __attribute__((aligned(16))) uint8_t fused_lds[kStats == 2 ? kFusedStatsLds : 16];
+  uint16_t* const lds_x = reinterpret_cast<uint16_t*>(fused_lds);
+  float* const lds_m = reinterpret_cast<float*>(fused_lds + nch * a.group * 64);
 
   // chunk index list of this wave: first chunk kb/32 + wave, stride NW
   const int c_end = (ke + 31) >> 5;   // chunks touching [kb, ke)
@@ -259,7 +266,17 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
       pv[i] = __builtin_amdgcn_exp2f(xv[i]);
       psum += pv[i];
     }
-    if (kStats) {
+    if (kStats == 2) {
+      if (r < a.group) {
+        u32x4 xw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          xw[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xv[2 * i], xv[2 * i + 1]));
+        *reinterpret_cast<u32x4*>(lds_x + (ci * a.group + r) * 32 + 8 * g) = xw;
+        if (g == 0) lds_m[ci * a.group + r] = m_new;
+      }
+    }
+    if (kStats == 1) {
       // heavy-hitter statistics, stored with the next chunk's loads (a store
       // issued amid the math would hold the wave until the memory pipeline
       // takes it).  fp16 keeps s - m to 2^-11 near 0, where the mass is.
@@ -333,33 +350,36 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
   }
 
   while (c < c_end) {
-    if (kStats) store_stats();
+    if (kStats == 1) store_stats();
     if (c + NW < c_end) load_chunk(c + NW, kB, vB);
     compute_chunk(c, kA, vA);
     c += NW;
     if (c >= c_end) break;
-    if (kStats) store_stats();
+    if (kStats == 1) store_stats();
     if (c + NW < c_end) load_chunk(c + NW, kA, vA);
     compute_chunk(c, kB, vB);
     c += NW;
   }
-  if (kStats) store_stats();
+  if (kStats == 1) store_stats();
 
   // ---- finish the wave: sum the lane-local partial sums of each head ----
   l_run = sum_xor16(l_run);
   l_run = sum_xor32(l_run);
 
   // ---- merge the NW waves through LDS ----
-  __shared__ float sm_o[NW][D][17];
+  __shared__ float sm_o_own[kStats == 2 ? 1 : NW][D][17];
+  float (*const sm_o)[D][17] = kStats == 2 ? reinterpret_cast<float (*)[D][17]>(fused_lds) : sm_o_own;
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
   __shared__ int sm_bad;
   if (threadIdx.x == 0) sm_bad = 0;
   __syncthreads();
+  if (kStats != 2) {
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm_o[wave][16 * dt + 4 * g + i][r] = acc[dt][i];
+      for (int i = 0; i < 4; ++i) sm_o[wave][16 * dt + 4 * g + i][r] = acc[dt][i];
+  }
   if (g == 0) {
     sm_m[wave][r] = m_run;
     sm_l[wave][r] = l_run;
@@ -369,6 +389,56 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
 
   const int G = a.group;
   const bool any_bad = sm_bad != 0;
+  if (kStats == 2) {
+    // each row's log2-sum-exp2, then score[j] += sum over the group's heads of
+    // exp2(s_j - lse2) for the visible non-prefix slots, 8 per thread (the
+    // capacity is a multiple of 64, so a group never crosses a chunk)
+    __shared__ float sm_lse2[16];
+    if (threadIdx.x < G) {
+      const int n = threadIdx.x;
+      float M = -INFINITY;
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][n]);
+      float l = 0.f;
+      if (M != -INFINITY)
+        for (int w = 0; w < NW; ++w) l += __builtin_amdgcn_exp2f(sm_m[w][n] - M) * sm_l[w][n];
+      sm_lse2[n] = M + __log2f(l);
+    }
+    __syncthreads();
+    float* score = a.heavy_score + ((int64_t)s * geo.hkv + h) * geo.slot_capacity;
+    if (!any_bad) {
+      for (int j0 = (L & ~7) + 8 * (int)threadIdx.x; j0 < nvis; j0 += 8 * NW * 64) {
+        const int cj = j0 >> 5;
+        float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < G; ++n) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(lds_x + (cj * G + n) * 32 + (j0 & 31));
+          const float off = lds_m[cj * G + n] - sm_lse2[n];
+          // (the element goes through a named scalar: a bit cast straight from a
+          // vector element read element 0 every time)
+          const uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const auto x = __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), ww[e]);
+            m[2 * e] += __builtin_amdgcn_exp2f((float)x[0] + off);
+            m[2 * e + 1] += __builtin_amdgcn_exp2f((float)x[1] + off);
+          }
+        }
+        float4* sp = reinterpret_cast<float4*>(score + j0);
+        const float4 s0 = sp[0], s1 = sp[1];
+        float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (j0 + i >= L && j0 + i < nvis) sv[i] += m[i];
+        sp[0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+        sp[1] = make_float4(sv[4], sv[5], sv[6], sv[7]);
+      }
+    }
+    __syncthreads();   // the statistics are consumed: their space takes the wave merge
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_o[wave][16 * dt + 4 * g + i][r] = acc[dt][i];
+    __syncthreads();
+  }
   for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
     const int n = idx / D;
     const int d = idx % D;
@@ -388,7 +458,7 @@ __global__ __launch_bounds__(NW * 64, PS_DECODE_MIN_BLOCKS) void decode_bf16_ker
     if (a.num_splits == 1) {
       const float val = any_bad ? __builtin_nanf("") : o / l;
       static_cast<uint16_t*>(a.out)[row * D + d] = f32_to_bf16_bits(val);
-      if (kStats && d == 0) a.stat_lse2[row] = any_bad ? __builtin_nanf("") : M + __log2f(l);
+      if (kStats == 1 && d == 0) a.stat_lse2[row] = any_bad ? __builtin_nanf("") : M + __log2f(l);
     } else {
       const int64_t prow = row * a.num_splits + split;
       a.part_o[prow * D + d] = any_bad ? __builtin_nanf("") : o;
@@ -582,12 +652,15 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((uint32_t)((int64_t)a.num_seqs * a.geom.hkv * a.num_splits));
   if (a.dtype == PS_BF16) {
     constexpr int NW = PS_DECODE_WAVES;
-    if (a.heavy_count)
-      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, true>), grid, dim3(NW * 64), 0, stream, a);
+    if (a.heavy_score)
+      hipLaunchKernelGGL((decode_bf16_kernel<D, kFusedStatsWaves, false, 2>), grid, dim3(kFusedStatsWaves * 64), 0,
+                         stream, a);
+    else if (a.heavy_count)
+      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, 1>), grid, dim3(NW * 64), 0, stream, a);
     else if (a.reset_pe)
-      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, true, false>), grid, dim3(NW * 64), 0, stream, a);
+      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, true, 0>), grid, dim3(NW * 64), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, false>), grid, dim3(NW * 64), 0, stream, a);
+      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, 0>), grid, dim3(NW * 64), 0, stream, a);
   } else {
     hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(256), 0, stream, a);
   }

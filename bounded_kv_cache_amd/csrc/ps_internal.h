@@ -54,6 +54,9 @@ struct DecodeArgs {
   void* stat_scores;
   float* stat_max;             // bf16 path: [num_seqs][hkv][slot_capacity / 32][group]; else NULL
   float* stat_lse2;            // [num_seqs][hq] log2-sum-exp2 of each query row
+  // bf16, one split, statistics fit kFusedStatsLds: the decode kernel keeps the statistics in LDS and
+  // adds the step's attention mass to these scores itself ([num_seqs][hkv][slot_capacity]); else NULL
+  float* heavy_score;
 };
 
 // Heavy-hitter bookkeeping around a decode step.
@@ -139,6 +142,15 @@ struct BackwardArgs {
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Heavy-hitter decode with the statistics in LDS: waves per workgroup (one
+// workgroup per CU) and the LDS it may give them; per 32-slot chunk and query
+// head they take 32 fp16 values and one fp32 max.
+constexpr int kFusedStatsWaves = 8;
+constexpr int kFusedStatsLds = 152 * 1024;
+inline size_t fused_stats_bytes(int32_t slot_capacity, int32_t group) {
+  return (size_t)(slot_capacity / 32) * group * (32 * 2 + 4);
+}
+
 hipError_t launch_heavy_retire(const HeavyArgs& a, hipStream_t stream);
 hipError_t launch_heavy_accumulate(const HeavyArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -83,8 +83,11 @@ def test_heavy_fp32_trace_matches_oracle(ps, splits):
                 np.testing.assert_allclose(sc[s, kv, L + W + i], want[s][2][kv][int(j)], rtol=1e-5)
 
 
+@pytest.mark.parametrize("splits", [1, 3])
 @pytest.mark.parametrize("paged", [False, True])
-def test_heavy_bf16_follows_the_rule_step_by_step(ps, paged):
+def test_heavy_bf16_follows_the_rule_step_by_step(ps, paged, splits):
+    """splits 1: statistics kept in LDS and the scores accumulated by the decode
+    kernel; 3: statistics through HBM and the accumulate kernel."""
     hq, hkv, d, W, H, steps = 16, 2, 128, 96, 40, 330
     prefixes = [20, 0, 37]
     n = len(prefixes)
@@ -109,7 +112,7 @@ def test_heavy_bf16_follows_the_rule_step_by_step(ps, paged):
         pre_pos = state.heavy_pos.cpu().numpy()
         pos = torch.full((n,), p, dtype=torch.int64, device="cuda")
         ps.ps_heavy_decode_step(attn, cache, H, kc, vc, pl, pos, qd[:, p].contiguous(), kd[:, p:p + 1].contiguous(),
-                                vd[:, p:p + 1].contiguous(), out, state, block_table=bt)
+                                vd[:, p:p + 1].contiguous(), out, state, block_table=bt, num_splits=splits)
         got = out.float().cpu().numpy()
         sc = state.score.cpu().numpy()
         cnt = state.heavy_count.cpu().numpy()

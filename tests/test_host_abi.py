@@ -284,20 +284,26 @@ def test_heavy_decode_validation_and_workspace(lib):
     a, c = _descs(cap=4352)
     need = lib.ps_heavy_workspace_size(ctypes.byref(a), ctypes.byref(c), 4, 1)
     al = lambda x: (x + 255) // 256 * 256
-    # bf16: fp16 s - m per slot and head, one fp32 max per 32-slot chunk, the row sums
+    # bf16, one split, statistics within the LDS budget (136 chunks x 8 heads x
+    # (32 fp16 + one fp32 max) = 74 KB): the decode kernel keeps them in LDS
+    assert need == 0
+    # more splits: fp16 s - m per slot and head, one fp32 max per 32-slot chunk, the row sums
     stats = al(4 * 16 * 4352 * 2) + al(4 * 16 * (4352 // 32) * 4) + al(4 * 16 * 4)
-    assert need == al(0) + stats
     need3 = lib.ps_heavy_workspace_size(ctypes.byref(a), ctypes.byref(c), 4, 3)
     assert need3 == al(4 * 16 * 3 * (128 + 2) * 4) + stats
+    # one split but statistics beyond the budget (9216 slots: 288 chunks x 8 x 68 B > 152 KB)
+    ab, cb = _descs(cap=9216)
+    assert lib.ps_heavy_workspace_size(ctypes.byref(ab), ctypes.byref(cb), 4, 1) == \
+        al(4 * 16 * 9216 * 2) + al(4 * 16 * (9216 // 32) * 4) + al(4 * 16 * 4)
     # fp32: the scores themselves, no maxima
     a32, c32 = _descs(cap=4352, dtype=1)
     assert lib.ps_heavy_workspace_size(ctypes.byref(a32), ctypes.byref(c32), 4, 1) == \
         al(4 * 16 * 4352 * 4) + al(4 * 16 * 4)
 
-    def call(attn=a, cache=c, H=128, score=FAKE, hpos=FAKE, ws=FAKE, wsb=need, splits=1, seqs=4):
+    def call(attn=a, cache=c, H=128, score=FAKE, hpos=FAKE, ws=FAKE, wsb=need3, splits=3, seqs=4):
         return lib.ps_heavy_decode_step(ctypes.byref(attn), ctypes.byref(cache), H, FAKE, FAKE, None, FAKE, FAKE,
                                         FAKE, FAKE, FAKE, FAKE, seqs, score, FAKE, hpos, splits, ws, wsb, None)
-    assert call(wsb=need - 1) == 3
+    assert call(wsb=need3 - 1) == 3
     assert call(score=None) == 1
     assert call(hpos=None) == 1
     assert call(hpos=None, H=0) != 1 or lib.ps_last_error()      # no heavy slots: heavy_pos may be NULL
