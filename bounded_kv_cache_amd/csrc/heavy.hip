@@ -13,8 +13,9 @@
 //     free, or replaces the weakest member (smallest score, oldest on ties) if
 //     its own score is strictly larger; otherwise it is dropped.
 // Kernels: retire (before the step's append, one wave per (sequence, KV head):
-// admission and the K/V copy into the heavy slot) and accumulate (after the
-// decode kernel has written the step's scores and each row's log2-sum-exp2).
+// admission and the K/V copy into the heavy slot) and accumulate (after a
+// decode kernel that wrote its statistics and each row's log2-sum-exp2 to the
+// workspace; when they fit in LDS the decode kernel adds the mass itself).
 #include "ps_internal.h"
 
 namespace ps {

@@ -243,7 +243,9 @@ size_t ps_prefill_workspace_size(const ps_attn_desc* attn, int32_t batch, int32_
  *                 members (entries past heavy_count are unspecified).
  * Steps must be issued for consecutive positions of a sequence (the
  * admission at p needs the scores accumulated up to p - 1).  workspace:
- * >= ps_heavy_workspace_size(...) bytes.  Continue PE only. */
+ * >= ps_heavy_workspace_size(...) bytes (may be 0, then workspace may be
+ * NULL: bf16 with one split whose per-slot statistics fit the kernel's LDS).
+ * Continue PE only. */
 ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* cache,
                                int32_t heavy_slots, void* k_cache, void* v_cache,
                                const int32_t* block_table, const int32_t* prefix_len,
