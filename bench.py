@@ -15,7 +15,9 @@ same workload, the masked prefill kernel (truncated-backprop chunk: 8 x 8192
 queries behind a 100-token prefix, W=2048, Hq=28, Hkv=4) in TFLOP/s against
 the 2.5 PFLOP/s bf16 MFMA peak, the chunk prefill that reads the ring (64
 rings at 32768, a 2048-token chunk each), and the full-attention decode
-comparator at the same position.
+comparator at the same position.  Next to the published peaks it measures
+this GPU's own ceilings: HBM read bandwidth of a plain streaming read (the
+library's probe), torch's copy bandwidth, and the bf16 rate of the vendor GEMM.
 """
 from __future__ import annotations
 
@@ -613,6 +615,37 @@ def run_cpu_prefill_baseline(cores):
             "cpu_seconds": sum(r[1] for r in res)}
 
 
+def measure_ceilings(ps, torch, reps=10):
+    """Measured ceilings on this GPU, next to the published peaks: the HBM read
+    bandwidth of a plain streaming read (the library's probe over 4 GiB), the
+    copy bandwidth of torch's copy kernel (1 GiB read + 1 GiB written), and the
+    bf16 rate of the vendor GEMM (torch.matmul, 8192^3)."""
+    out = {}
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")   # 4 GiB
+    ck = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ps.ps_read_probe(x, ck)
+    t = timed(torch, lambda k: [ps.ps_read_probe(x, ck) for _ in range(k)], reps) / reps
+    out["hbm_read_gbs"] = x.numel() * 4 / t / 1e9
+    del x
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    t = timed(torch, lambda k: [dst.copy_(src) for _ in range(k)], reps) / reps
+    out["torch_copy_gbs"] = 2 * src.numel() * 4 / t / 1e9
+    del src, dst
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(3)
+    a = torch.randn((n, n), generator=g, device="cuda").bfloat16()
+    b = torch.randn((n, n), generator=g, device="cuda").bfloat16()
+    c = torch.matmul(a, b)
+    t = timed(torch, lambda k: [torch.matmul(a, b, out=c) for _ in range(k)], reps) / reps
+    out["bf16_gemm_tflops"] = 2.0 * n ** 3 / t / 1e12
+    out["gemm"] = f"torch.matmul bf16 {n}x{n}x{n}"
+    del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def load_traffic(kernel_bytes):
     """HBM traffic per launch from the committed counter summary, if it was
     taken on the current kernel source."""
@@ -669,6 +702,8 @@ def main():
     if args.only == "heavy":
         print(json.dumps({"heavy_hitters": run_heavy(ps, torch)}))
         return
+    ceil = measure_ceilings(ps, torch)
+    print(f"[bench] ceilings: {ceil}", file=sys.stderr, flush=True)
     dec = run_decode(ps, torch, args)
     print(f"[bench] decode done: {dec['tok_s']:.0f} tok/s, kernel {dec['kernel_s'] * 1e6:.1f} us",
           file=sys.stderr, flush=True)
@@ -721,7 +756,9 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(dec["kernel_bytes"]),
                      "kernel": "decode_bf16_kernel", "kernel_us": dec["kernel_s"] * 1e6,
                      "kernel_launches_timed": dec["kernel_launches"],
-                     "bytes_per_launch": dec["kernel_bytes"]},
+                     "bytes_per_launch": dec["kernel_bytes"],
+                     "measured_read_gbs": ceil["hbm_read_gbs"], "frac_of_measured_read": achieved / ceil["hbm_read_gbs"]},
+        "ceilings": ceil,
         "cpu_baseline": cpu,
         "cpu_baseline_prefill": cpu_prefill,
         "prefill": prefill,
@@ -730,6 +767,9 @@ def main():
         "heavy_hitters": heavy,
         "full_attention": full,
     }
+    if prefill:
+        for v in prefill.values():
+            v["frac_of_measured_gemm"] = v["tflops"] / ceil["bf16_gemm_tflops"]
     if extra:
         line["decode_other_workloads"] = extra
     if sweep:

@@ -22,7 +22,7 @@ __all__ = ["AttnSpec", "CacheSpec", "PSError", "ps_kv_append", "ps_decode_attn",
            "ps_chunk_prefill_attn", "ps_chunk_prefill_workspace_size", "ps_prefill_attn_backward",
            "ps_prefill_backward_workspace_size", "ps_heavy_decode_step", "ps_heavy_workspace_size", "HeavyState",
            "ps_prefill_plan", "ps_decode_workspace_size", "ps_decode_num_splits", "ps_prefill_workspace_size",
-           "ps_prefill_tile_shape", "ps_abi_version", "cache_shapes", "PS_BF16", "PS_F32", "PS_PE_CONTINUE",
+           "ps_prefill_tile_shape", "ps_read_probe", "ps_abi_version", "cache_shapes", "PS_BF16", "PS_F32", "PS_PE_CONTINUE",
            "PS_PE_RESET", "PS_PE_RESET_RECOMPUTE"]
 
 _TORCH_DTYPE = {PS_BF16: torch.bfloat16, PS_F32: torch.float32}
@@ -105,6 +105,18 @@ def ps_decode_workspace_size(attn: AttnSpec, cache: CacheSpec, num_seqs: int, nu
 def ps_prefill_workspace_size(attn: AttnSpec, batch: int, num_queries: int, num_keys: int) -> int:
     a = attn.c()
     return _lib.load().ps_prefill_workspace_size(ctypes.byref(a), batch, num_queries, num_keys)
+
+
+def ps_read_probe(src: torch.Tensor, checksum: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """Read every byte of `src` once on the GPU; `checksum` (one int32 on the
+    device) receives the XOR of its 32-bit words.  A bandwidth-measurement helper."""
+    if not src.is_cuda or not checksum.is_cuda or checksum.dtype != torch.int32 or checksum.numel() < 1:
+        raise ValueError("src and a one-element int32 checksum must be device tensors")
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    _lib.check(_lib.load().ps_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(checksum),
+                                         _stream(stream)))
+    return checksum
 
 
 def ps_prefill_tile_shape(attn: AttnSpec):

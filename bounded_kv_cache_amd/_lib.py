@@ -51,6 +51,7 @@ SIGNATURES = {
     "ps_heavy_workspace_size": (_sz, [_pA, _pC, _i32, _i32]),
     "ps_prefill_tile_shape": (_i32, [_pA, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "ps_prefill_plan": (_i32, [_pA, _i32, _i32, _i64, _i32, _i32, _vp, _i32, _vp, _vp]),
+    "ps_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
     "ps_last_error": (ctypes.c_char_p, []),
     "ps_status_string": (ctypes.c_char_p, [_i32]),
     "ps_abi_version": (_i32, []),

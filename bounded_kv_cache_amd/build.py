@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libprefix_sliding.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "append.hip", "decode.hip", "prefill.hip", "backward.hip", "heavy.hip", "reset_pe.hip"]
+SOURCES = ["api.hip", "append.hip", "decode.hip", "prefill.hip", "backward.hip", "heavy.hip", "reset_pe.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -506,6 +506,14 @@ size_t ps_prefill_workspace_size(const ps_attn_desc* attn, int32_t batch, int32_
   return prefill_ws_bytes(attn, batch, num_queries, num_keys);
 }
 
+ps_status ps_read_probe(const void* src, size_t bytes, uint32_t* checksum, hipStream_t stream) {
+  if (!checksum || (bytes > 0 && !src)) return fail(PS_INVALID_ARGUMENT, "NULL pointer");
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0)
+    return fail(PS_INVALID_ARGUMENT, "src and bytes must be 16-byte aligned");
+  if (bytes > ((size_t)1 << 40)) return fail(PS_INVALID_ARGUMENT, "bytes %zu beyond 2^40", bytes);
+  return from_hip(ps::launch_read_probe(src, (int64_t)bytes, checksum, device_cu_count(), stream), "ps_read_probe");
+}
+
 ps_status ps_prefill_tile_shape(const ps_attn_desc* attn, int32_t* block_m, int32_t* block_n) {
   ps_status st = check_attn(attn);
   if (st != PS_OK) return st;

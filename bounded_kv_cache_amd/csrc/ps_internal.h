@@ -151,6 +151,7 @@ inline size_t fused_stats_bytes(int32_t slot_capacity, int32_t group) {
   return (size_t)(slot_capacity / 32) * group * (32 * 2 + 4);
 }
 
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* checksum, int cu_count, hipStream_t stream);
 hipError_t launch_heavy_retire(const HeavyArgs& a, hipStream_t stream);
 hipError_t launch_heavy_accumulate(const HeavyArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

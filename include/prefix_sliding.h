@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 6
+#define PS_ABI_VERSION 7
 
 typedef enum {
   PS_OK = 0,
@@ -335,6 +335,16 @@ ps_status ps_prefill_plan(const ps_attn_desc* attn, int32_t window, int32_t pref
                           int64_t kv_start, int32_t num_queries, int32_t num_keys,
                           int32_t* tiles, int32_t max_tiles, int32_t* num_tiles,
                           hipStream_t stream);
+
+/* ps_read_probe -- measurement helper, not part of the method: reads `bytes`
+ * of device memory at src once (16-byte non-temporal loads, grid-stride over
+ * the whole GPU) and stores the XOR of all its 32-bit words in *checksum
+ * (device memory; 0 for bytes == 0).  Timed around a large buffer it gives the
+ * HBM read bandwidth this GPU actually sustains, the measured ceiling the
+ * decode kernel is reported against next to the published 8 TB/s.  src and
+ * bytes must be 16-byte aligned, bytes <= 2^40; PS_INVALID_ARGUMENT otherwise,
+ * before anything is launched. */
+ps_status ps_read_probe(const void* src, size_t bytes, uint32_t* checksum, hipStream_t stream);
 
 const char* ps_last_error(void);
 const char* ps_status_string(ps_status status);

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ps_abi_version() == 6
+    assert lib.ps_abi_version() == 7
     assert lib.ps_status_string(0) == b"ok"
     assert lib.ps_status_string(3) == b"workspace too small"
 
@@ -312,3 +312,12 @@ def test_heavy_decode_validation_and_workspace(lib):
     assert call(seqs=0) == 0
     r, _ = _descs(pe=1)
     assert call(attn=r) == 2
+
+
+def test_read_probe_validation(lib):
+    assert lib.ps_read_probe(None, 16, FAKE, None) == 1
+    assert lib.ps_read_probe(FAKE, 16, None, None) == 1
+    assert lib.ps_read_probe(FAKE, 24, FAKE, None) == 1                       # bytes not a multiple of 16
+    assert lib.ps_read_probe(ctypes.c_void_p(0x1008), 16, FAKE, None) == 1    # src not 16-byte aligned
+    assert b"aligned" in lib.ps_last_error()
+    assert lib.ps_read_probe(FAKE, (1 << 40) + 16, FAKE, None) == 1
