@@ -619,7 +619,7 @@ def measure_ceilings(ps, torch, reps=10):
     """Measured ceilings on this GPU, next to the published peaks: the HBM read
     bandwidth of a plain streaming read (the library's probe over 4 GiB), the
     copy bandwidth of torch's copy kernel (1 GiB read + 1 GiB written), and the
-    bf16 rate of the vendor GEMM (torch.matmul, 8192^3)."""
+    bf16 rate of the vendor GEMM (torch.matmul, 16384^3)."""
     out = {}
     x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")   # 4 GiB
     ck = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -633,14 +633,16 @@ def measure_ceilings(ps, torch, reps=10):
     t = timed(torch, lambda k: [dst.copy_(src) for _ in range(k)], reps) / reps
     out["torch_copy_gbs"] = 2 * src.numel() * 4 / t / 1e9
     del src, dst
-    n = 8192
+    # the fastest of the shapes and layouts tried (4096^3 .. 32768x8192x8192, B row- or
+    # column-major: 1.12-1.60 PFLOP/s): 16384^3 with B column-major (A B^T, B stored [n][k])
+    n = 16384
     g = torch.Generator(device="cuda").manual_seed(3)
     a = torch.randn((n, n), generator=g, device="cuda").bfloat16()
     b = torch.randn((n, n), generator=g, device="cuda").bfloat16()
-    c = torch.matmul(a, b)
-    t = timed(torch, lambda k: [torch.matmul(a, b, out=c) for _ in range(k)], reps) / reps
+    c = torch.matmul(a, b.t())
+    t = timed(torch, lambda k: [torch.matmul(a, b.t(), out=c) for _ in range(k)], reps) / reps
     out["bf16_gemm_tflops"] = 2.0 * n ** 3 / t / 1e12
-    out["gemm"] = f"torch.matmul bf16 {n}x{n}x{n}"
+    out["gemm"] = f"torch.matmul bf16 {n}x{n}x{n}, B column-major"
     del a, b, c
     torch.cuda.empty_cache()
     return out
