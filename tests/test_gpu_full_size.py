@@ -222,3 +222,94 @@ def test_backward_truncated_backprop_chunk(ps):
         err = np.abs(got - want).max() / big
         print(name, err, flush=True)
         assert err <= 2e-2, (name, err)
+
+
+def _ring_slot(j, L, W):
+    return j if j < L else L + (j - L) % W
+
+
+@pytest.mark.parametrize("splits", [0, 2], ids=["auto-split", "two-splits"])
+def test_heavy_decode_128k_256_sequences(ps, splits):
+    """One prefix + heavy hitters + window step at the timed shape (256 sequences
+    at 131072, L=100, W=4096, H=512, heavy sets full): automatic splits keep the
+    statistics in LDS, two splits send them through the workspace.  For sampled
+    (sequence, KV head): the admission is exactly the rule on the scores before
+    the step, the K/V moves are exact, the output matches the oracle's attention
+    over the visible slots, and every score grew by the oracle's attention mass."""
+    n, L, W, H, p = 256, 100, 4096, 512, 131072
+    hq, hkv, d = 16, 2, 128
+    g = hq // hkv
+    scale = 1 / math.sqrt(d)
+    attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16, 10000.0, scale)
+    cap = -(-(L + W + H) // 64) * 64
+    cache = ps.CacheSpec(window=W, slot_capacity=cap)
+    gen = torch.Generator(device="cuda").manual_seed(21)
+    ks, vs = ps.cache_shapes(attn, cache, n)
+    kc = (torch.randn(ks, generator=gen, device="cuda") * 0.5).bfloat16()   # contents = already rotated keys
+    vc = (torch.randn(vs, generator=gen, device="cuda") * 0.5).bfloat16()
+    state = ps.HeavyState.new(attn, cache, n, H)
+    state.score.uniform_(0.0, 1.0, generator=gen)
+    state.heavy_count.fill_(H)
+    state.heavy_pos.copy_(torch.arange(H, device="cuda").view(1, 1, H) * 37 + 500)
+    pl = torch.full((n,), L, dtype=torch.int32, device="cuda")
+    q = torch.randn((n, hq, d), generator=gen, device="cuda").bfloat16()
+    kn = (torch.randn((n, 1, hkv, d), generator=gen, device="cuda") * 0.5).bfloat16()
+    vn = (torch.randn((n, 1, hkv, d), generator=gen, device="cuda") * 0.5).bfloat16()
+    out = torch.empty((n, hq, d), dtype=torch.bfloat16, device="cuda")
+    sampled = [0, 101, 255]
+
+    def host_kv(s):   # [hkv][cap][d] each, V from its [cap/8][d][8] blocks
+        k = kc[s].float().cpu().numpy()
+        v = vc[s].float().cpu().numpy().transpose(0, 1, 3, 2).reshape(hkv, cap, d)
+        return k, v
+
+    pre = {s: (host_kv(s), state.score[s].cpu().numpy().copy(), state.heavy_pos[s].cpu().numpy().copy())
+           for s in sampled}
+    pos = torch.full((n,), p, dtype=torch.int64, device="cuda")
+    ps.ps_heavy_decode_step(attn, cache, H, kc, vc, pl, pos, q, kn, vn, out, state, num_splits=splits)
+    got = out.float().cpu().numpy()
+    cnt = state.heavy_count.cpu().numpy()
+    e = p - W
+    se = _ring_slot(e, L, W)
+    assert se == _ring_slot(p, L, W)
+    admitted = 0
+    for s in sampled:
+        (k0, v0), sc0, hp0 = pre[s]
+        k1, v1 = host_kv(s)
+        sc1 = state.score[s].cpu().numpy()
+        hp1 = state.heavy_pos[s].cpu().numpy()
+        qh = q[s].float().cpu().numpy()
+        knew = oracle.rope(kn[s, 0].float().cpu().numpy(), p, 10000.0)
+        for kv in range(hkv):
+            slot, _ = oracle.h2o_admit([int(x) for x in hp0[kv]], [float(x) for x in sc0[kv, L + W:L + W + H]], e,
+                                       float(sc0[kv, se]), H)
+            assert cnt[s, kv] == H
+            want_hp = hp0[kv].copy()
+            k_exp, v_exp = k0[kv].copy(), v0[kv].copy()
+            before = sc0[kv].astype(np.float64)
+            if slot >= 0:
+                admitted += 1
+                want_hp[slot] = e
+                k_exp[L + W + slot], v_exp[L + W + slot] = k0[kv, se], v0[kv, se]
+                before[L + W + slot] = sc0[kv, se]
+            assert np.array_equal(hp1[kv], want_hp), (s, kv, slot)
+            # the new token at its slot: K rotated at p (bf16), V as given
+            np.testing.assert_allclose(k1[kv, se], knew[kv], rtol=2 ** -7, atol=4e-3)
+            np.testing.assert_array_equal(v1[kv, se], vn[s, 0, kv].float().cpu().numpy())
+            k_exp[se], v_exp[se] = k1[kv, se], v1[kv, se]
+            before[se] = 0.0
+            np.testing.assert_array_equal(k1[kv, :L + W + H], k_exp[:L + W + H])
+            np.testing.assert_array_equal(v1[kv, :L + W + H], v_exp[:L + W + H])
+            # attention over every visible slot: prefix, window, full heavy set
+            kvis, vvis = k_exp[:L + W + H], v_exp[:L + W + H]
+            heads = qh[kv * g:(kv + 1) * g]
+            want = oracle.decode_from_slots(heads, p, kvis[:, None, :], vvis[:, None, :], scale, 10000.0)
+            assert normwise_err(got[s, kv * g:(kv + 1) * g], want) <= BF16_TOL, (s, kv)
+            qr = oracle.rope(heads, p, 10000.0)
+            logits = scale * (kvis.astype(np.float64) @ qr.T)       # [slots, g]
+            w = np.exp(logits - logits.max(axis=0))
+            mass = (w / w.sum(axis=0)).sum(axis=1)
+            np.testing.assert_array_equal(sc1[kv, :L], sc0[kv, :L])   # prefix scores are not kept
+            grew = sc1[kv, L:L + W + H].astype(np.float64) - before[L:L + W + H]
+            assert normwise_err(grew, mass[L:]) <= BF16_TOL, (s, kv)
+    assert admitted > 0
