@@ -198,7 +198,29 @@ def run_decode(ps, torch, args):
     kt = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs) / 1000.0
     p_last = args.position + args.warmup + 2 * args.steps - 1
     kbytes = bench.kernel_bytes(p_last)
+    # the same step captured once in a HIP graph (28 x append + decode, then the
+    # positions advance inside the graph) and replayed: what a serving loop that
+    # captures its decode step would see
+    gpos = bench.pos[args.warmup + 2 * args.steps - 1].clone()
+
+    def graph_step():
+        for li in range(bench.layers):
+            i = li % bench.pool
+            ps.ps_kv_append(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, gpos, bench.kn[i], bench.vn[i])
+            ps.ps_decode_attn(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, gpos, bench.q[i], bench.out,
+                              num_splits=bench.splits, workspace=bench.ws)
+        gpos.add_(1)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graph_step()
+    for _ in range(2):
+        graph.replay()
+    g_s = timed(torch, lambda k: [graph.replay() for _ in range(k)], args.steps)
+    del graph
     res = {
+        "graph_tok_s": args.num_seqs * args.steps / g_s,
+        "graph_ms_per_step": g_s / args.steps * 1000.0,
         "tok_s": args.num_seqs * args.steps / elapsed,
         "ms_per_step": elapsed / args.steps * 1000.0,
         "splits": splits,
@@ -761,6 +783,9 @@ def main():
                      "bytes_per_launch": dec["kernel_bytes"],
                      "measured_read_gbs": ceil["hbm_read_gbs"], "frac_of_measured_read": achieved / ceil["hbm_read_gbs"]},
         "ceilings": ceil,
+        "decode_step_in_hip_graph": {"tok_s": dec["graph_tok_s"], "ms_per_step": dec["graph_ms_per_step"],
+                                     "note": "the timed step captured once (28 x append + decode + position "
+                                             "advance) and replayed; value is the eager loop"},
         "cpu_baseline": cpu,
         "cpu_baseline_prefill": cpu_prefill,
         "prefill": prefill,
