@@ -123,7 +123,24 @@ __global__ __launch_bounds__(256) void bwd_key_prep_kernel(BackwardArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. query prep: one workgroup per (batch, query head, 64-query tile)
+// 2a. cos/sin of every query position, once (the query prep of every batch and
+//     head and the dq kernel's back-rotation read it)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_query_cs_kernel(BackwardArgs a) {
+  constexpr int HALF = D / 2;
+  PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, 64, 64};
+  const int64_t n = (int64_t)a.num_q * HALF;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
+    const int32_t t = (int32_t)(idx / HALF), i = (int32_t)(idx % HALF);
+    float c = 1.f, sn = 0.f;
+    if (a.rope.enabled) rope_cos_sin(pf_query_pos(geo, t), a.rope.inv_freq[i], c, sn);
+    reinterpret_cast<float2*>(a.cs_q)[idx] = make_float2(c, sn);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2b. query prep: one workgroup per (batch, query head, 64-query tile)
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_query_prep_kernel(BackwardArgs a) {
@@ -131,10 +148,8 @@ __global__ __launch_bounds__(256) void bwd_query_prep_kernel(BackwardArgs a) {
   constexpr int HALF = D / 2;
   constexpr int PQ = HALF / 4;
   constexpr int DQ = D / 4;
-  __shared__ float cs_lds[TQ][HALF][2];
   __shared__ T t_lds[D][TQ + 8];
   __shared__ T o_lds[D][TQ + 8];
-  PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, 64, 64};
   const int32_t nqt = a.tqp / TQ;
   const int tid = threadIdx.x;
   const int j = tid >> 2, qq = tid & 3;
@@ -149,20 +164,7 @@ __global__ __launch_bounds__(256) void bwd_query_prep_kernel(BackwardArgs a) {
     const int64_t rest = blk / nqt;
     const int32_t h = (int32_t)(rest % a.hq);
     const int32_t b = (int32_t)(rest / a.hq);
-    __syncthreads();
-    for (int idx = tid; idx < TQ * HALF; idx += 256) {
-      const int jj = idx / HALF, i = idx % HALF;
-      const int32_t t = qt * TQ + jj;
-      float c = 1.f, sn = 0.f;
-      if (a.rope.enabled && t < a.num_q) rope_cos_sin(pf_query_pos(geo, t), a.rope.inv_freq[i], c, sn);
-      cs_lds[jj][i][0] = c;
-      cs_lds[jj][i][1] = sn;
-      if (b == 0 && h == 0 && t < a.num_q) {
-        a.cs_q[((int64_t)t * HALF + i) * 2 + 0] = c;
-        a.cs_q[((int64_t)t * HALF + i) * 2 + 1] = sn;
-      }
-    }
-    __syncthreads();
+    __syncthreads();   // the previous block's LDS reads are done
     const int32_t t = qt * TQ + j;
     const bool row_ok = t < a.num_q;
     const int64_t bh = (int64_t)b * a.hq + h;
@@ -172,9 +174,19 @@ __global__ __launch_bounds__(256) void bwd_query_prep_kernel(BackwardArgs a) {
       const int64_t src = (((int64_t)b * a.num_q + t) * a.hq + h) * D;
       load_vec(q + src + PQ * qq, x1, PQ);
       load_vec(q + src + HALF + PQ * qq, x2, PQ);
+      const float4* cs = reinterpret_cast<const float4*>(a.cs_q + ((int64_t)t * HALF + PQ * qq) * 2);
+      float csv[2 * PQ];
+#pragma unroll
+      for (int e = 0; e < PQ / 2; ++e) {
+        const float4 w = cs[e];
+        csv[4 * e] = w.x;
+        csv[4 * e + 1] = w.y;
+        csv[4 * e + 2] = w.z;
+        csv[4 * e + 3] = w.w;
+      }
 #pragma unroll
       for (int e = 0; e < PQ; ++e) {
-        const float c = cs_lds[j][PQ * qq + e][0], sn = cs_lds[j][PQ * qq + e][1];
+        const float c = csv[2 * e], sn = csv[2 * e + 1];
         const float y1 = x1[e] * c - x2[e] * sn, y2 = x2[e] * c + x1[e] * sn;
         x1[e] = y1 * a.scale_log2;
         x2[e] = y2 * a.scale_log2;
@@ -857,6 +869,9 @@ hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t stream) {
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_query_cs_kernel<D>), dim3(clamp(((int64_t)a.num_q * (D / 2) + 255) / 256)), dim3(256), 0,
+                     stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_query_prep_kernel<T, D>), dim3(clamp((int64_t)a.batch * a.hq * (a.tqp / 64))), dim3(256),
                      0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
