@@ -49,18 +49,19 @@ struct PfTraits<float> {
 // ---------------------------------------------------------------------------
 // 1. prep: rotated K [b][hkv][nkp][D], V^T [b][hkv][D][nkp], query cos/sin table
 // ---------------------------------------------------------------------------
-// One workgroup per (batch, 64-key tile): the tile's cos/sin are formed once in
-// LDS and reused for every KV head.  Each thread owns a quarter of one key row
-// (16-byte loads and stores); V is transposed through LDS so the V^T rows are
-// written contiguously.  Keys past num_k are written as zeros.
+// One workgroup per (batch, 64-key tile).  Each thread owns a quarter of one
+// key row (16-byte loads and stores) and forms the cos/sin of its own dims
+// once for every KV head; the loads of two KV heads are in flight together.
+// V is transposed through LDS so the V^T rows are written contiguously.  Keys
+// past num_k are written as zeros.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
   constexpr int TK = 64;
   constexpr int HALF = D / 2;
   constexpr int PQ = HALF / 4;   // rotation pairs per thread
   constexpr int DQ = D / 4;      // V dims per thread
-  __shared__ float cs_lds[TK][HALF][2];
-  __shared__ T vt_lds[D][TK + 8];
+  constexpr int KH = 2;          // KV heads per pass
+  __shared__ T vt_lds[KH][D][TK + 8];
   PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, a.bm, a.bn};
   const int32_t nkp = a.nkp;
   const int32_t nkt = nkp / TK;
@@ -74,64 +75,78 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillArgs a) {
   for (int64_t blk = blockIdx.x; blk < (int64_t)a.batch * nkt; blk += gridDim.x) {
     const int32_t kt = (int32_t)(blk % nkt);
     const int32_t b = (int32_t)(blk / nkt);
-    for (int idx = tid; idx < TK * HALF; idx += 256) {
-      const int jj = idx / HALF, i = idx % HALF;
-      const int32_t key = kt * TK + jj;
-      float c = 1.f, sn = 0.f;
-      if (a.rope.enabled && key < a.num_k) rope_cos_sin(pf_key_pos(geo, key), a.rope.inv_freq[i], c, sn);
-      cs_lds[jj][i][0] = c;
-      cs_lds[jj][i][1] = sn;
-    }
-    __syncthreads();
     const int32_t key = kt * TK + j;
-    for (int32_t h = 0; h < a.hkv; ++h) {
-      const int64_t bh = (int64_t)b * a.hkv + h;
-      float x1[PQ], x2[PQ], vv[DQ];
-      if (key < a.num_k) {
-        const int64_t src = (((int64_t)b * a.num_k + key) * a.hkv + h) * D;
-        load_vec(k + src + PQ * qq, x1, PQ);
-        load_vec(k + src + HALF + PQ * qq, x2, PQ);
-        load_vec(v + src + DQ * qq, vv, DQ);
+    const bool live = key < a.num_k;
+    float cs_c[PQ], cs_s[PQ];
+    {
+      const int64_t pos = live ? pf_key_pos(geo, key) : 0;
 #pragma unroll
-        for (int e = 0; e < PQ; ++e) {
-          const float c = cs_lds[j][PQ * qq + e][0], sn = cs_lds[j][PQ * qq + e][1];
-          const float y1 = x1[e] * c - x2[e] * sn, y2 = x2[e] * c + x1[e] * sn;
-          x1[e] = y1;
-          x2[e] = y2;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < PQ; ++e) x1[e] = x2[e] = 0.f;
-#pragma unroll
-        for (int e = 0; e < DQ; ++e) vv[e] = 0.f;
+      for (int e = 0; e < PQ; ++e) {
+        cs_c[e] = 1.f;
+        cs_s[e] = 0.f;
+        if (a.rope.enabled && live) rope_cos_sin(pos, a.rope.inv_freq[PQ * qq + e], cs_c[e], cs_s[e]);
       }
-      T* krow = kr + (bh * nkp + key) * D;
-      store_vec(krow + PQ * qq, x1, PQ);
-      store_vec(krow + HALF + PQ * qq, x2, PQ);
+    }
+    for (int32_t h0 = 0; h0 < a.hkv; h0 += KH) {
+      float x1[KH][PQ], x2[KH][PQ], vv[KH][DQ];
+#pragma unroll
+      for (int hh = 0; hh < KH; ++hh) {
+        if (live && h0 + hh < a.hkv) {
+          const int64_t src = (((int64_t)b * a.num_k + key) * a.hkv + h0 + hh) * D;
+          load_vec(k + src + PQ * qq, x1[hh], PQ);
+          load_vec(k + src + HALF + PQ * qq, x2[hh], PQ);
+          load_vec(v + src + DQ * qq, vv[hh], DQ);
+        } else {
+#pragma unroll
+          for (int e = 0; e < PQ; ++e) x1[hh][e] = x2[hh][e] = 0.f;
+#pragma unroll
+          for (int e = 0; e < DQ; ++e) vv[hh][e] = 0.f;
+        }
+      }
       const int js = vt_slot(j);
 #pragma unroll
-      for (int e = 0; e < DQ; ++e) {
-        T tv;
-        if (sizeof(T) == 2)
-          tv = (T)f32_to_bf16_bits(vv[e]);   // exact: vv holds bf16 values
-        else
-          tv = (T)vv[e];
-        vt_lds[DQ * qq + e][js] = tv;
+      for (int hh = 0; hh < KH; ++hh) {
+        if (h0 + hh >= a.hkv) break;
+        const int64_t bh = (int64_t)b * a.hkv + h0 + hh;
+#pragma unroll
+        for (int e = 0; e < PQ; ++e) {
+          const float y1 = x1[hh][e] * cs_c[e] - x2[hh][e] * cs_s[e];
+          const float y2 = x2[hh][e] * cs_c[e] + x1[hh][e] * cs_s[e];
+          x1[hh][e] = y1;
+          x2[hh][e] = y2;
+        }
+        T* krow = kr + (bh * nkp + key) * D;
+        store_vec(krow + PQ * qq, x1[hh], PQ);
+        store_vec(krow + HALF + PQ * qq, x2[hh], PQ);
+#pragma unroll
+        for (int e = 0; e < DQ; ++e) {
+          T tv;
+          if (sizeof(T) == 2)
+            tv = (T)f32_to_bf16_bits(vv[hh][e]);   // exact: vv holds bf16 values
+          else
+            tv = (T)vv[hh][e];
+          vt_lds[hh][DQ * qq + e][js] = tv;
+        }
       }
       __syncthreads();
-      // V^T rows: D rows x 64 keys, 16-byte pieces
+      // V^T rows: D rows x 64 keys per head, 16-byte pieces
       constexpr int EP = 16 / sizeof(T);
-      for (int idx = tid; idx < D * (TK / EP); idx += 256) {
-        const int d = idx / (TK / EP), c = idx % (TK / EP);
+      const int nh = a.hkv - h0 < KH ? a.hkv - h0 : KH;
+      for (int idx = tid; idx < nh * D * (TK / EP); idx += 256) {
+        const int hh = idx / (D * (TK / EP));
+        const int rem = idx % (D * (TK / EP));
+        const int d = rem / (TK / EP), c = rem % (TK / EP);
         u32x4 w;
         if (sizeof(T) == 2) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            w[e] = (uint32_t)(uint16_t)vt_lds[d][c * EP + 2 * e] | ((uint32_t)(uint16_t)vt_lds[d][c * EP + 2 * e + 1] << 16);
+            w[e] = (uint32_t)(uint16_t)vt_lds[hh][d][c * EP + 2 * e] |
+                   ((uint32_t)(uint16_t)vt_lds[hh][d][c * EP + 2 * e + 1] << 16);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = __float_as_uint((float)vt_lds[d][c * EP + e]);
+          for (int e = 0; e < 4; ++e) w[e] = __float_as_uint((float)vt_lds[hh][d][c * EP + e]);
         }
+        const int64_t bh = (int64_t)b * a.hkv + h0 + hh;
         *reinterpret_cast<u32x4*>(vt + (bh * D + d) * nkp + kt * TK + c * EP) = w;
       }
       __syncthreads();
