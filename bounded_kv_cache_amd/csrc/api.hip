@@ -450,24 +450,12 @@ ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* ca
   h.stat_scores = stat_scores;
   h.stat_max = stat_max;
   h.stat_lse2 = stat_lse2;
-  hipError_t e = ps::launch_heavy_retire(h, stream);   // 1. the token leaving the window
+  h.k_new = k_new;
+  h.v_new = v_new;
+  h.rope = rope;
+  // 1-2. the token leaving the window (admission), then the new token into the ring
+  hipError_t e = ps::launch_heavy_retire(h, stream);
   if (e != hipSuccess) return from_hip(e, "ps_heavy_decode_step retire launch");
-  ps::AppendArgs ap;                                    // 2. the new token into the ring
-  ap.geom = geom;
-  ap.dtype = attn->dtype;
-  ap.k_cache = k_cache;
-  ap.v_cache = v_cache;
-  ap.block_table = block_table;
-  ap.prefix_len = prefix_len;
-  ap.start_pos = pos;
-  ap.seq_tokens = nullptr;
-  ap.tokens_per_seq = 1;
-  ap.k_new = k_new;
-  ap.v_new = v_new;
-  ap.num_seqs = num_seqs;
-  ap.slot_pos = nullptr;
-  ap.rope = rope;
-  if ((e = ps::launch_append(ap, stream)) != hipSuccess) return from_hip(e, "ps_heavy_decode_step append launch");
   ps::DecodeArgs a;                                     // 3. attention over prefix + window + heavy slots
   a.geom = geom;
   a.dtype = attn->dtype;

@@ -195,6 +195,16 @@ __global__ __launch_bounds__(NW * 64, kStats == 2 ? 1 : PS_DECODE_MIN_BLOCKS) vo
     }
   };
 
+  // kStats 2: this thread's first 8 scores, loaded now so that the update at
+  // the end does not wait a memory round trip
+  float4 sc_pre0 = make_float4(0.f, 0.f, 0.f, 0.f), sc_pre1 = sc_pre0;
+  const int j_first = (L & ~7) + 8 * (int)threadIdx.x;
+  if (kStats == 2 && !bad && j_first < nvis) {
+    const float4* sp = reinterpret_cast<const float4*>(a.heavy_score +
+                                                       ((int64_t)s * geo.hkv + h) * geo.slot_capacity + j_first);
+    sc_pre0 = sp[0];
+    sc_pre1 = sp[1];
+  }
   // statistics of the last computed chunk, awaiting their store
   u32x4 st_x = {0u, 0u, 0u, 0u};
   float st_m = 0.f;
@@ -423,7 +433,8 @@ __global__ __launch_bounds__(NW * 64, kStats == 2 ? 1 : PS_DECODE_MIN_BLOCKS) vo
           }
         }
         float4* sp = reinterpret_cast<float4*>(score + j0);
-        const float4 s0 = sp[0], s1 = sp[1];
+        const bool first = j0 == j_first;
+        const float4 s0 = first ? sc_pre0 : sp[0], s1 = first ? sc_pre1 : sp[1];
         float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i)

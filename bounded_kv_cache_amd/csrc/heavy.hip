@@ -12,8 +12,9 @@
 //   * when a token leaves the window it joins the heavy set if a slot is
 //     free, or replaces the weakest member (smallest score, oldest on ties) if
 //     its own score is strictly larger; otherwise it is dropped.
-// Kernels: retire (before the step's append, one wave per (sequence, KV head):
-// admission and the K/V copy into the heavy slot) and accumulate (after a
+// Kernels: retire (one wave per (sequence, KV head): admission, the K/V copy
+// into the heavy slot, then the step's token appended into the ring slot it
+// frees) and accumulate (after a
 // decode kernel that wrote its statistics and each row's log2-sum-exp2 to the
 // workspace; when they fit in LDS the decode kernel adds the mass itself).
 #include "ps_internal.h"
@@ -30,66 +31,90 @@ __global__ __launch_bounds__(64) void heavy_retire_kernel(HeavyArgs a) {
   const int32_t L = a.prefix_len[s];
   const int64_t p = a.pos[s];
   const int32_t H = a.heavy_slots;
-  if (L < 0 || p < 0 || (int64_t)L + g.window + H > g.slot_capacity) return;
+  if (L < 0 || p < 0) return;   // invalid sequence: nothing is written (the decode rows are NaN)
   const int64_t e = p - g.window;   // the token leaving the window at this step
-  if (e < L) return;
   const int32_t se = ring_slot(e, L, g.window);
   const int64_t sh = (int64_t)s * g.hkv + h;
-  float* score = a.score + sh * g.slot_capacity;
-  int64_t* hpos = a.heavy_pos + sh * H;
-  const float cand = score[se];
-  const int32_t base = L + g.window;
-  const int32_t cnt = a.heavy_count[sh];
-  int32_t dst = -1;
-  if (H > 0) {
-    if (cnt < H) {
-      dst = cnt;
-    } else {
-      // the weakest member: smallest score, then oldest position
-      float best = INFINITY;
-      int64_t bpos = INT64_MAX;
-      int32_t bidx = -1;
-      for (int32_t i = lane; i < H; i += 64) {
-        const float sc = score[base + i];
-        const int64_t hp = hpos[i];
-        if (sc < best || (sc == best && hp < bpos)) {
-          best = sc;
-          bpos = hp;
-          bidx = i;
+  T* kc = static_cast<T*>(a.k_cache);
+  T* vc = static_cast<T*>(a.v_cache);
+  if ((int64_t)L + g.window + H <= g.slot_capacity && e >= L) {
+    float* score = a.score + sh * g.slot_capacity;
+    int64_t* hpos = a.heavy_pos + sh * H;
+    const float cand = score[se];
+    const int32_t base = L + g.window;
+    const int32_t cnt = a.heavy_count[sh];
+    int32_t dst = -1;
+    if (H > 0) {
+      if (cnt < H) {
+        dst = cnt;
+      } else {
+        // the weakest member: smallest score, then oldest position
+        float best = INFINITY;
+        int64_t bpos = INT64_MAX;
+        int32_t bidx = -1;
+        for (int32_t i = lane; i < H; i += 64) {
+          const float sc = score[base + i];
+          const int64_t hp = hpos[i];
+          if (sc < best || (sc == best && hp < bpos)) {
+            best = sc;
+            bpos = hp;
+            bidx = i;
+          }
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+          const float ob = __shfl_xor(best, off);
+          const int64_t op = __shfl_xor(bpos, off);
+          const int32_t oi = __shfl_xor(bidx, off);
+          if (ob < best || (ob == best && op < bpos)) {
+            best = ob;
+            bpos = op;
+            bidx = oi;
+          }
+        }
+        if (cand > best) dst = bidx;
+      }
+    }
+    if (dst >= 0) {
+      const int32_t sd = base + dst;
+      const int64_t re = region_offset(g, a.block_table, s, h, se);
+      const int64_t rd = region_offset(g, a.block_table, s, h, sd);
+      if (re >= 0 && rd >= 0) {
+        for (int32_t d = lane; d < g.head_dim; d += 64) {
+          kc[rd + k_in_region(sd, d, g.head_dim)] = kc[re + k_in_region(se, d, g.head_dim)];
+          vc[rd + v_in_region(sd, d, g.head_dim)] = vc[re + v_in_region(se, d, g.head_dim)];
         }
       }
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ob = __shfl_xor(best, off);
-        const int64_t op = __shfl_xor(bpos, off);
-        const int32_t oi = __shfl_xor(bidx, off);
-        if (ob < best || (ob == best && op < bpos)) {
-          best = ob;
-          bpos = op;
-          bidx = oi;
-        }
-      }
-      if (cand > best) dst = bidx;
-    }
-  }
-  if (dst >= 0) {
-    const int32_t sd = base + dst;
-    const int64_t re = region_offset(g, a.block_table, s, h, se);
-    const int64_t rd = region_offset(g, a.block_table, s, h, sd);
-    if (re >= 0 && rd >= 0) {
-      T* kc = static_cast<T*>(a.k_cache);
-      T* vc = static_cast<T*>(a.v_cache);
-      for (int32_t d = lane; d < g.head_dim; d += 64) {
-        kc[rd + k_in_region(sd, d, g.head_dim)] = kc[re + k_in_region(se, d, g.head_dim)];
-        vc[rd + v_in_region(sd, d, g.head_dim)] = vc[re + v_in_region(se, d, g.head_dim)];
+      if (lane == 0) {
+        score[sd] = cand;
+        hpos[dst] = e;
+        if (dst == cnt) a.heavy_count[sh] = cnt + 1;
       }
     }
-    if (lane == 0) {
-      score[sd] = cand;
-      hpos[dst] = e;
-      if (dst == cnt) a.heavy_count[sh] = cnt + 1;
-    }
+    if (lane == 0) score[se] = 0.f;   // the slot receives position p next
   }
-  if (lane == 0) score[se] = 0.f;   // the slot receives position p next
+  // the step's token for this KV head into its ring slot (after the copy above
+  // has read the slot's previous token): K rotated at p, V as given
+  const int32_t slot = ring_slot(p, L, g.window);
+  if (slot >= g.slot_capacity) return;   // the ring is too small for this position: dropped
+  const int64_t rb = region_offset(g, a.block_table, s, h, slot);
+  if (rb < 0) return;                    // page outside the pool: dropped
+  const int32_t D = g.head_dim, half = D >> 1;
+  const T* kn = static_cast<const T*>(a.k_new) + sh * D;
+  const T* vn = static_cast<const T*>(a.v_new) + sh * D;
+  for (int32_t i = lane; i < half; i += 64) {
+    const float x1 = Elem<T>::load(kn + i), x2 = Elem<T>::load(kn + i + half);
+    float y1 = x1, y2 = x2;
+    if (a.rope.enabled) {
+      float c, sn;
+      rope_cos_sin(p, a.rope.inv_freq[i], c, sn);
+      y1 = x1 * c - x2 * sn;
+      y2 = x2 * c + x1 * sn;
+    }
+    Elem<T>::store(kc + rb + k_in_region(slot, i, D), y1);
+    Elem<T>::store(kc + rb + k_in_region(slot, i + half, D), y2);
+    vc[rb + v_in_region(slot, i, D)] = vn[i];
+    vc[rb + v_in_region(slot, i + half, D)] = vn[i + half];
+  }
 }
 
 // score[j] += sum over the group's query heads of exp2(s_j - lse2), j in [L, n_vis)

@@ -77,6 +77,9 @@ struct HeavyArgs {
   const void* stat_scores;     // as DecodeArgs
   const float* stat_max;
   const float* stat_lse2;
+  const void* k_new;           // the step's token [num_seqs][1][hkv][D], appended by the retire kernel
+  const void* v_new;
+  RopeFreq rope;
 };
 
 struct PrefillArgs {
