@@ -11,6 +11,9 @@
 namespace ps {
 namespace {
 
+// calls appending at least this many tokens per sequence take the block path
+constexpr int32_t kBulkAppendTokens = 16;
+
 // One wavefront per (sequence, token).  Each lane rotates rotate-half pairs
 // (i, i + D/2) of one KV head; V is copied into the 8-slot d-major blocks.
 template <typename T>
@@ -59,11 +62,111 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   if (threadIdx.x == 0 && a.slot_pos) a.slot_pos[(int64_t)s * g.slot_capacity + slot] = (int32_t)j;
 }
 
+// Bulk path (many tokens per sequence): one wavefront per (sequence, 8-slot
+// block).  Each slot of the block finds in O(1) which token of this call it
+// keeps (the last position that maps to it, if that position stays visible),
+// so a V block [D][8] is written as one 16-byte store per dim instead of 8
+// scattered 2-byte stores.  Same rules and results as append_kernel.
+template <typename T>
+__global__ __launch_bounds__(64) void append_block_kernel(AppendArgs a) {
+  const CacheGeom& g = a.geom;
+  const int32_t nblk = g.slot_capacity >> 3;
+  const int32_t s = (int32_t)(blockIdx.x / nblk);
+  const int32_t kb = (int32_t)(blockIdx.x % nblk);
+  const int lane = threadIdx.x;
+  const int32_t L = a.prefix_len[s];
+  const int64_t start = a.start_pos[s];
+  if (L < 0 || start < 0) return;  // invalid sequence: dropped
+  int32_t n_tok = a.seq_tokens ? a.seq_tokens[s] : a.tokens_per_seq;
+  n_tok = n_tok < a.tokens_per_seq ? n_tok : a.tokens_per_seq;
+  if (n_tok <= 0) return;
+  const int64_t last = start + n_tok - 1;
+  // lanes 0..7: the position this call leaves in slot 8 kb + lane, or -1
+  int64_t src = -1;
+  if (lane < 8) {
+    const int32_t slot = 8 * kb + lane;
+    if (slot < L) {
+      if (slot >= start && slot <= last) src = slot;
+    } else if ((int64_t)slot < (int64_t)L + g.window && last >= L) {
+      const int64_t r = slot - L;
+      int64_t back = ((last - L) - r) % g.window;
+      if (back < 0) back += g.window;
+      const int64_t j = last - back;   // the last position <= last that maps to this slot
+      if (j >= L && j >= start) src = j;
+    }
+  }
+  int64_t pos[8];
+  int32_t written = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    pos[k] = __shfl(src, k);
+    written += pos[k] >= 0;
+  }
+  if (written == 0) return;
+  if (a.slot_pos && lane < 8 && src >= 0) a.slot_pos[(int64_t)s * g.slot_capacity + 8 * kb + lane] = (int32_t)src;
+  const int32_t D = g.head_dim, half = D >> 1;
+  // the new tokens and the cache never overlap: restrict lets every load of
+  // the block be issued ahead of its stores
+  const T* __restrict__ kn = static_cast<const T*>(a.k_new);
+  const T* __restrict__ vn = static_cast<const T*>(a.v_new);
+  T* __restrict__ kc = static_cast<T*>(a.k_cache);
+  T* __restrict__ vc = static_cast<T*>(a.v_cache);
+  const int64_t tok0 = (int64_t)s * a.tokens_per_seq - start;   // token row of position j: tok0 + j
+  // K: rotate each kept token at its position (cos/sin shared by the KV heads)
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (pos[k] < 0) continue;
+    const int32_t slot = 8 * kb + k;
+    for (int32_t i = lane; i < half; i += 64) {
+      float c = 1.f, sn = 0.f;
+      if (a.rope.enabled) rope_cos_sin(pos[k], a.rope.inv_freq[i], c, sn);
+      for (int32_t h = 0; h < g.hkv; ++h) {
+        const int64_t base = region_offset(g, a.block_table, s, h, slot);
+        if (base < 0) continue;  // page outside the pool: dropped
+        const T* row = kn + ((tok0 + pos[k]) * g.hkv + h) * D;
+        const float x1 = Elem<T>::load(row + i), x2 = Elem<T>::load(row + i + half);
+        Elem<T>::store(kc + base + k_in_region(slot, i, D), x1 * c - x2 * sn);
+        Elem<T>::store(kc + base + k_in_region(slot, i + half, D), x2 * c + x1 * sn);
+      }
+    }
+  }
+  // V: per (KV head, dim) the block's 8 slots are 8 contiguous elements
+  for (int32_t hd = lane; hd < g.hkv * D; hd += 64) {
+    const int32_t h = hd / D, d = hd % D;
+    const int64_t base = region_offset(g, a.block_table, s, h, 8 * kb);
+    if (base < 0) continue;
+    T* dst = vc + base + v_in_region(8 * kb, d, D);   // slot 8 kb + k at dst[k]
+    T val[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) val[k] = pos[k] >= 0 ? vn[((tok0 + pos[k]) * g.hkv + h) * D + d] : dst[k];
+    // (a slot no token of this call keeps holds its previous value)
+    if constexpr (sizeof(T) == 2) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)__builtin_bit_cast(uint16_t, val[2 * e]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, val[2 * e + 1]) << 16);
+      *reinterpret_cast<u32x4*>(dst) = w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dst[k] = val[k];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.num_seqs * a.tokens_per_seq;
   if (items == 0) return hipSuccess;
+  if (a.tokens_per_seq >= kBulkAppendTokens) {
+    const dim3 grid((uint32_t)((int64_t)a.num_seqs * (a.geom.slot_capacity >> 3))), block(64);
+    if (a.dtype == PS_BF16)
+      hipLaunchKernelGGL(append_block_kernel<uint16_t>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(append_block_kernel<float>, grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 grid((uint32_t)items), block(64);
   if (a.dtype == PS_BF16)
     hipLaunchKernelGGL(append_kernel<uint16_t>, grid, block, 0, stream, a);

@@ -253,3 +253,56 @@ def test_full_attention_comparator_is_the_same_kernel(ps):
                       torch.tensor([p], device="cuda"), to_dev(q, torch.bfloat16), out, num_splits=8)
     want = oracle.decode_attention(q[0], k, v, p, 0, 1 << 30, 1 / math.sqrt(d), 10000.0)
     assert normwise_err(out.float().cpu().numpy()[0], want) <= BF16_TOL
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("paged", [False, True])
+def test_append_calls_of_mixed_lengths_keep_the_ring_exact(ps, dtype, paged):
+    """Appends of 1..70 tokens per call (short calls take the per-token path,
+    long ones the 8-slot block path, which rewrites partly covered blocks):
+    after every call the ring holds exactly A(p) -- K rotated at its position,
+    V bit-exact, the slot map bit-exact -- including prefix/window blocks that
+    straddle (L = 13) and the ring wrapping inside a call (W = 45)."""
+    L, W, hkv, d, theta = 13, 45, 2, 64, 10000.0
+    cap = 64
+    pt = ps.PS_F32 if dtype == "f32" else ps.PS_BF16
+    attn = ps.AttnSpec(2 * hkv, hkv, d, pt, theta, 0.125)
+    bt = None
+    if paged:
+        bt, num_pages = paged_table(1, cap // 64, seed=9)
+        cache = ps.CacheSpec(window=W, slot_capacity=cap, page_size=64, num_pages=num_pages)
+    else:
+        cache = ps.CacheSpec(window=W, slot_capacity=cap)
+    total = 400
+    k, v = _hist(5, 31, 0, total, hkv, d, 1.0, dtype)
+    kc, vc = new_cache(ps, attn, cache, 1)
+    slot_pos = torch.full((1, cap), -1, dtype=torch.int32, device="cuda")
+    pl = torch.tensor([L], dtype=torch.int32, device="cuda")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    rng = np.random.default_rng(3)
+    p = 0
+    calls = 0
+    while p < total:
+        n = int(min(total - p, rng.choice([1, 3, 8, 15, 16, 17, 33, 45, 46, 70])))
+        ps.ps_kv_append(attn, cache, kc, vc, pl, torch.tensor([p], dtype=torch.int64, device="cuda"),
+                        to_dev(k[p:p + n][None], tdt), to_dev(v[p:p + n][None], tdt), block_table=bt,
+                        slot_pos=slot_pos)
+        p += n
+        calls += 1
+        ring = oracle.simulate_ring(range(p), L, W, cap)
+        np.testing.assert_array_equal(slot_pos.cpu().numpy()[0], ring)
+        kf, vf = kc.float().cpu().numpy(), vc.float().cpu().numpy()
+        if paged:
+            page = int(bt.cpu().numpy()[0, 0])
+            kg, vg = kf[page, 0], vf[page, 0]
+        else:
+            kg, vg = kf[0, 0], vf[0, 0]
+        vg = vg.transpose(0, 2, 1).reshape(-1, d)
+        for slot, pos in enumerate(ring):
+            if pos < 0:
+                continue
+            want_k = oracle.rope(k[pos, 0], pos, theta)
+            tol = 2e-6 if dtype == "f32" else 2 ** -7 * np.abs(want_k).max()
+            np.testing.assert_allclose(kg[slot], want_k, rtol=0, atol=tol, err_msg=f"call {calls} slot {slot}")
+            np.testing.assert_array_equal(vg[slot], v[pos, 0], err_msg=f"call {calls} slot {slot}")
+    assert calls > 10
