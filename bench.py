@@ -56,7 +56,8 @@ def parse():
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunk prefill that reads the ring")
     ap.add_argument("--no-backward", action="store_true", help="skip the masked prefill backward")
     ap.add_argument("--no-heavy", action="store_true", help="skip prefix + heavy hitters + window decoding")
-    ap.add_argument("--only", choices=["decode", "prefill", "chunk", "backward", "heavy"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "chunk", "backward", "heavy", "batch-sweep"],
+                    default=None,
                     help="run only one leg (for profiling); the JSON line then carries that leg only")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run one device-to-device copy of BYTES first (reference for HBM counter scaling)")
@@ -312,6 +313,36 @@ def run_sweep(ps, torch, num_seqs=256, layers=28, reps=10):
                         "tok_s": round(num_seqs / (t * layers), 1), "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)})
         rows[label] = res
         del k, v, ws
+        torch.cuda.empty_cache()
+    return rows
+
+
+def run_batch_sweep(ps, torch, layers=28, reps=20):
+    """Decode-kernel time per layer against the number of sequences at 131072
+    (prefix 100, W = 4096), with the library's automatic split count: where
+    the kernel reaches its bandwidth plateau as the batch grows."""
+    attn = ps.AttnSpec(16, 2, 128, ps.PS_BF16, 10000.0, 1 / math.sqrt(128))
+    cache = ps.CacheSpec(window=4096, slot_capacity=4224)
+    g = torch.Generator(device="cuda").manual_seed(17)
+    p, n_vis = 131072, 4196
+    rows = []
+    for n in (8, 16, 32, 64, 128, 256, 512, 1024):
+        ks, vs = ps.cache_shapes(attn, cache, n)
+        k = torch.empty(ks, dtype=torch.bfloat16, device="cuda").normal_(0, 0.5, generator=g)
+        v = torch.empty(vs, dtype=torch.bfloat16, device="cuda").normal_(0, 0.5, generator=g)
+        q = torch.randn((n, 16, 128), generator=g, device="cuda").bfloat16()
+        out = torch.empty_like(q)
+        pl = torch.full((n,), 100, dtype=torch.int32, device="cuda")
+        pos = torch.full((n,), p, dtype=torch.int64, device="cuda")
+        ws = torch.empty(max(ps.ps_decode_workspace_size(attn, cache, n, 0), 1), dtype=torch.uint8, device="cuda")
+        run = lambda kk: [ps.ps_decode_attn(attn, cache, k, v, pl, pos, q, out, workspace=ws) for _ in range(kk)]
+        run(3)
+        t = timed(torch, run, reps) / reps
+        nbytes = n * (n_vis * 2 * 128 * 2 * 2 + 16 * 128 * 4)
+        rows.append({"num_seqs": n, "splits": ps.ps_decode_num_splits(attn, cache, n), "us_per_layer": round(t * 1e6, 2),
+                     "tok_s": round(n / (t * layers), 1), "hbm_gbs": round(nbytes / t / 1e9, 1),
+                     "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)})
+        del k, v, q, out, ws
         torch.cuda.empty_cache()
     return rows
 
@@ -722,6 +753,9 @@ def main():
         return
     if args.only == "backward":
         print(json.dumps({"prefill_backward": run_backward(ps, torch)}))
+        return
+    if args.only == "batch-sweep":
+        print(json.dumps({"decode_batch_sweep": run_batch_sweep(ps, torch)}))
         return
     if args.only == "heavy":
         print(json.dumps({"heavy_hitters": run_heavy(ps, torch)}))

@@ -321,3 +321,15 @@ def test_read_probe_validation(lib):
     assert lib.ps_read_probe(ctypes.c_void_p(0x1008), 16, FAKE, None) == 1    # src not 16-byte aligned
     assert b"aligned" in lib.ps_last_error()
     assert lib.ps_read_probe(FAKE, (1 << 40) + 16, FAKE, None) == 1
+
+
+def test_automatic_split_count(lib):
+    """The split count minimises the waves of one workgroup per CU times the
+    share of keys per split (ties: fewer splits); without a GPU the library
+    assumes 256 CUs.  At capacity 4224 a split keeps at least 512 keys."""
+    a, c = _descs(cap=4224)
+    got = [lib.ps_decode_num_splits(ctypes.byref(a), ctypes.byref(c), n) for n in (8, 16, 32, 64, 96, 128, 192, 256,
+                                                                                   1024)]
+    assert got == [8, 8, 4, 2, 4, 1, 2, 1, 1]
+    a, c = _descs(cap=128)
+    assert lib.ps_decode_num_splits(ctypes.byref(a), ctypes.byref(c), 1) == 1
