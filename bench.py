@@ -3,13 +3,14 @@
 
 Workload (default): decode at position 131072 with a 100-token prefix and a
 4096-token window -- 256 sequences, 28 layers, Hq=16, Hkv=2, head_dim=128,
-bf16 (a Qwen3-1.7B attention geometry).  One step = for every layer, append
-the new token's K/V (RoPE at its absolute position) into the ring and run
-split-KV decode attention over the ring.  Timed: K steps after W warm-up
-steps, inputs resident in HBM, positions advancing by one per step.
+bf16 (a Qwen3-1.7B attention geometry).  One step = for every layer,
+ps_decode_step: append the new token's K/V (RoPE at its absolute position)
+into the ring and run split-KV decode attention over it, one launch.  Timed:
+K steps after W warm-up steps, inputs resident in HBM, positions advancing by
+one per step.
 
 Printed (one JSON line): whole-job decode tok/s, the roofline of the decode
-attention kernel (algorithmic HBM bytes per launch / average launch time,
+step kernel (algorithmic HBM bytes per launch / average launch time,
 against 8 TB/s), the float64 CPU oracle timed on a bounded sample of the
 same workload, the masked prefill kernel (truncated-backprop chunk: 8 x 8192
 queries behind a 100-token prefix, W=2048, Hq=28, Hkv=4) in TFLOP/s against
@@ -124,9 +125,8 @@ class DecodeBench:
         pos = self.pos[s]
         for li in range(self.layers):
             i = (s * self.layers + li) % self.pool
-            ps.ps_kv_append(self.attn, self.cache, self.k[li], self.v[li], self.pl, pos, self.kn[i], self.vn[i])
-            ps.ps_decode_attn(self.attn, self.cache, self.k[li], self.v[li], self.pl, pos, self.q[i], self.out,
-                              num_splits=self.splits, workspace=self.ws)
+            ps.ps_decode_step(self.attn, self.cache, self.k[li], self.v[li], self.pl, pos, self.q[i], self.kn[i],
+                              self.vn[i], self.out, num_splits=self.splits, workspace=self.ws)
 
     def decode_only(self, reps, pos):
         ps = self.ps
@@ -141,6 +141,11 @@ class DecodeBench:
         """Algorithmic HBM bytes of one decode-attention launch (one layer): the
         visible K/V rows, the queries and the outputs."""
         return self.n * (self.n_vis(p) * 2 * 128 * 2 * 2 + 16 * 128 * 2 * 2)
+
+    def step_kernel_bytes(self, p):
+        """Algorithmic HBM bytes of one decode-step launch (one layer): the
+        attention's bytes plus the new token's K and V, read and written."""
+        return self.kernel_bytes(p) + self.n * 2 * 2 * 128 * 2 * 2
 
     def release(self):
         self.k.clear()
@@ -176,11 +181,11 @@ def run_decode(ps, torch, args):
     wall = time.perf_counter() - t0
     gpu_s = start.elapsed_time(end) / 1000.0
     elapsed = max(wall, gpu_s)
-    # dominant kernel: the decode-attention launches of the step loop.  The
-    # timed steps are replayed once more (same workload, next positions) with a
-    # pair of HIP events on the launch stream around every decode launch; the
-    # average is the kernel's in-step launch duration.  `value` above comes
-    # from the plain, un-instrumented steps.
+    # dominant kernel: the decode-step launches of the step loop (append fused
+    # into the decode kernel).  The timed steps are replayed once more (same
+    # workload, next positions) with a pair of HIP events on the launch stream
+    # around every launch; the average is the kernel's in-step launch duration.
+    # `value` above comes from the plain, un-instrumented steps.
     n_steps = args.steps
     evs = []
     torch.cuda.synchronize()
@@ -188,17 +193,16 @@ def run_decode(ps, torch, args):
         pos = bench.pos[s_]
         for li in range(bench.layers):
             i = (s_ * bench.layers + li) % bench.pool
-            ps.ps_kv_append(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, pos, bench.kn[i], bench.vn[i])
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            ps.ps_decode_attn(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, pos, bench.q[i], bench.out,
-                              num_splits=bench.splits, workspace=bench.ws)
+            ps.ps_decode_step(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, pos, bench.q[i],
+                              bench.kn[i], bench.vn[i], bench.out, num_splits=bench.splits, workspace=bench.ws)
             e1.record()
             evs.append((e0, e1))
     torch.cuda.synchronize()
     kt = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs) / 1000.0
     p_last = args.position + args.warmup + 2 * args.steps - 1
-    kbytes = bench.kernel_bytes(p_last)
+    kbytes = bench.step_kernel_bytes(p_last)
     # the same step captured once in a HIP graph (28 x append + decode, then the
     # positions advance inside the graph) and replayed: what a serving loop that
     # captures its decode step would see
@@ -207,9 +211,8 @@ def run_decode(ps, torch, args):
     def graph_step():
         for li in range(bench.layers):
             i = li % bench.pool
-            ps.ps_kv_append(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, gpos, bench.kn[i], bench.vn[i])
-            ps.ps_decode_attn(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, gpos, bench.q[i], bench.out,
-                              num_splits=bench.splits, workspace=bench.ws)
+            ps.ps_decode_step(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, gpos, bench.q[i],
+                              bench.kn[i], bench.vn[i], bench.out, num_splits=bench.splits, workspace=bench.ws)
         gpos.add_(1)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -812,7 +815,7 @@ def main():
                    "hq": 16, "hkv": 2, "head_dim": 128, "splits": dec["splits"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(dec["kernel_bytes"]),
-                     "kernel": "decode_bf16_kernel", "kernel_us": dec["kernel_s"] * 1e6,
+                     "kernel": "decode_bf16_kernel (append fused)", "kernel_us": dec["kernel_s"] * 1e6,
                      "kernel_launches_timed": dec["kernel_launches"],
                      "bytes_per_launch": dec["kernel_bytes"],
                      "measured_read_gbs": ceil["hbm_read_gbs"], "frac_of_measured_read": achieved / ceil["hbm_read_gbs"]},

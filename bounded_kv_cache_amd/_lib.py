@@ -36,6 +36,7 @@ _pC = ctypes.POINTER(CacheDesc)
 SIGNATURES = {
     "ps_kv_append": (_i32, [_pA, _pC, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp]),
     "ps_decode_attn": (_i32, [_pA, _pC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _sz, _vp]),
+    "ps_decode_step": (_i32, [_pA, _pC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _sz, _vp]),
     "ps_decode_num_splits": (_i32, [_pA, _pC, _i32]),
     "ps_decode_workspace_size": (_sz, [_pA, _pC, _i32, _i32]),
     "ps_prefill_attn": (_i32, [_pA, _i32, _i32, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),

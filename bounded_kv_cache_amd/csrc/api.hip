@@ -295,7 +295,7 @@ ps_status ps_kv_append(const ps_attn_desc* attn, const ps_cache_desc* cache, voi
     return fail(PS_INVALID_ARGUMENT, "num_seqs*tokens_per_seq exceeds 2^26 per call");
   if (!k_cache || !v_cache || !prefix_len || !start_pos || !k_new || !v_new)
     return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
-  ps::AppendArgs a;
+  ps::AppendArgs a{};
   a.geom = make_geom(attn, cache);
   a.dtype = attn->dtype;
   a.k_cache = k_cache;
@@ -327,10 +327,12 @@ size_t ps_decode_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* c
   return decode_ws_bytes(attn, num_seqs, s);
 }
 
-ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, const void* k_cache,
-                         const void* v_cache, const int32_t* block_table, const int32_t* prefix_len, const int64_t* pos,
-                         const void* q, void* out, int32_t num_seqs, int32_t num_splits, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+namespace {
+// ps_decode_attn, and with k_new / v_new the fused append of ps_decode_step
+ps_status decode_call(const ps_attn_desc* attn, const ps_cache_desc* cache, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* prefix_len, const int64_t* pos, const void* q,
+                      void* out, int32_t num_seqs, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream, const void* k_new, const void* v_new, bool dry = false) {
   ps_status st = check_attn(attn);
   if (st != PS_OK) return st;
   if ((st = check_cache(cache, block_table)) != PS_OK) return st;
@@ -350,7 +352,8 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, c
                                 : decode_ws_bytes(attn, num_seqs, splits);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PS_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
-  ps::DecodeArgs a;
+  if (dry) return ok();   // validation only
+  ps::DecodeArgs a{};
   a.geom = make_geom(attn, cache);
   a.dtype = attn->dtype;
   a.hq = attn->num_q_heads;
@@ -378,10 +381,12 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, c
   a.stat_scores = nullptr;
   a.stat_max = nullptr;
   a.stat_lse2 = nullptr;
+  a.k_new = k_new;
+  a.v_new = v_new;
   if (recompute) {   // rotate the visible keys at their renumbered positions, then decode the copy
     const RecomputeLayout l = recompute_layout(attn, cache, num_seqs, splits);
     char* w = static_cast<char*>(workspace);
-    ps::ResetArgs r;
+    ps::ResetArgs r{};
     r.geom = a.geom;
     r.dtype = attn->dtype;
     r.num_seqs = num_seqs;
@@ -399,6 +404,37 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, c
     a.reset_pe = 0;
   }
   return from_hip(ps::launch_decode(a, stream), "ps_decode_attn launch");
+}
+}  // namespace
+
+ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table, const int32_t* prefix_len, const int64_t* pos,
+                         const void* q, void* out, int32_t num_seqs, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return decode_call(attn, cache, k_cache, v_cache, block_table, prefix_len, pos, q, out, num_seqs, num_splits,
+                     workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+ps_status ps_decode_step(const ps_attn_desc* attn, const ps_cache_desc* cache, void* k_cache, void* v_cache,
+                         const int32_t* block_table, const int32_t* prefix_len, const int64_t* pos, const void* q,
+                         const void* k_new, const void* v_new, void* out, int32_t num_seqs, int32_t num_splits,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ps_status st = check_attn(attn);
+  if (st != PS_OK) return st;
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if (attn->dtype == PS_BF16 && attn->pe_mode == PS_PE_CONTINUE)   // one launch: append inside the decode kernel
+    return decode_call(attn, cache, k_cache, v_cache, block_table, prefix_len, pos, q, out, num_seqs, num_splits,
+                       workspace, workspace_bytes, stream, k_new, v_new);
+  // other dtypes and PE modes: the append, then the decode, as two launches
+  // everything the decode checks is checked before the append runs
+  if ((st = decode_call(attn, cache, k_cache, v_cache, block_table, prefix_len, pos, q, out, num_seqs, num_splits,
+                        workspace, workspace_bytes, stream, nullptr, nullptr, true)) != PS_OK)
+    return st;
+  if ((st = ps_kv_append(attn, cache, k_cache, v_cache, block_table, prefix_len, pos, nullptr, 1, k_new, v_new,
+                         num_seqs, nullptr, stream)) != PS_OK)
+    return st;
+  return decode_call(attn, cache, k_cache, v_cache, block_table, prefix_len, pos, q, out, num_seqs, num_splits,
+                     workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 size_t ps_heavy_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* cache, int32_t num_seqs,
@@ -442,7 +478,7 @@ ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* ca
   float* stat_lse2 = reinterpret_cast<float*>(w + hl.lse2);
   const ps::CacheGeom geom = make_geom(attn, cache);
   const ps::RopeFreq rope = make_rope(attn);
-  ps::HeavyArgs h;
+  ps::HeavyArgs h{};
   h.geom = geom;
   h.dtype = attn->dtype;
   h.hq = attn->num_q_heads;
@@ -466,7 +502,7 @@ ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* ca
   // 1-2. the token leaving the window (admission), then the new token into the ring
   hipError_t e = ps::launch_heavy_retire(h, stream);
   if (e != hipSuccess) return from_hip(e, "ps_heavy_decode_step retire launch");
-  ps::DecodeArgs a;                                     // 3. attention over prefix + window + heavy slots
+  ps::DecodeArgs a{};   // 3. attention over prefix + window + heavy slots
   a.geom = geom;
   a.dtype = attn->dtype;
   a.hq = attn->num_q_heads;
@@ -494,6 +530,8 @@ ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* ca
   a.stat_max = fused ? nullptr : stat_max;
   a.stat_lse2 = fused ? nullptr : stat_lse2;
   a.heavy_score = fused ? score : nullptr;   // fused: the decode kernel also does step 4
+  a.k_new = nullptr;   // the token is appended by the retire kernel above
+  a.v_new = nullptr;
   if ((e = ps::launch_decode(a, stream)) != hipSuccess) return from_hip(e, "ps_heavy_decode_step decode launch");
   if (fused) return ok();
   return from_hip(ps::launch_heavy_accumulate(h, stream), "ps_heavy_decode_step accumulate launch");  // 4.
@@ -537,7 +575,7 @@ ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t pref
   ps::prefill_tile_shape(attn->dtype, attn->head_dim, &bm, &bn);
   if ((int64_t)batch * attn->num_q_heads * ((num_queries + bm - 1) / bm) + 8 > (int64_t)1 << 31)
     return fail(PS_INVALID_ARGUMENT, "prefill grid too large");
-  ps::PrefillArgs a;
+  ps::PrefillArgs a{};
   a.dtype = attn->dtype;
   a.hq = attn->num_q_heads;
   a.hkv = attn->num_kv_heads;
@@ -601,7 +639,7 @@ ps_status ps_prefill_attn_backward(const ps_attn_desc* attn, int32_t window, int
   if (!workspace || workspace_bytes < l.total)
     return fail(PS_WORKSPACE_TOO_SMALL, "backward needs %zu workspace bytes, got %zu", l.total, workspace_bytes);
   char* w = static_cast<char*>(workspace);
-  ps::BackwardArgs a;
+  ps::BackwardArgs a{};
   a.dtype = attn->dtype;
   a.hq = attn->num_q_heads;
   a.hkv = attn->num_kv_heads;
@@ -675,7 +713,7 @@ ps_status ps_chunk_prefill_attn(const ps_attn_desc* attn, const ps_cache_desc* c
   if (attn->dtype == PS_BF16 && nkp > kMaxBf16PrefillKeys)
     return fail(PS_INVALID_ARGUMENT, "bf16 chunk prefill takes at most 2^28 keys per sequence");
   const size_t kv = 2 * (size_t)num_seqs * attn->num_kv_heads * nkp * attn->head_dim * elem;
-  ps::PrefillArgs a;
+  ps::PrefillArgs a{};
   a.dtype = attn->dtype;
   a.hq = attn->num_q_heads;
   a.hkv = attn->num_kv_heads;
@@ -708,7 +746,7 @@ ps_status ps_chunk_prefill_attn(const ps_attn_desc* attn, const ps_cache_desc* c
   hipError_t e = ps::launch_chunk_prefill(a, stream);
   if (e != hipSuccess) return from_hip(e, "ps_chunk_prefill_attn launch");
   // the chunk joins the ring only after every chunk query has read the ring
-  ps::AppendArgs ap;
+  ps::AppendArgs ap{};
   ap.geom = a.cg;
   ap.dtype = attn->dtype;
   ap.k_cache = k_cache;

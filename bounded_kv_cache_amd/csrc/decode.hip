@@ -60,7 +60,9 @@ __device__ inline u32x4 stream_load(const uint16_t* p) {
 // kStats (heavy-hitter mode): 0 off; 1 per-slot statistics to HBM for the
 // accumulate kernel; 2 statistics kept in LDS and the scores accumulated here
 // (one workgroup per CU, the whole sequence in one split).
-template <int D, int NW, bool kReset, int kStats>
+// kAppend: the step's token (k_new / v_new at pos) is appended by this kernel
+// (one launch per decode step instead of an append launch and a decode launch).
+template <int D, int NW, bool kReset, int kStats, bool kAppend = false>
 __global__ __launch_bounds__(NW * 64, kStats == 2 ? 1 : PS_DECODE_MIN_BLOCKS) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NC = D / 32;   // QK k-steps (32 dims each)
   constexpr int NDT = D / 16;  // PV d-tiles (16 dims each)
@@ -357,6 +359,40 @@ __global__ __launch_bounds__(NW * 64, kStats == 2 ? 1 : PS_DECODE_MIN_BLOCKS) vo
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int i = 0; i < 8; ++i) qop[c][i] = (bf16)(qv[c][i] * a.scale_log2);
+  }
+
+  // ---- kAppend: the token at pos goes to its ring slot (the append rule:
+  // dropped for an invalid sequence or a slot beyond the capacity), written by
+  // the wave that will read that slot's chunk, while its first chunk's loads
+  // are in flight.  Vector memory operations of a wave complete in order, so
+  // a load it issues after a later wait sees the token; if the slot's chunk is
+  // the first one (already loaded) it is loaded again, and if it is the second
+  // one (loaded at the top of the loop) the stores are waited for first. ----
+  if (kAppend && L >= 0 && pos >= 0) {
+    const int32_t sn = ring_slot(pos, L, geo.window);
+    const int ci_new = sn >> 5;
+    if (sn < geo.slot_capacity && sn / a.split_keys == split && ci_new >= c && (ci_new - c) % NW == 0) {
+      const int64_t base = region_offset(geo, a.block_table, s, h, sn);
+      if (base >= 0) {
+        const uint16_t* kn = static_cast<const uint16_t*>(a.k_new) + ((int64_t)s * geo.hkv + h) * D;
+        const uint16_t* vn = static_cast<const uint16_t*>(a.v_new) + ((int64_t)s * geo.hkv + h) * D;
+        uint16_t* kw = const_cast<uint16_t*>(kc) + base;
+        uint16_t* vw = const_cast<uint16_t*>(vc) + base;
+        for (int i = lane; i < D / 2; i += 64) {   // rotate-half pair (i, i + D/2), as the append kernel
+          const float x1 = bf16_to_f32(kn[i]), x2 = bf16_to_f32(kn[i + D / 2]);
+          float cs = 1.f, sn_ = 0.f;
+          if (a.rope.enabled) rope_cos_sin(pos, a.rope.inv_freq[i], cs, sn_);
+          kw[k_in_region(sn, i, D)] = f32_to_bf16_bits(x1 * cs - x2 * sn_);
+          kw[k_in_region(sn, i + D / 2, D)] = f32_to_bf16_bits(x2 * cs + x1 * sn_);
+          vw[v_in_region(sn, i, D)] = vn[i];
+          vw[v_in_region(sn, i + D / 2, D)] = vn[i + D / 2];
+        }
+        if (ci_new - c < 2 * NW) {
+          __builtin_amdgcn_s_waitcnt(0);   // the stores (and the first chunk's loads) are complete
+          if (ci_new == c) load_chunk(c, kA, vA);
+        }
+      }
+    }
   }
 
   while (c < c_end) {
@@ -666,6 +702,8 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     if (a.heavy_score)
       hipLaunchKernelGGL((decode_bf16_kernel<D, kFusedStatsWaves, false, 2>), grid, dim3(kFusedStatsWaves * 64), 0,
                          stream, a);
+    else if (a.k_new)
+      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, 0, true>), grid, dim3(NW * 64), 0, stream, a);
     else if (a.heavy_count)
       hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, 1>), grid, dim3(NW * 64), 0, stream, a);
     else if (a.reset_pe)

@@ -57,6 +57,10 @@ struct DecodeArgs {
   // bf16, one split, statistics fit kFusedStatsLds: the decode kernel keeps the statistics in LDS and
   // adds the step's attention mass to these scores itself ([num_seqs][hkv][slot_capacity]); else NULL
   float* heavy_score;
+  // bf16, Continue PE: the step's token [num_seqs][1][hkv][D] at pos, appended by the decode kernel
+  // itself (k_cache / v_cache are then written); NULL otherwise
+  const void* k_new;
+  const void* v_new;
 };
 
 // Heavy-hitter bookkeeping around a decode step.

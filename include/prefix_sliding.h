@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 7
+#define PS_ABI_VERSION 8
 
 typedef enum {
   PS_OK = 0,
@@ -179,6 +179,21 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache,
                          const int32_t* prefix_len, const int64_t* pos,
                          const void* q, void* out, int32_t num_seqs, int32_t num_splits,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ps_decode_step -- one decode step: ps_kv_append of the token at pos
+ * (k_new, v_new: [num_seqs][1][Hkv][D]) followed by ps_decode_attn at pos,
+ * with the same arguments, rules and results (the same ring contents; the
+ * output within the decode tolerance of the two calls made in turn).  For
+ * bf16 and Continue PE it is one launch: the decode kernel writes the token
+ * into its ring slot and attends to it from registers.  Other dtypes and PE
+ * modes run the two calls.  Every argument is validated before anything is
+ * enqueued.  Same workspace as ps_decode_attn. */
+ps_status ps_decode_step(const ps_attn_desc* attn, const ps_cache_desc* cache,
+                         void* k_cache, void* v_cache, const int32_t* block_table,
+                         const int32_t* prefix_len, const int64_t* pos, const void* q,
+                         const void* k_new, const void* v_new, void* out, int32_t num_seqs,
+                         int32_t num_splits, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /* Split count ps_decode_attn uses for num_splits == 0 (queries the current
  * device; assumes 256 CUs when none is visible).  Returns >= 1, or 0 on

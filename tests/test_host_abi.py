@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ps_abi_version() == 7
+    assert lib.ps_abi_version() == 8
     assert lib.ps_status_string(0) == b"ok"
     assert lib.ps_status_string(3) == b"workspace too small"
 
@@ -333,3 +333,25 @@ def test_automatic_split_count(lib):
     assert got == [8, 8, 4, 2, 4, 1, 2, 1, 1]
     a, c = _descs(cap=128)
     assert lib.ps_decode_num_splits(ctypes.byref(a), ctypes.byref(c), 1) == 1
+
+
+def test_decode_step_validation(lib):
+    """ps_decode_step checks everything (its own pointers and every decode
+    argument) before anything is enqueued, on both the one-launch and the
+    two-call paths."""
+    for dtype in (0, 1):
+        a, c = _descs(dtype=dtype)
+        assert lib.ps_decode_step(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE,
+                                  FAKE, 4, 1, None, 0, None) == 1                      # k_new NULL
+        assert lib.ps_decode_step(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, 4, 3, FAKE, 1, None) == 3                      # workspace too small
+        assert lib.ps_decode_step(ctypes.byref(a), ctypes.byref(c), None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, 4, 1, None, 0, None) == 1                      # cache NULL
+        assert lib.ps_decode_step(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, 4, 500, FAKE, 1 << 40, None) == 1              # too many splits
+    a, c = _descs(pe=2, page=64, mp=66, npages=1000)
+    assert lib.ps_decode_step(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, 4, 1, FAKE, 1 << 40, None) == 2                    # recompute needs contiguous
+    a, c = _descs()
+    assert lib.ps_decode_step(ctypes.byref(a), ctypes.byref(c), None, None, None, None, None, None, None, None,
+                              None, 0, 1, None, 0, None) == 0                          # no sequences
