@@ -203,7 +203,7 @@ def run_decode(ps, torch, args):
     kt = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs) / 1000.0
     p_last = args.position + args.warmup + 2 * args.steps - 1
     kbytes = bench.step_kernel_bytes(p_last)
-    # the same step captured once in a HIP graph (28 x append + decode, then the
+    # the same step captured once in a HIP graph (28 decode steps, then the
     # positions advance inside the graph) and replayed: what a serving loop that
     # captures its decode step would see
     gpos = bench.pos[args.warmup + 2 * args.steps - 1].clone()
@@ -821,7 +821,7 @@ def main():
                      "measured_read_gbs": ceil["hbm_read_gbs"], "frac_of_measured_read": achieved / ceil["hbm_read_gbs"]},
         "ceilings": ceil,
         "decode_step_in_hip_graph": {"tok_s": dec["graph_tok_s"], "ms_per_step": dec["graph_ms_per_step"],
-                                     "note": "the timed step captured once (28 x append + decode + position "
+                                     "note": "the timed step captured once (28 x ps_decode_step + position "
                                              "advance) and replayed; value is the eager loop"},
         "cpu_baseline": cpu,
         "cpu_baseline_prefill": cpu_prefill,
