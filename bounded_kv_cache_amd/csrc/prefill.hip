@@ -547,9 +547,16 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
   // prefix and band ranges are exact except at their ends) is treated as a
   // partly visible tile whose mask hides everything, which keeps the walk free
   // of data-dependent loops.  Loads past the last candidate repeat it.
+  // prefix candidates: the general classification; band candidates: one
+  // precomputed range of fully visible tiles
+  const FullRange full = pf_band_full_range(geo, it.qt);
   auto kind_at = [&](int32_t ci) {
-    const int k = pf_classify(geo, it.qt, cand_tile(ci));
-    return k == 0 ? 2 : k;
+    if (ci < tr.n_prefix) {
+      const int k = pf_classify(geo, it.qt, ci);
+      return k == 0 ? 2 : k;
+    }
+    const int32_t kt = tr.band_lo + (ci - tr.n_prefix);
+    return (kt >= full.lo && kt <= full.hi) ? 1 : 2;
   };
   auto tile_at = [&](int32_t ci) { return cand_tile(ci < n_cand ? ci : n_cand - 1); };
 

@@ -73,6 +73,25 @@ PS_HD inline int pf_classify(const PrefillGeom& g, int32_t qt, int32_t kt) {
   return (all && whole) ? 1 : 2;
 }
 
+// Band tiles (k-tiles at or after n_prefix) hold chunk keys only; such a tile
+// is fully visible to every query of q-tile qt iff its first key is inside the
+// window of the tile's last query and its last key is at or before its first
+// query, and both tiles are whole: one range [lo, hi] of k-tile indices (empty
+// when lo > hi).  Equal to pf_classify(g, qt, kt) == 1 for every band tile.
+struct FullRange {
+  int32_t lo, hi;
+};
+PS_HD inline FullRange pf_band_full_range(const PrefillGeom& g, int32_t qt) {
+  FullRange r{0, -1};
+  const int32_t t0 = qt * g.bm;
+  if (t0 + g.bm > g.T) return r;                      // the q-tile is not whole
+  const int32_t u0 = g.Nk - g.T + t0, u1 = u0 + g.bm - 1;
+  const int64_t first = (int64_t)u1 - g.W + 1;        // first key the last query sees
+  r.lo = first <= 0 ? 0 : (int32_t)((first + g.bn - 1) / g.bn);
+  r.hi = pf_min((u0 + 1) / g.bn - 1, g.Nk / g.bn - 1);
+  return r;
+}
+
 // Candidate k-tiles of q-tile qt: [0, n_prefix) then [band_lo, band_hi]
 // (band_lo >= n_prefix; empty when band_lo > band_hi).
 struct TileRange {

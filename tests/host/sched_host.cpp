@@ -34,3 +34,21 @@ extern "C" int ps_host_classify_all(int T, int Nk, int L, int W, long long kv_st
   return nqt * nkt;
 }
 
+
+// For every band tile of every q-tile: 1 when pf_band_full_range contains it
+// and pf_classify calls it fully visible, 2 when neither, -1 on disagreement.
+extern "C" int ps_host_full_range_check(int T, int Nk, int L, int W, long long kv_start, int bm, int bn) {
+  ps::PrefillGeom g{T, Nk, L, W, kv_start, bm, bn};
+  const int nqt = ps::pf_num_qtiles(g);
+  int checked = 0;
+  for (int qt = 0; qt < nqt; ++qt) {
+    const ps::TileRange r = ps::pf_tile_range(g, qt);
+    const ps::FullRange f = ps::pf_band_full_range(g, qt);
+    for (int kt = r.band_lo; kt <= r.band_hi; ++kt) {
+      const bool full = ps::pf_classify(g, qt, kt) == 1;
+      if (full != (kt >= f.lo && kt <= f.hi)) return -1;
+      ++checked;
+    }
+  }
+  return checked;
+}

@@ -355,3 +355,24 @@ def test_decode_step_validation(lib):
     a, c = _descs()
     assert lib.ps_decode_step(ctypes.byref(a), ctypes.byref(c), None, None, None, None, None, None, None, None,
                               None, 0, 1, None, 0, None) == 0                          # no sequences
+
+
+def test_band_full_range_equals_the_classification(sched):
+    """The attention kernel marks band tiles fully visible from one closed-form
+    index range; it must agree with the general classification on every band
+    tile, over random geometries (warm-up, ragged ends, W >= n, tiny tiles)."""
+    sched.ps_host_full_range_check.restype = ctypes.c_int
+    sched.ps_host_full_range_check.argtypes = [ctypes.c_int] * 4 + [ctypes.c_longlong, ctypes.c_int, ctypes.c_int]
+    rng = np.random.default_rng(11)
+    total = 0
+    for _ in range(400):
+        L = int(rng.integers(0, 300))
+        T = int(rng.integers(1, 700))
+        W = int(rng.choice([1, 2, 7, 33, 64, 100, 257, 1 << 30]))
+        start = L + int(rng.integers(0, 500)) if rng.random() < 0.7 else L
+        nk = L + (start - L) + T
+        bm, bn = [(128, 64), (64, 64), (32, 16), (16, 32)][int(rng.integers(0, 4))]
+        n = sched.ps_host_full_range_check(T, nk, L, W, start, bm, bn)
+        assert n >= 0, (T, nk, L, W, start, bm, bn)
+        total += n
+    assert total > 10000
