@@ -90,6 +90,39 @@ def test_decode_step_trace(ps, dtype, case, paged, splits):
     np.testing.assert_allclose(a_[both], b_[both], rtol=2 ** -7 if dtype == "bf16" else 1e-6, atol=1e-6)
 
 
+def test_decode_step_head_dim_64(ps):
+    """head_dim 64 (two QK k-steps, 32 rotation pairs per token) through the
+    one-launch step, 80 steps from warm-up past the window, vs the oracle."""
+    hq, hkv, d, L, W, steps = 8, 1, 64, 9, 70, 80
+    starts = [0, 50, 300]
+    n = len(starts)
+    cap = -(-(L + W) // 64) * 64
+    attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16, 10000.0, 1 / math.sqrt(d))
+    cache = ps.CacheSpec(window=W, slot_capacity=cap)
+    last = [p + steps for p in starts]
+    hist = [(synth.history(8, 300, synth.T_K, s, 0, 0, last[s], hkv, d, 0.5, "bf16"),
+             synth.history(8, 300, synth.T_V, s, 0, 0, last[s], hkv, d, 0.5, "bf16")) for s in range(n)]
+    qs = [synth.history(8, 300, synth.T_Q, s, 0, 0, last[s], hq, d, 1.0, "bf16") for s in range(n)]
+    kc, vc = new_cache(ps, attn, cache, n)
+    fill_ring(ps, attn, cache, kc, vc, [L] * n, [p - 1 for p in starts], [h[0] for h in hist], [h[1] for h in hist])
+    pl = torch.full((n,), L, dtype=torch.int32, device="cuda")
+    out = torch.empty((n, hq, d), dtype=torch.bfloat16, device="cuda")
+    worst = 0.0
+    for i in range(steps):
+        p = [starts[s] + i for s in range(n)]
+        ps.ps_decode_step(attn, cache, kc, vc, pl, torch.tensor(p, dtype=torch.int64, device="cuda"),
+                          to_dev(np.stack([qs[s][p[s]] for s in range(n)]), torch.bfloat16),
+                          to_dev(np.stack([hist[s][0][p[s]] for s in range(n)])[:, None], torch.bfloat16),
+                          to_dev(np.stack([hist[s][1][p[s]] for s in range(n)])[:, None], torch.bfloat16), out,
+                          num_splits=2)
+        got = out.float().cpu().numpy()
+        for s in range(n):
+            want = oracle.decode_attention(qs[s][p[s]], hist[s][0], hist[s][1], p[s], L, W, 1 / math.sqrt(d),
+                                           10000.0)
+            worst = max(worst, normwise_err(got[s], want))
+    assert worst <= BF16_TOL, worst
+
+
 def test_decode_step_reset_pe_and_invalid_sequences(ps):
     """Reset PE takes the two-call path and matches it bit for bit; a sequence
     with a negative prefix gets NaN rows and its ring is left untouched, the
