@@ -22,7 +22,8 @@ def ps():
     return ps
 
 
-@pytest.mark.parametrize("mode,splits", [("decode", 1), ("decode", 3), ("heavy", 1), ("heavy", 2)])
+@pytest.mark.parametrize("mode,splits", [("decode", 1), ("decode", 3), ("step", 1), ("step", 3), ("heavy", 1),
+                                         ("heavy", 2)])
 def test_graph_replays_match_eager(ps, mode, splits):
     n, hq, hkv, d, L, W, H, layers, p0 = 6, 16, 2, 128, 10, 64, 24, 3, 200
     attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16, 10000.0, 1 / math.sqrt(d))
@@ -61,6 +62,9 @@ def test_graph_replays_match_eager(ps, mode, splits):
             if mode == "heavy":
                 ps.ps_heavy_decode_step(attn, cache, H, kc, vc, pl, pos[c], q[li], kn[li], vn[li], outs[c][li], st,
                                         num_splits=splits, workspace=ws[c])
+            elif mode == "step":
+                ps.ps_decode_step(attn, cache, kc, vc, pl, pos[c], q[li], kn[li], vn[li], outs[c][li],
+                                  num_splits=splits, workspace=ws[c])
             else:
                 ps.ps_kv_append(attn, cache, kc, vc, pl, pos[c], kn[li], vn[li])
                 ps.ps_decode_attn(attn, cache, kc, vc, pl, pos[c], q[li], outs[c][li], num_splits=splits,
@@ -72,7 +76,7 @@ def test_graph_replays_match_eager(ps, mode, splits):
     with torch.cuda.graph(graph):
         step(0)
     torch.cuda.synchronize()
-    replays = 6 if mode == "decode" else 40   # heavy: fill the heavy sets (24 slots), then replace members
+    replays = 40 if mode == "heavy" else 6   # heavy: fill the heavy sets (24 slots), then replace members
     for r in range(replays):
         for li in range(layers):
             q[li].copy_(torch.randn((n, hq, d), generator=g, device="cuda").bfloat16())
