@@ -720,8 +720,8 @@ def load_traffic(kernel_bytes):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU sharding is "
-                                   "described in DESIGN.md, not implemented)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 (sharding the path "
+                                   "across GPUs is not implemented)"}))
         sys.exit(2)
     # the CPU oracle's worker processes start before anything initialises the GPU
     cpu = cpu_prefill = None
