@@ -21,9 +21,10 @@ def ps():
     return ps
 
 
-def _decode_full_size(ps, cfg, sampled_seqs, prefix, positions, paged=False, seed=0):
-    """One decode step (append p, attend at p) of one layer for every sequence;
-    returns the worst row-normwise error over the sampled sequences."""
+def _decode_full_size(ps, cfg, sampled_seqs, prefix, positions, paged=False, seed=0, fused=False):
+    """One decode step (append p, attend at p) of one layer for every sequence,
+    as two calls or (fused) one ps_decode_step; returns the worst row-normwise
+    error over the sampled sequences."""
     n = cfg.num_seqs
     attn = ps.AttnSpec(cfg.hq, cfg.hkv, cfg.dim, ps.PS_BF16, cfg.rope_theta, 1 / math.sqrt(cfg.dim))
     ring = [min(int(positions[s]) + 1, int(prefix[s]) + cfg.window) for s in range(n)]
@@ -64,9 +65,12 @@ def _decode_full_size(ps, cfg, sampled_seqs, prefix, positions, paged=False, see
         q[s] = to_dev(qs[s], torch.bfloat16)
     pl = torch.tensor(np.asarray(prefix, dtype=np.int32), device="cuda")
     pos = torch.tensor(np.asarray(positions, dtype=np.int64), device="cuda")
-    ps.ps_kv_append(attn, cache, kc, vc, pl, pos, kn, vn, block_table=bt)
     out = torch.empty((n, cfg.hq, cfg.dim), dtype=torch.bfloat16, device="cuda")
-    ps.ps_decode_attn(attn, cache, kc, vc, pl, pos, q, out, block_table=bt)
+    if fused:
+        ps.ps_decode_step(attn, cache, kc, vc, pl, pos, q, kn, vn, out, block_table=bt)
+    else:
+        ps.ps_kv_append(attn, cache, kc, vc, pl, pos, kn, vn, block_table=bt)
+        ps.ps_decode_attn(attn, cache, kc, vc, pl, pos, q, out, block_table=bt)
     got = out.float().cpu().numpy()
     assert not np.isnan(got).any()
     worst = 0.0
@@ -83,9 +87,11 @@ def test_decode_32k_64_sequences(ps):
     assert err <= BF16_TOL, err
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two-calls", "decode-step"])
 @pytest.mark.parametrize("cfg", [synth.C3_DECODE_W4096, synth.C3_DECODE_W8192], ids=lambda c: c.name)
-def test_decode_128k_256_sequences(ps, cfg):
-    err = _decode_full_size(ps, cfg, [0, 255], [cfg.prefix] * cfg.num_seqs, [cfg.position] * cfg.num_seqs)
+def test_decode_128k_256_sequences(ps, cfg, fused):
+    err = _decode_full_size(ps, cfg, [0, 97, 255], [cfg.prefix] * cfg.num_seqs, [cfg.position] * cfg.num_seqs,
+                            fused=fused)
     assert err <= BF16_TOL, err
 
 
@@ -95,8 +101,9 @@ def test_decode_ragged_paged_1024_sequences(ps):
     # sampled: the longest, the shortest, one in warm-up if any, and one at random
     warm = [s for s in range(c.num_seqs) if pos[s] + 1 < pre[s] + c.window]
     sampled = sorted({int(np.argmax(pos)), int(np.argmin(pos)), 17} | set(warm[:1]))
-    err = _decode_full_size(ps, c, sampled, pre, pos, paged=True)
-    assert err <= BF16_TOL, err
+    for fused in (False, True):
+        err = _decode_full_size(ps, c, sampled, pre, pos, paged=True, fused=fused)
+        assert err <= BF16_TOL, (fused, err)
 
 
 def _prefill_rows(ps, cfg, rows, batches, heads):
