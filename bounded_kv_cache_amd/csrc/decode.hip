@@ -63,7 +63,8 @@ __device__ inline u32x4 stream_load(const uint16_t* p) {
 // kAppend: the step's token (k_new / v_new at pos) is appended by this kernel
 // (one launch per decode step instead of an append launch and a decode launch).
 template <int D, int NW, bool kReset, int kStats, bool kAppend = false>
-__global__ __launch_bounds__(NW * 64, kStats == 2 ? 1 : PS_DECODE_MIN_BLOCKS) void decode_bf16_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64, kStats == 2 && NW == kFusedStatsWaves ? 1 : PS_DECODE_MIN_BLOCKS) void decode_bf16_kernel(
+    DecodeArgs a) {
   constexpr int NC = D / 32;   // QK k-steps (32 dims each)
   constexpr int NDT = D / 16;  // PV d-tiles (16 dims each)
   const int lane = threadIdx.x & 63;
@@ -127,7 +128,8 @@ __global__ __launch_bounds__(NW * 64, kStats == 2 ? 1 : PS_DECODE_MIN_BLOCKS) vo
       kStats == 1 ? a.stat_max + ((int64_t)s * geo.hkv + h) * a.group * nch : nullptr, (short)0,
       kStats == 1 ? a.group * nch * 4 : 0, 0x00020000);
   // kStats 2: the same two arrays in LDS (the wave merge reuses the space later)
-  __shared__ __attribute__((aligned(16))) uint8_t fused_lds[kStats == 2 ? kFusedStatsLds : 16];
+  __shared__ __attribute__((aligned(16)))
+  uint8_t fused_lds[kStats == 2 ? (NW == kFusedStatsWaves ? kFusedStatsLds : kFusedStatsLdsSmall) : 16];
   uint16_t* const lds_x = reinterpret_cast<uint16_t*>(fused_lds);
   float* const lds_m = reinterpret_cast<float*>(fused_lds + nch * a.group * 64);
 
@@ -699,7 +701,9 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((uint32_t)((int64_t)a.num_seqs * a.geom.hkv * a.num_splits));
   if (a.dtype == PS_BF16) {
     constexpr int NW = PS_DECODE_WAVES;
-    if (a.heavy_score)
+    if (a.heavy_score && fused_stats_bytes(a.geom.slot_capacity, a.group) <= (size_t)kFusedStatsLdsSmall)
+      hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, 2>), grid, dim3(NW * 64), 0, stream, a);
+    else if (a.heavy_score)
       hipLaunchKernelGGL((decode_bf16_kernel<D, kFusedStatsWaves, false, 2>), grid, dim3(kFusedStatsWaves * 64), 0,
                          stream, a);
     else if (a.k_new)

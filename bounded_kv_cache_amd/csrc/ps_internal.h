@@ -149,11 +149,13 @@ struct BackwardArgs {
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-// Heavy-hitter decode with the statistics in LDS: waves per workgroup (one
-// workgroup per CU) and the LDS it may give them; per 32-slot chunk and query
-// head they take 32 fp16 values and one fp32 max.
+// Heavy-hitter decode with the statistics in LDS; per 32-slot chunk and query
+// head they take 32 fp16 values and one fp32 max.  Statistics up to
+// kFusedStatsLdsSmall: 4 waves per workgroup, two workgroups per CU (as the
+// plain decode); up to kFusedStatsLds: 8 waves, one workgroup per CU.
 constexpr int kFusedStatsWaves = 8;
 constexpr int kFusedStatsLds = 152 * 1024;
+constexpr int kFusedStatsLdsSmall = 79 * 1024;
 inline size_t fused_stats_bytes(int32_t slot_capacity, int32_t group) {
   return (size_t)(slot_capacity / 32) * group * (32 * 2 + 4);
 }
