@@ -43,10 +43,11 @@ the pages; no page is quoted):
 * Reset PE (``decode_attention_reset_pe``; blog section "位置编码：Reset PE 还是
   Continue PE？", the alternative the paper ablated): same visible set, visible
   window tokens renumbered to follow the prefix, rotation at the new numbers.
-* Prefix + heavy hitters + window (``h2o_admit``, ``h2o_decode_trace``): the
-  combination the blog proposes when comparing with H2O; the admission rule
-  and the per-KV-head score (attention received, summed over the group's query
-  heads, accumulated while cached) are readings, stated in the docstrings.
+* Prefix + heavy hitters + window (``h2o_admit``, ``h2o_decode_trace``,
+  ``slot_attention_mass``): the combination the blog proposes when comparing
+  with H2O; the admission rule and the per-KV-head score (attention received,
+  summed over the group's query heads, accumulated while cached) are
+  readings, stated in the docstrings.
 * Backward of the masked prefill (``prefill_attention_backward``): the chain
   rule of masked softmax attention, written out; gradients are taken with
   respect to the raw (un-rotated) inputs.
@@ -302,6 +303,28 @@ def decode_from_slots(q: np.ndarray, p: int, k_rot: np.ndarray, v: np.ndarray, s
         e = np.exp(s - s.max())
         out[h] = (e @ np.asarray(v[:, kv, :], dtype=np.float64)) / e.sum()
     return out
+
+
+def slot_attention_mass(q: np.ndarray, p: int, k_rot: np.ndarray, scale: float, theta: float) -> np.ndarray:
+    """Attention mass each cached key draws from a query at ``p``: for every
+    slot of an explicit set of keys already rotated at their own positions (as
+    in ``decode_from_slots``), the softmax weight it receives, summed over the
+    query heads that share its KV head -- the per-step increment of a token's
+    heavy-hitter score (the prefix + heavy-hitter + window reading stated in
+    ``h2o_decode_trace``).  q: raw [Hq, D]; k_rot: [n_slots, Hkv, D].
+    Returns [n_slots, Hkv] float64; each column sums to Hq / Hkv."""
+    q = np.asarray(q, dtype=np.float64)
+    hq, d = q.shape
+    hkv = k_rot.shape[1]
+    g = hq // hkv
+    qr = rope(q, p, theta)
+    mass = np.zeros((k_rot.shape[0], hkv), dtype=np.float64)
+    for h in range(hq):
+        kv = h // g
+        s = scale * (np.asarray(k_rot[:, kv, :], dtype=np.float64) @ qr[h])
+        e = np.exp(s - s.max())
+        mass[:, kv] += e / e.sum()
+    return mass
 
 
 def key_positions(nk: int, prefix_len: int, kv_start: int) -> np.ndarray:

@@ -8,8 +8,9 @@ scores (1e-5 relative) must agree.  bf16: admission is an argmin over
 accumulated scores, a decision taken from floating point, so the test follows
 the GPU's own state: at every step it checks that the admission the GPU made
 is exactly what the rule gives on the GPU's scores, that the output matches
-the oracle's attention over the GPU's visible set, and that each score grew by
-the oracle's attention mass within the bf16 tolerance."""
+the oracle's attention over the GPU's visible set, and that the scores grew by
+the oracle's attention mass (oracle.slot_attention_mass) within the bf16
+row-normwise bound."""
 import math
 
 import numpy as np
@@ -155,10 +156,8 @@ def test_heavy_bf16_follows_the_rule_step_by_step(ps, paged, splits, geom):
                                                 10000.0)
                 assert normwise_err(got[s, kv * g:(kv + 1) * g], want) <= BF16_TOL, (p, s, kv)
                 # scores grew by the attention each visible token received
-                qr = oracle.rope(q[s][p][kv * g:(kv + 1) * g], p, 10000.0)
-                logits = scale * (kr[:, 0, :] @ qr.T)                      # [vis, G]
-                w = np.exp(logits - logits.max(axis=0))
-                mass = (w / w.sum(axis=0)).sum(axis=1)
+                mass = oracle.slot_attention_mass(q[s][p][kv * g:(kv + 1) * g], p, kr, scale, 10000.0)[:, 0]
+                grew, want_mass = [], []
                 for j, m in zip(vis, mass):
                     if j < L:
                         continue
@@ -170,7 +169,10 @@ def test_heavy_bf16_follows_the_rule_step_by_step(ps, paged, splits, geom):
                         slot_j = L + W + i
                         before = pre_sc[s, kv, L + W + i] if int(j) in members_pre and \
                             members_pre.index(int(j)) == i else pre_sc[s, kv, _ring_slot(int(j), L, W)]
-                    assert abs(sc[s, kv, slot_j] - before - m) <= 2e-2 * g / 8 + 1e-3, (p, s, kv, int(j))
+                    grew.append(float(sc[s, kv, slot_j]) - float(before))
+                    want_mass.append(m)
+                if want_mass:   # the row-normwise bf16 bound over the visible non-prefix slots
+                    assert normwise_err(np.array(grew), np.array(want_mass)) <= BF16_TOL, (p, s, kv)
     if geom == "narrow":
         assert admitted > 0 and replaced > 0 and dropped > 0, (admitted, replaced, dropped)
     else:   # 24 steps into 64 free heavy slots: every token leaving past the prefix is admitted

@@ -33,6 +33,8 @@ PIN_CHECKS = [
     lambda: pins.test_h2o_zero_query_trace_hand_worked(),
     lambda: pins.test_h2o_reduces_to_prefix_sliding_and_full_attention(3, 5),
     lambda: pins.test_h2o_trace_invariants(),
+    lambda: pins.test_slot_attention_mass_closed_forms(),
+    lambda: pins.test_slot_attention_mass_against_outputs_and_trace_increments(),
 ]
 
 
@@ -155,6 +157,23 @@ def _h2o_evict_newest(heavy_pos, heavy_score, cand_pos, cand_score, capacity):
     return -1, int(cand_pos)
 
 
+def _mass_with(bug):
+    def f(q, p, k_rot, scale, theta):
+        q = np.asarray(q, dtype=np.float64)
+        hq, d = q.shape
+        hkv = k_rot.shape[1]
+        g = hq // hkv
+        qr = q if bug == "unrotated-query" else ops.rope(q, p, theta)
+        mass = np.zeros((k_rot.shape[0], hkv))
+        for h in range(hq):
+            kv = h % hkv if bug == "interleaved" else h // g
+            s = scale * (k_rot[:, kv, :] @ qr[h])
+            e = np.exp(s - s.max())
+            mass[:, kv] += e / e.sum()
+        return mass
+    return f
+
+
 MUTANTS = {
     "window-off-by-one": ("visible", _window_off_by_one),
     "prefix-not-causal": ("visible", _prefix_not_causal),
@@ -170,6 +189,8 @@ MUTANTS = {
     "reset-pe-not-renumbered": ("decode_attention_reset_pe", _reset_pe_not_renumbered),
     "h2o-admit-on-tie": ("h2o_admit", _h2o_admit_on_tie),
     "h2o-evict-newest": ("h2o_admit", _h2o_evict_newest),
+    "mass-unrotated-query": ("slot_attention_mass", _mass_with("unrotated-query")),
+    "mass-interleaved-heads": ("slot_attention_mass", _mass_with("interleaved")),
 }
 
 

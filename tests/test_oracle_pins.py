@@ -544,6 +544,54 @@ def test_h2o_trace_invariants():
         assert set(scores[kv]) == set(members.tolist()) | set(range(n - W, n))
 
 
+def test_slot_attention_mass_closed_forms():
+    # q = 0: every cached key draws the same weight from every head, so each slot
+    # of a KV head gets G / n; two keys whose scores differ by a known amount
+    # split a head's unit mass as a logistic function of that difference
+    rs = np.random.default_rng(11)
+    n, hq, hkv, d = 9, 6, 2, 8
+    k = rs.standard_normal((n, hkv, d))
+    mass = oracle.slot_attention_mass(np.zeros((hq, d)), 17, k, 0.7, 10000.0)
+    np.testing.assert_allclose(mass, np.full((n, hkv), (hq // hkv) / n), rtol=0, atol=1e-15)
+    # theta = 0 (no rotation): key 0 scores scale * <q, k0> = 0.5 * 2 = 1 with every
+    # query head, key 1 scores 0
+    q = np.zeros((4, 2))
+    q[:, 0] = 2.0
+    kk = np.zeros((2, 1, 2))
+    kk[0, 0, 0] = 1.0
+    got = oracle.slot_attention_mass(q, 5, kk, 0.5, 0.0)
+    e = math.e
+    np.testing.assert_allclose(got[:, 0], [4 * e / (e + 1), 4 / (e + 1)], rtol=1e-15)
+
+
+def test_slot_attention_mass_against_outputs_and_trace_increments():
+    rs = np.random.default_rng(12)
+    hq, hkv, d, L, W, p = 8, 2, 16, 3, 50, 23
+    g = hq // hkv
+    q = rs.standard_normal((p + 2, hq, d))
+    k = rs.standard_normal((p + 2, hkv, d))
+    v = rs.standard_normal((p + 2, hkv, d))
+    pos = np.arange(p + 1)
+    k_rot = oracle.rope(k[:p + 1], pos[:, None], 10000.0)
+    mass = oracle.slot_attention_mass(q[p], p, k_rot, 0.3, 10000.0)
+    # each KV head's column sums to its G heads' unit masses
+    np.testing.assert_allclose(mass.sum(axis=0), [g, g], rtol=1e-14)
+    # the group's outputs summed over heads are the mass-weighted sum of values
+    # (ties the weights to the pinned decode oracle: same rotation, scale, map)
+    out = oracle.decode_from_slots(q[p], p, k_rot, v[:p + 1], 0.3, 10000.0)
+    for kv in range(hkv):
+        np.testing.assert_allclose(out[kv * g:(kv + 1) * g].sum(axis=0), mass[:, kv] @ v[:p + 1, kv],
+                                   rtol=0, atol=1e-12)
+    # the heavy-hitter trace adds exactly this mass at step p to every cached
+    # non-prefix token (W > p: nothing has left the window yet)
+    _, _, before = oracle.h2o_decode_trace(q[:p], k[:p], v[:p], L, W, 4, 0.3, 10000.0)
+    _, _, after = oracle.h2o_decode_trace(q[:p + 1], k[:p + 1], v[:p + 1], L, W, 4, 0.3, 10000.0)
+    for kv in range(hkv):
+        for j in range(L, p + 1):
+            grew = after[kv][j] - before[kv].get(j, 0.0)
+            assert abs(grew - mass[j, kv]) < 1e-12, (kv, j)
+
+
 # ---------------------------------------------------------------- tile plan
 def test_tile_plan_hand_worked_cases():
     for case in _golden("tile_plan_small.json")["cases"]:
