@@ -5,18 +5,21 @@ The forward output and LSE handed to the backward come from the oracle
 (rounded to the kernel dtype), so the check isolates the backward kernels; one
 test also runs the GPU forward into the GPU backward.
 
-Tolerances (derived from the arithmetic; the pages fix none for gradients).
-In bf16 the scaled, rotated queries and keys are bf16, so a score carries an
-absolute error of about 2^-9 times its magnitude (a few units in log2 scale):
-each probability is off by a few tenths of a percent.  The softmax gradient
-dS = P (dP - Di) sums to zero over a row, so these per-probability errors do
-not cancel -- they survive at that relative size against the terms, not
-against the (smaller) result.  With the bf16 rounding of P and dS on top, a
-gradient tensor is held to 2e-2 of its largest row's max-norm, and each row to
-5e-2 of the larger of its own max-norm and a tenth of the largest (rows whose
-exact gradient nearly cancels have no meaningful relative error).  The fp32
-debug path: 1e-5 for both.  Rows that no gradient can reach (a zero upstream
-row; keys no query with a non-zero upstream row sees) must be exactly zero."""
+Tolerances.  The pages fix none for gradients; the contract's bf16 bound is
+1e-2.  Two metrics per gradient tensor: the largest row error against the
+larger of the row's max-norm and a tenth of the tensor's (rows whose exact
+gradient nearly cancels have no meaningful relative error), and the largest
+error against the tensor's max-norm.  A bf16 pipeline cannot reach 1e-2 on
+every input: tests/bf16_backward_model.py evaluates the same chain rule with
+the operands rounded to bf16 where the kernels round them (rotated query and
+key, P and dS; float32 elsewhere) on exact forward statistics, and its
+distance to the oracle -- the floor -- exceeds 1e-2 on some of these cases
+(tests/test_bf16_backward_floor.py shows it comes from the rounded query and
+key).  Each case therefore holds the kernel to max(1e-2, 1.25 x the floor
+measured on that case's own inputs), per tensor and metric; a floor above
+1.5e-2 fails the test (the model would be wrong).  The fp32 debug path: 1e-5
+for both.  Rows that no gradient can reach (a zero upstream row; keys no query
+with a non-zero upstream row sees) must be exactly zero."""
 import math
 
 import numpy as np
@@ -25,12 +28,19 @@ import torch
 
 import oracle
 import synth
+from tests import bf16_backward_model as model
 from tests.gpu_common import normwise_err, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
-BF16_ROW_TOL, BF16_TENSOR_TOL = 5e-2, 2e-2
+BF16_TOL, FLOOR_FACTOR, FLOOR_MAX = 1e-2, 1.25, 1.5e-2
 F32_ROW_TOL, F32_TENSOR_TOL = 1e-5, 1e-5
+
+
+def bf16_tolerances(floor_row, floor_tensor):
+    """max(1e-2, 1.25 x the bf16 model's floor) for each metric."""
+    assert floor_row <= FLOOR_MAX and floor_tensor <= FLOOR_MAX, (floor_row, floor_tensor)
+    return max(BF16_TOL, FLOOR_FACTOR * floor_row), max(BF16_TOL, FLOOR_FACTOR * floor_tensor)
 
 
 @pytest.fixture(scope="module")
@@ -40,13 +50,7 @@ def ps():
     return ps
 
 
-def _errs(got, want):
-    """(worst row error against max(row max-norm, 0.1 * largest), error against the tensor's max-norm)"""
-    g = np.asarray(got, dtype=np.float64).reshape(-1, want.shape[-1])
-    w = np.asarray(want, dtype=np.float64).reshape(-1, want.shape[-1])
-    big = np.abs(w).max()
-    row = (np.abs(g - w).max(axis=1) / np.maximum(np.abs(w).max(axis=1), 0.1 * big)).max()
-    return float(row), float(np.abs(g - w).max() / big)
+_errs = model.errors
 
 
 def _structural_zero_rows(do, L, W, ks, nk):
@@ -73,12 +77,15 @@ def _run(ps, dtype, hq, hkv, d, L, W, ks, T, chunk, batch=1, seed=0, loss_rows=N
     if loss_rows is not None:            # the trainer's loss mask: only the last rows carry gradient
         do[:, :T - loss_rows] = 0.0
     scale = 1 / math.sqrt(d)
-    outs, lses, wants = [], [], []
+    outs, lses, wants, floors = [], [], [], []
     for b in range(batch):
         o, l = oracle.prefill_attention(q[b], k[b], v[b], L, W, ks, scale, 10000.0)
         outs.append(synth.round_to(o, dt_name))
         lses.append(l.T.astype(np.float32))            # [Hq, T]
         wants.append(oracle.prefill_attention_backward(q[b], k[b], v[b], do[b], L, W, ks, scale, 10000.0))
+        if dtype == "bf16":   # what an ideal bf16 pipeline reaches on these inputs
+            ideal = model.backward(q[b], k[b], v[b], outs[-1], do[b], lses[-1].T, L, W, ks, scale, 10000.0)
+            floors.append([_errs(x, w) for x, w in zip(ideal, wants[-1])])
     dq = torch.full((batch, T, hq, d), float("nan"), dtype=tdt, device="cuda")
     dk = torch.full((batch, nk, hkv, d), float("nan"), dtype=tdt, device="cuda")
     dv = torch.full((batch, nk, hkv, d), float("nan"), dtype=tdt, device="cuda")
@@ -87,14 +94,19 @@ def _run(ps, dtype, hq, hkv, d, L, W, ks, T, chunk, batch=1, seed=0, loss_rows=N
                                 torch.from_numpy(np.ascontiguousarray(np.stack(lses))).cuda(), dq, dk, dv)
     torch.cuda.synchronize()
     got = [x.float().cpu().numpy() for x in (dq, dk, dv)]
-    row_tol, ten_tol = (BF16_ROW_TOL, BF16_TENSOR_TOL) if dtype == "bf16" else (F32_ROW_TOL, F32_TENSOR_TOL)
     worst = {}
     for b in range(batch):
-        for name, g, w in zip(("dq", "dk", "dv"), got, wants[b]):
+        for i, (name, g, w) in enumerate(zip(("dq", "dk", "dv"), got, wants[b])):
             assert np.isfinite(g[b]).all(), name
             r, tn = _errs(g[b], w)
+            if dtype == "bf16":
+                row_tol, ten_tol = bf16_tolerances(*floors[b][i])
+                print(f"{name} batch {b}: error (row, tensor) ({r:.4f}, {tn:.4f}), bf16 floor "
+                      f"({floors[b][i][0]:.4f}, {floors[b][i][1]:.4f})", flush=True)
+            else:
+                row_tol, ten_tol = F32_ROW_TOL, F32_TENSOR_TOL
             worst[name] = max(worst.get(name, (0, 0))[0], r), max(worst.get(name, (0, 0))[1], tn)
-            assert r <= row_tol and tn <= ten_tol, (name, b, r, tn)
+            assert r <= row_tol and tn <= ten_tol, (name, b, r, tn, row_tol, ten_tol)
         dead_q, vis, live_q = _structural_zero_rows(do[b], L, W, ks, nk)
         assert np.all(got[0][b][dead_q] == 0.0)
         g = hq // hkv
@@ -151,8 +163,14 @@ def test_forward_then_backward_pipeline(ps):
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     ps.ps_prefill_attn_backward(attn, W, L, ks, qd, kd, vd, out, dod, lse, dq, dk, dv)
     torch.cuda.synchronize()
-    want = oracle.prefill_attention_backward(q, k, v, do, L, W, ks, 1 / math.sqrt(d), 10000.0)
-    for name, g, w in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+    scale = 1 / math.sqrt(d)
+    want = oracle.prefill_attention_backward(q, k, v, do, L, W, ks, scale, 10000.0)
+    o_ref, l_ref = oracle.prefill_attention(q, k, v, L, W, ks, scale, 10000.0)
+    ideal = model.backward(q, k, v, synth.round_to(o_ref, "bf16"), do, l_ref.astype(np.float32), L, W, ks, scale,
+                           10000.0)
+    for name, g, w, x in zip(("dq", "dk", "dv"), (dq, dk, dv), want, ideal):
         r, tn = _errs(g[0].float().cpu().numpy(), w)
-        print(name, r, tn, flush=True)
-        assert r <= BF16_ROW_TOL and tn <= BF16_TENSOR_TOL, (name, r, tn)
+        fr, ft = _errs(x, w)
+        print(name, r, tn, "floor", fr, ft, flush=True)
+        row_tol, ten_tol = bf16_tolerances(fr, ft)
+        assert r <= row_tol and tn <= ten_tol, (name, r, tn, row_tol, ten_tol)
