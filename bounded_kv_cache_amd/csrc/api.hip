@@ -4,7 +4,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <initializer_list>
 #include <string>
+#include <utility>
 
 #include "ps_internal.h"
 #include "ps_reset.h"
@@ -31,6 +33,16 @@ ps_status fail(ps_status st, const char* fmt, ...) {
 
 ps_status ok() {
   g_last_error.clear();
+  return PS_OK;
+}
+
+// Element tensors are read and written with 16-byte vector accesses: every
+// such pointer must be 16-byte aligned (a contiguous view at an odd storage
+// offset is rejected here instead of being accessed misaligned).
+ps_status check_aligned(std::initializer_list<std::pair<const void*, const char*>> ptrs, size_t align = 16) {
+  for (const auto& p : ptrs)
+    if (p.first && reinterpret_cast<uintptr_t>(p.first) % align != 0)
+      return fail(PS_INVALID_ARGUMENT, "%s is not %zu-byte aligned", p.second, align);
   return PS_OK;
 }
 
@@ -295,6 +307,8 @@ ps_status ps_kv_append(const ps_attn_desc* attn, const ps_cache_desc* cache, voi
     return fail(PS_INVALID_ARGUMENT, "num_seqs*tokens_per_seq exceeds 2^26 per call");
   if (!k_cache || !v_cache || !prefix_len || !start_pos || !k_new || !v_new)
     return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if ((st = check_aligned({{k_cache, "k_cache"}, {v_cache, "v_cache"}, {k_new, "k_new"}, {v_new, "v_new"}})) != PS_OK)
+    return st;
   ps::AppendArgs a{};
   a.geom = make_geom(attn, cache);
   a.dtype = attn->dtype;
@@ -340,6 +354,9 @@ ps_status decode_call(const ps_attn_desc* attn, const ps_cache_desc* cache, cons
   if (num_splits < 0) return fail(PS_INVALID_ARGUMENT, "negative num_splits");
   if (num_seqs == 0) return ok();
   if (!k_cache || !v_cache || !prefix_len || !pos || !q || !out) return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if ((st = check_aligned({{k_cache, "k_cache"}, {v_cache, "v_cache"}, {q, "q"}, {out, "out"}, {k_new, "k_new"},
+                           {v_new, "v_new"}, {workspace, "workspace"}})) != PS_OK)
+    return st;
   if ((int64_t)num_seqs * attn->num_kv_heads * 64 > (int64_t)1 << 31)
     return fail(PS_INVALID_ARGUMENT, "num_seqs too large for one launch");
   const int32_t splits = num_splits > 0 ? num_splits : auto_splits(attn, cache, num_seqs, device_cu_count());
@@ -463,6 +480,9 @@ ps_status ps_heavy_decode_step(const ps_attn_desc* attn, const ps_cache_desc* ca
   if (!k_cache || !v_cache || !prefix_len || !pos || !q || !k_new || !v_new || !out || !score || !heavy_count ||
       (heavy_slots > 0 && !heavy_pos))
     return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if ((st = check_aligned({{k_cache, "k_cache"}, {v_cache, "v_cache"}, {q, "q"}, {out, "out"}, {k_new, "k_new"},
+                           {v_new, "v_new"}, {score, "score"}, {workspace, "workspace"}})) != PS_OK)
+    return st;
   if ((int64_t)num_seqs * attn->num_kv_heads * 64 > (int64_t)1 << 31)
     return fail(PS_INVALID_ARGUMENT, "num_seqs too large for one launch");
   const int32_t splits = num_splits > 0 ? num_splits : auto_splits(attn, cache, num_seqs, device_cu_count());
@@ -568,6 +588,9 @@ ps_status ps_prefill_attn(const ps_attn_desc* attn, int32_t window, int32_t pref
   if ((st = check_prefill_geom(window, prefix_len, kv_start, batch, num_queries, num_keys)) != PS_OK) return st;
   if (batch == 0 || num_queries == 0) return ok();
   if (!q || !k || !v || !out) return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if ((st = check_aligned({{q, "q"}, {k, "k"}, {v, "v"}, {out, "out"}, {workspace, "workspace"}})) != PS_OK ||
+      (st = check_aligned({{lse, "lse"}}, 4)) != PS_OK)
+    return st;
   const size_t need = prefill_ws_bytes(attn, batch, num_queries, num_keys);
   if (!workspace || workspace_bytes < need)
     return fail(PS_WORKSPACE_TOO_SMALL, "prefill needs %zu workspace bytes, got %zu", need, workspace_bytes);
@@ -630,6 +653,10 @@ ps_status ps_prefill_attn_backward(const ps_attn_desc* attn, int32_t window, int
   if (batch == 0 || num_queries == 0) return ok();
   if (!q || !k || !v || !out || !d_out || !lse || !dq || !dk || !dv)
     return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if ((st = check_aligned({{q, "q"}, {k, "k"}, {v, "v"}, {out, "out"}, {d_out, "d_out"}, {dq, "dq"}, {dk, "dk"},
+                           {dv, "dv"}, {workspace, "workspace"}})) != PS_OK ||
+      (st = check_aligned({{lse, "lse"}}, 4)) != PS_OK)
+    return st;
   if ((int64_t)batch * attn->num_q_heads * ((num_queries + 127) / 128) + 8 > (int64_t)1 << 31 ||
       (int64_t)batch * attn->num_q_heads * num_queries > (int64_t)1 << 31 ||
       (int64_t)batch * attn->num_kv_heads * num_keys > (int64_t)1 << 31)
@@ -697,6 +724,10 @@ ps_status ps_chunk_prefill_attn(const ps_attn_desc* attn, const ps_cache_desc* c
   if (num_seqs == 0 || chunk_len == 0) return ok();
   if (!k_cache || !v_cache || !prefix_len || !start_pos || !q || !k_new || !v_new || !out)
     return fail(PS_INVALID_ARGUMENT, "NULL device pointer");
+  if ((st = check_aligned({{k_cache, "k_cache"}, {v_cache, "v_cache"}, {q, "q"}, {k_new, "k_new"}, {v_new, "v_new"},
+                           {out, "out"}, {workspace, "workspace"}})) != PS_OK ||
+      (st = check_aligned({{lse, "lse"}}, 4)) != PS_OK)
+    return st;
   if ((int64_t)cache->slot_capacity + chunk_len > ((int64_t)1 << 30))
     return fail(PS_INVALID_ARGUMENT, "slot_capacity + chunk_len exceeds 2^30");
   if ((int64_t)num_seqs * chunk_len > (int64_t)1 << 26)

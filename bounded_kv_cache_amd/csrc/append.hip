@@ -51,8 +51,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     if (a.rope.enabled) {
       float c, sn;
       rope_cos_sin(j, a.rope.inv_freq[i], c, sn);
-      y1 = x1 * c - x2 * sn;
-      y2 = x2 * c + x1 * sn;
+      rotate_pair(x1, x2, c, sn, y1, y2);
     }
     Elem<T>::store(kc + base + k_in_region(slot, i, D), y1);
     Elem<T>::store(kc + base + k_in_region(slot, i + half, D), y2);
@@ -125,8 +124,10 @@ __global__ __launch_bounds__(64) void append_block_kernel(AppendArgs a) {
         if (base < 0) continue;  // page outside the pool: dropped
         const T* row = kn + ((tok0 + pos[k]) * g.hkv + h) * D;
         const float x1 = Elem<T>::load(row + i), x2 = Elem<T>::load(row + i + half);
-        Elem<T>::store(kc + base + k_in_region(slot, i, D), x1 * c - x2 * sn);
-        Elem<T>::store(kc + base + k_in_region(slot, i + half, D), x2 * c + x1 * sn);
+        float y1, y2;
+        rotate_pair(x1, x2, c, sn, y1, y2);
+        Elem<T>::store(kc + base + k_in_region(slot, i, D), y1);
+        Elem<T>::store(kc + base + k_in_region(slot, i + half, D), y2);
       }
     }
   }

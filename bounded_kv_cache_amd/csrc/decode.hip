@@ -366,10 +366,14 @@ __global__ __launch_bounds__(NW * 64, kStats == 2 && NW == kFusedStatsWaves ? 1 
   // ---- kAppend: the token at pos goes to its ring slot (the append rule:
   // dropped for an invalid sequence or a slot beyond the capacity), written by
   // the wave that will read that slot's chunk, while its first chunk's loads
-  // are in flight.  Vector memory operations of a wave complete in order, so
-  // a load it issues after a later wait sees the token; if the slot's chunk is
-  // the first one (already loaded) it is loaded again, and if it is the second
-  // one (loaded at the top of the loop) the stores are waited for first. ----
+  // are in flight.  The wave loads that chunk only after the stores have
+  // completed: if it is the first chunk (already loaded) the stores are waited
+  // for and the chunk is loaded again; if it is the second (loaded at the top
+  // of the loop) the stores are waited for first; any later chunk is loaded
+  // after the wait for the first chunk's data, and the vector memory counter
+  // retires a wave's loads and stores in issue order, so that wait has also
+  // seen the stores (issued between the first chunk's loads and the second's)
+  // complete.  The key is rotated with the append kernel's expression. ----
   if (kAppend && L >= 0 && pos >= 0) {
     const int32_t sn = ring_slot(pos, L, geo.window);
     const int ci_new = sn >> 5;
@@ -384,8 +388,10 @@ __global__ __launch_bounds__(NW * 64, kStats == 2 && NW == kFusedStatsWaves ? 1 
           const float x1 = bf16_to_f32(kn[i]), x2 = bf16_to_f32(kn[i + D / 2]);
           float cs = 1.f, sn_ = 0.f;
           if (a.rope.enabled) rope_cos_sin(pos, a.rope.inv_freq[i], cs, sn_);
-          kw[k_in_region(sn, i, D)] = f32_to_bf16_bits(x1 * cs - x2 * sn_);
-          kw[k_in_region(sn, i + D / 2, D)] = f32_to_bf16_bits(x2 * cs + x1 * sn_);
+          float y1, y2;
+          rotate_pair(x1, x2, cs, sn_, y1, y2);
+          kw[k_in_region(sn, i, D)] = f32_to_bf16_bits(y1);
+          kw[k_in_region(sn, i + D / 2, D)] = f32_to_bf16_bits(y2);
           vw[v_in_region(sn, i, D)] = vn[i];
           vw[v_in_region(sn, i + D / 2, D)] = vn[i + D / 2];
         }

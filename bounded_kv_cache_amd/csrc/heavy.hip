@@ -107,8 +107,7 @@ __global__ __launch_bounds__(64) void heavy_retire_kernel(HeavyArgs a) {
     if (a.rope.enabled) {
       float c, sn;
       rope_cos_sin(p, a.rope.inv_freq[i], c, sn);
-      y1 = x1 * c - x2 * sn;
-      y2 = x2 * c + x1 * sn;
+      rotate_pair(x1, x2, c, sn, y1, y2);
     }
     Elem<T>::store(kc + rb + k_in_region(slot, i, D), y1);
     Elem<T>::store(kc + rb + k_in_region(slot, i + half, D), y2);

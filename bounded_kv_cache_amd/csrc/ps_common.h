@@ -86,6 +86,16 @@ __device__ inline void rope_cos_sin(int64_t pos, double inv_freq, float& c, floa
   sincosf((float)r, &s, &c);
 }
 
+// Rotate-half pair (x1, x2) -> (x1 c - x2 s, x2 c + x1 s).  Every kernel that
+// stores a rotated key into the cache uses this one expression (explicit fused
+// multiply-adds, no compiler contraction), so a key is bit-identical whichever
+// kernel wrote it.
+__device__ inline void rotate_pair(float x1, float x2, float c, float s, float& y1, float& y2) {
+#pragma clang fp contract(off)
+  y1 = __builtin_fmaf(x1, c, -(x2 * s));
+  y2 = __builtin_fmaf(x2, c, x1 * s);
+}
+
 __device__ inline float bf16_to_f32(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
 
 __device__ inline uint16_t f32_to_bf16_bits(float f) {

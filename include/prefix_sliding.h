@@ -33,6 +33,10 @@
  *    A ring of L + W <= slot_capacity slots serves any position; a window
  *    wider than the capacity (the full-attention comparator, W >= n) works
  *    while the sequence is shorter than the capacity.
+ *  - Element tensors (caches, q, k, v, out, k_new, v_new, d_out, dq, dk, dv,
+ *    score, workspace) are accessed with 16-byte vector loads and stores and
+ *    must be 16-byte aligned; lse must be 4-byte aligned.  A misaligned
+ *    pointer (e.g. a view at an odd storage offset) is PS_INVALID_ARGUMENT.
  *  - The library keeps no mutable global state; calls are reentrant.
  *
  * KV cache layout (owned by the caller, defined here)
@@ -182,12 +186,18 @@ ps_status ps_decode_attn(const ps_attn_desc* attn, const ps_cache_desc* cache,
 
 /* ps_decode_step -- one decode step: ps_kv_append of the token at pos
  * (k_new, v_new: [num_seqs][1][Hkv][D]) followed by ps_decode_attn at pos,
- * with the same arguments, rules and results (the same ring contents; the
- * output within the decode tolerance of the two calls made in turn).  For
- * bf16 and Continue PE it is one launch: the decode kernel writes the token
- * into its ring slot and attends to it from registers.  Other dtypes and PE
- * modes run the two calls.  Every argument is validated before anything is
- * enqueued.  Same workspace as ps_decode_attn. */
+ * with the same arguments, rules and results: the ring contents are
+ * bit-identical to those ps_kv_append writes, and the output is within the
+ * decode tolerance of the two calls made in turn.  For bf16 and Continue PE it
+ * is one launch: inside the decode kernel, the wave that will read the ring
+ * chunk holding the token's slot rotates and stores the token while its
+ * first loads are in flight, and issues its loads of that chunk only after
+ * its stores have completed (an explicit wait when the chunk is among its
+ * first two, otherwise the completion wait on an earlier chunk's loads, which
+ * a wave's vector memory counter retires in issue order), so the token is read
+ * back from memory like every other key.  Other dtypes and PE modes run the
+ * two calls.  Every argument is validated before anything is enqueued.  Same
+ * workspace as ps_decode_attn. */
 ps_status ps_decode_step(const ps_attn_desc* attn, const ps_cache_desc* cache,
                          void* k_cache, void* v_cache, const int32_t* block_table,
                          const int32_t* prefix_len, const int64_t* pos, const void* q,

@@ -1,7 +1,8 @@
 """ps_decode_step (append the token at pos, then attend at pos) against the
 float64 oracle over the full history, step after step, and against the two
-separate calls on a twin cache: same ring contents (V bit-exact, K within the
-bf16 rounding of its rotation), the same slot map, outputs within tolerance.
+separate calls on a twin cache: the same ring contents bit for bit, outputs
+within tolerance; and a ring snapshot restored after S steps replays them
+bit-identically.
 bf16 with Continue PE is one launch (the decode kernel appends); fp32 and
 Reset PE take the two-call path."""
 import math
@@ -81,13 +82,12 @@ def test_decode_step_trace(ps, dtype, case, paged, splits):
             worst = max(worst, normwise_err(got[s], want))
             assert normwise_err(got[s], two[s]) <= tol, (i, s)
     assert worst <= tol, worst
-    # the same ring contents as the two calls
+    # the same ring contents as the two calls, bit for bit (the fused append
+    # rotates keys with the append kernel's expression)
     (k0, v0), (k1, v1) = caches
-    np.testing.assert_array_equal(v0.view(torch.int16 if dtype == "bf16" else torch.int32).cpu().numpy(),
-                                  v1.view(torch.int16 if dtype == "bf16" else torch.int32).cpu().numpy())
-    a_, b_ = k0.float().cpu().numpy(), k1.float().cpu().numpy()
-    both = ~(np.isnan(a_) & np.isnan(b_))
-    np.testing.assert_allclose(a_[both], b_[both], rtol=2 ** -7 if dtype == "bf16" else 1e-6, atol=1e-6)
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    np.testing.assert_array_equal(v0.view(bits).cpu().numpy(), v1.view(bits).cpu().numpy())
+    np.testing.assert_array_equal(k0.view(bits).cpu().numpy(), k1.view(bits).cpu().numpy())
 
 
 def test_decode_step_head_dim_64(ps):
@@ -158,3 +158,59 @@ def test_decode_step_reset_pe_and_invalid_sequences(ps):
             assert normwise_err(a_[[0, 2]], b_[[0, 2]]) <= BF16_TOL
         assert torch.equal(vc.view(torch.int16), vc2.view(torch.int16))
         assert torch.equal(kc[1].view(torch.int16), kc2[1].view(torch.int16))   # the invalid sequence: untouched
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_ring_snapshot_restore_replays_bit_identically(ps, splits):
+    """Checkpoint / resume of the bounded cache: snapshot every ring (plain
+    device copies of the K and V caches), run S decode steps, restore the
+    snapshot, run the same S steps again: every output and the final rings are
+    bit-identical to the first run (the kernels are deterministic and the ring
+    is the whole state a sequence carries); the first run also matches the
+    oracle.  Positions cross the window edge, the prefix ends inside a chunk."""
+    hq, hkv, d, L, W, steps = 16, 2, 128, 37, 300, 24
+    starts = [330, 1000, 5]
+    n = len(starts)
+    cap = -(-(L + W) // 64) * 64
+    attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16, 10000.0, 1 / math.sqrt(d))
+    cache = ps.CacheSpec(window=W, slot_capacity=cap)
+    last = [p + steps for p in starts]
+    hist = [(synth.history(9, 400, synth.T_K, s, 0, 0, last[s], hkv, d, 0.5, "bf16"),
+             synth.history(9, 400, synth.T_V, s, 0, 0, last[s], hkv, d, 0.5, "bf16")) for s in range(n)]
+    qs = [synth.history(9, 400, synth.T_Q, s, 0, 0, last[s], hq, d, 1.0, "bf16") for s in range(n)]
+    kc, vc = new_cache(ps, attn, cache, n)
+    fill_ring(ps, attn, cache, kc, vc, [L] * n, [p - 1 for p in starts], [h[0] for h in hist], [h[1] for h in hist])
+    snap = (kc.clone(), vc.clone())
+    pl = torch.full((n,), L, dtype=torch.int32, device="cuda")
+    inputs = []
+    for i in range(steps):
+        p = [starts[s] + i for s in range(n)]
+        inputs.append((torch.tensor(p, dtype=torch.int64, device="cuda"),
+                       to_dev(np.stack([qs[s][p[s]] for s in range(n)]), torch.bfloat16),
+                       to_dev(np.stack([hist[s][0][p[s]] for s in range(n)])[:, None], torch.bfloat16),
+                       to_dev(np.stack([hist[s][1][p[s]] for s in range(n)])[:, None], torch.bfloat16)))
+
+    def run():
+        outs = []
+        for pos, q, kn, vn in inputs:
+            out = torch.empty((n, hq, d), dtype=torch.bfloat16, device="cuda")
+            ps.ps_decode_step(attn, cache, kc, vc, pl, pos, q, kn, vn, out, num_splits=splits)
+            outs.append(out)
+        torch.cuda.synchronize()
+        return [o.view(torch.int16).cpu().numpy() for o in outs], kc.view(torch.int16).cpu().numpy(), \
+            vc.view(torch.int16).cpu().numpy()
+
+    first, k1, v1 = run()
+    for i, o in enumerate(first):
+        got = torch.from_numpy(o).view(torch.bfloat16).float().numpy()
+        for s in range(n):
+            p = starts[s] + i
+            want = oracle.decode_attention(qs[s][p], hist[s][0], hist[s][1], p, L, W, 1 / math.sqrt(d), 10000.0)
+            assert normwise_err(got[s], want) <= BF16_TOL, (i, s)
+    kc.copy_(snap[0])
+    vc.copy_(snap[1])
+    second, k2, v2 = run()
+    for a_, b_ in zip(first, second):
+        np.testing.assert_array_equal(a_, b_)
+    np.testing.assert_array_equal(k1, k2)
+    np.testing.assert_array_equal(v1, v2)

@@ -376,3 +376,44 @@ def test_band_full_range_equals_the_classification(sched):
         assert n >= 0, (T, nk, L, W, start, bm, bn)
         total += n
     assert total > 10000
+
+
+ODD = ctypes.c_void_p(0x1008)   # 8-byte aligned only; never dereferenced
+
+
+def test_misaligned_element_pointers_are_rejected(lib):
+    # element tensors are accessed with 16-byte vector loads and stores: a
+    # pointer that is not 16-byte aligned (a view at an odd storage offset) is
+    # an invalid argument, reported before anything is launched
+    a, c = _descs()
+    B = ctypes.byref
+
+    def err(name):
+        return f"{name} is not".encode() in lib.ps_last_error()
+
+    assert lib.ps_decode_attn(B(a), B(c), FAKE, FAKE, None, FAKE, FAKE, ODD, FAKE, 4, 1, None, 0, None) == 1
+    assert err("q")
+    assert lib.ps_decode_attn(B(a), B(c), FAKE, ODD, None, FAKE, FAKE, FAKE, FAKE, 4, 1, None, 0, None) == 1
+    assert err("v_cache")
+    assert lib.ps_decode_step(B(a), B(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, ODD, FAKE, FAKE, 4, 1, None, 0,
+                              None) == 1
+    assert err("k_new")
+    assert lib.ps_kv_append(B(a), B(c), FAKE, FAKE, None, FAKE, FAKE, None, 1, FAKE, ODD, 2, None, None) == 1
+    assert err("v_new")
+    assert lib.ps_prefill_attn(B(a), 64, 0, 0, FAKE, FAKE, FAKE, 1, 64, 64, ODD, None, FAKE, 1 << 40, None) == 1
+    assert err("out")
+    # the LSE is written one float at a time: 4-byte alignment is enough
+    assert lib.ps_prefill_attn(B(a), 64, 0, 0, FAKE, FAKE, FAKE, 1, 64, 64, FAKE, ctypes.c_void_p(0x1002), FAKE,
+                               1 << 40, None) == 1
+    assert err("lse")
+    assert lib.ps_prefill_attn_backward(B(a), 64, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 64, FAKE, FAKE,
+                                        ODD, FAKE, 1 << 40, None) == 1
+    assert err("dv")
+    assert lib.ps_chunk_prefill_attn(B(a), B(c), ODD, FAKE, None, FAKE, FAKE, 16, FAKE, FAKE, FAKE, 1, FAKE, None,
+                                     None, FAKE, 1 << 40, None) == 1
+    assert err("k_cache")
+    ah, ch = _descs(cap=4352)
+    assert lib.ps_heavy_decode_step(B(ah), B(ch), 8, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, ODD,
+                                    FAKE, FAKE, 1, FAKE, 1 << 30, None) == 1
+    assert err("score")
+
