@@ -163,76 +163,93 @@ def timed(torch, fn, iters):
     return start.elapsed_time(end) / 1000.0
 
 
-def run_decode(ps, torch, args):
-    bench = DecodeBench(ps, torch, args.num_seqs, args.layers, args.window, 100, args.position, args.splits)
-    bench.prepare_positions(args.warmup + 2 * args.steps)
-    splits = args.splits or ps.ps_decode_num_splits(bench.attn, bench.cache, args.num_seqs)
-    for s in range(args.warmup):
-        bench.step(s)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for s in range(args.warmup, args.warmup + args.steps):
-        bench.step(s)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_s = start.elapsed_time(end) / 1000.0
-    elapsed = max(wall, gpu_s)
-    # dominant kernel: the decode-step launches of the step loop (append fused
-    # into the decode kernel).  The timed steps are replayed once more (same
-    # workload, next positions) with a pair of HIP events on the launch stream
-    # around every launch; the average is the kernel's in-step launch duration.
-    # `value` above comes from the plain, un-instrumented steps.
-    n_steps = args.steps
-    evs = []
-    torch.cuda.synchronize()
-    for s_ in range(args.warmup + args.steps, args.warmup + 2 * args.steps):
-        pos = bench.pos[s_]
-        for li in range(bench.layers):
-            i = (s_ * bench.layers + li) % bench.pool
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            ps.ps_decode_step(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, pos, bench.q[i],
-                              bench.kn[i], bench.vn[i], bench.out, num_splits=bench.splits, workspace=bench.ws)
-            e1.record()
-            evs.append((e0, e1))
-    torch.cuda.synchronize()
-    kt = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs) / 1000.0
-    p_last = args.position + args.warmup + 2 * args.steps - 1
-    kbytes = bench.step_kernel_bytes(p_last)
-    # the same step captured once in a HIP graph (28 decode steps, then the
-    # positions advance inside the graph) and replayed: what a serving loop that
-    # captures its decode step would see
-    gpos = bench.pos[args.warmup + 2 * args.steps - 1].clone()
+def time_decode_steps(bench, torch, steps, warmup, reps=5):
+    """The timing protocol: the rings and positions of every layer are
+    snapshotted once; each rep restores them (untimed), then runs `steps`
+    decode steps (28 ps_decode_step launches each) between two HIP events on
+    the launch stream, bracketed by device synchronisation.  One warm-up rep
+    (which also runs `warmup` untimed steps first) is discarded; the median of
+    `reps` timed reps is returned, with every rep's time."""
+    snap_k = [k.clone() for k in bench.k]
+    snap_v = [v.clone() for v in bench.v]
 
-    def graph_step():
-        for li in range(bench.layers):
-            i = li % bench.pool
-            ps.ps_decode_step(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, gpos, bench.q[i],
-                              bench.kn[i], bench.vn[i], bench.out, num_splits=bench.splits, workspace=bench.ws)
-        gpos.add_(1)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        graph_step()
-    for _ in range(2):
-        graph.replay()
-    g_s = timed(torch, lambda k: [graph.replay() for _ in range(k)], args.steps)
-    del graph
+    def restore():
+        for dst, src in zip(bench.k, snap_k):
+            dst.copy_(src)
+        for dst, src in zip(bench.v, snap_v):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    times = []
+    for rep in range(reps + 1):
+        restore()
+        if rep == 0:
+            for s in range(warmup):
+                bench.step(s)
+            torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        for s in range(steps):
+            bench.step(s)
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if rep > 0:
+            times.append(max(wall, start.elapsed_time(end) / 1000.0))
+    restore()
+    del snap_k, snap_v
+    return sorted(times)[len(times) // 2], times
+
+
+def run_decode(ps, torch, args, num_seqs=None, position=None, window=None, graph=True):
+    n = num_seqs or args.num_seqs
+    p0 = position or args.position
+    w = window or args.window
+    bench = DecodeBench(ps, torch, n, args.layers, w, 100, p0, args.splits)
+    bench.prepare_positions(max(args.warmup, args.steps))
+    splits = args.splits or ps.ps_decode_num_splits(bench.attn, bench.cache, n)
+    med, times = time_decode_steps(bench, torch, args.steps, args.warmup)
+    launches = args.steps * bench.layers
+    # the dominant kernel: every launch of the timed loop is one decode-step
+    # kernel (append fused); its average launch duration is the timed loop's
+    # time over its launches (an upper bound: launch gaps are included)
+    kt = med / launches
+    p_last = p0 + args.steps - 1
+    kbytes = bench.step_kernel_bytes(p_last)
     res = {
-        "graph_tok_s": args.num_seqs * args.steps / g_s,
-        "graph_ms_per_step": g_s / args.steps * 1000.0,
-        "tok_s": args.num_seqs * args.steps / elapsed,
-        "ms_per_step": elapsed / args.steps * 1000.0,
+        "tok_s": n * args.steps / med,
+        "ms_per_step": med / args.steps * 1000.0,
+        "rep_ms": [t * 1000.0 for t in times],
         "splits": splits,
         "kernel_s": kt,
-        "kernel_launches": len(evs),
+        "kernel_launches": launches,
         "kernel_bytes": kbytes,
         "n_vis": bench.n_vis(p_last),
     }
+    if graph:
+        # the same step captured once in a HIP graph (28 decode steps, then the
+        # positions advance inside the graph) and replayed: what a serving loop
+        # that captures its decode step would see
+        gpos = bench.pos[args.steps - 1].clone()
+
+        def graph_step():
+            for li in range(bench.layers):
+                i = li % bench.pool
+                ps.ps_decode_step(bench.attn, bench.cache, bench.k[li], bench.v[li], bench.pl, gpos, bench.q[i],
+                                  bench.kn[i], bench.vn[i], bench.out, num_splits=bench.splits, workspace=bench.ws)
+            gpos.add_(1)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            graph_step()
+        for _ in range(2):
+            g.replay()
+        g_s = timed(torch, lambda k: [g.replay() for _ in range(k)], args.steps)
+        del g
+        res["graph_tok_s"] = n * args.steps / g_s
+        res["graph_ms_per_step"] = g_s / args.steps * 1000.0
     bench.release()
     del bench
     torch.cuda.empty_cache()
@@ -435,7 +452,22 @@ def run_decode_extra(ps, torch, layers=28, reps=30):
     return out
 
 # ------------------------------------------------------------------------- prefill
-def run_prefill(ps, torch, reps=10, full_causal=True):
+def median_call_s(torch, fn, reps):
+    """Median over `reps` calls of fn(), each between two HIP events on the
+    current stream (fn enqueues its launches there)."""
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / 1000.0)
+    return sorted(ts)[len(ts) // 2]
+
+
+def run_prefill(ps, torch, reps=9, full_causal=True):
     import synth
     out = {}
     for cfg in ([synth.C4_PREFILL, synth.C4_PREFILL_FULL] if full_causal else [synth.C4_PREFILL]):
@@ -447,10 +479,11 @@ def run_prefill(ps, torch, reps=10, full_causal=True):
         o = torch.empty_like(q)
         ws = torch.empty(ps.ps_prefill_workspace_size(attn, cfg.batch, cfg.queries, cfg.nk), dtype=torch.uint8,
                          device="cuda")
-        r = reps if cfg is synth.C4_PREFILL else 2
-        ps.ps_prefill_attn(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, o, workspace=ws)
-        t = timed(torch, lambda n: [ps.ps_prefill_attn(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, o,
-                                                       workspace=ws) for _ in range(n)], r) / r
+        r = reps if cfg is synth.C4_PREFILL else 3
+        call = lambda: ps.ps_prefill_attn(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, o, workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        t = median_call_s(torch, call, r)
         if cfg is synth.C4_PREFILL:   # every query sees the prefix and min(t+1, W) chunk keys
             pairs = cfg.prefix * cfg.queries + sum(min(t_ + 1, cfg.window) for t_ in range(cfg.queries))
         else:                         # full causal: query t sits at position Nk - T + t
@@ -487,7 +520,8 @@ def run_backward(ps, torch, reps=5):
             ps.ps_prefill_attn_backward(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, o, do, lse, dq, dk, dv,
                                         workspace=ws)
     call(1)
-    t = timed(torch, call, reps) / reps
+    torch.cuda.synchronize()
+    t = median_call_s(torch, lambda: call(1), reps)
     pairs = cfg.prefix * cfg.queries + sum(min(t_ + 1, cfg.window) for t_ in range(cfg.queries))
     flops = 10.0 * cfg.dim * pairs * cfg.batch * cfg.hq
     res = {"workload": cfg.name + "-backward", "ms": t * 1e3, "tflops": flops / t / 1e12,
@@ -576,7 +610,8 @@ def run_chunk(ps, torch, reps=5):
         for _ in range(k_):
             ps.ps_chunk_prefill_attn(attn, cache, kc, vc, pl, sp, q, kn, vn, out, workspace=ws)
     call(1)
-    t = timed(torch, call, reps) / reps
+    torch.cuda.synchronize()
+    t = median_call_s(torch, lambda: call(1), reps)
     # every chunk query sits beyond L + W: it sees exactly L + W keys
     pairs = sum(min(cfg.position + t_ + 1, cfg.prefix + cfg.window) for t_ in range(T))
     flops = 4.0 * cfg.dim * pairs * n * cfg.hq
@@ -609,7 +644,8 @@ def _oracle_worker(args):
 def run_cpu_baseline(args):
     import concurrent.futures
     import multiprocessing
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    host = len(os.sched_getaffinity(0))
+    cores = min(host, 16)   # a GPU machine's CPU share is 16 cores, whatever the host shows
     reps = 2
     jobs = [(i, args.position, 100, args.window, reps) for i in range(cores)]
     ctx = multiprocessing.get_context("spawn")
@@ -618,7 +654,7 @@ def run_cpu_baseline(args):
     tuples = sum(r[0] for r in res)
     slowest = max(r[1] for r in res)
     tok_s = tuples / slowest / args.layers
-    return {"value": tok_s, "unit": "tok/s", "cores": cores, "kind": "oracle",
+    return {"value": tok_s, "unit": "tok/s", "cores": cores, "host_cores": host, "kind": "oracle",
             "sample": f"{tuples} (sequence, layer) decode tuples at position {args.position} over the full "
                       f"un-evicted history, {cores} worker processes x 1 BLAS thread, {reps} tuples each; "
                       f"tok/s = tuples / slowest worker's oracle time / {args.layers} layers",
@@ -664,7 +700,8 @@ def run_cpu_prefill_baseline(cores):
         res = list(ex.map(_oracle_prefill_worker, jobs))
     pairs = sum(r[0] for r in res)
     slowest = max(r[1] for r in res)
-    return {"value": float(4.0 * cfg.dim * pairs / slowest / 1e12), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": float(4.0 * cfg.dim * pairs / slowest / 1e12), "unit": "TFLOP/s", "cores": len(jobs),
+            "host_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{n_pairs} (batch, head) pairs of the 8 x 8192-query prefill (W=2048, prefix 100), all "
                       f"{cfg.queries} query rows, split over {len(jobs)} worker processes x 1 BLAS thread; "
                       f"TFLOP/s = 4 D x visible pairs / slowest worker's oracle time",
@@ -766,34 +803,41 @@ def main():
     ceil = measure_ceilings(ps, torch)
     print(f"[bench] ceilings: {ceil}", file=sys.stderr, flush=True)
     dec = run_decode(ps, torch, args)
-    print(f"[bench] decode done: {dec['tok_s']:.0f} tok/s, kernel {dec['kernel_s'] * 1e6:.1f} us",
+    print(f"[bench] decode done: {dec['tok_s']:.0f} tok/s, {dec['kernel_s'] * 1e6:.1f} us per launch",
           file=sys.stderr, flush=True)
+    if args.only == "decode":
+        print(json.dumps({"decode": dec}))
+        return
+    small = None
+    if not args.no_extra:
+        small = run_decode(ps, torch, args, num_seqs=64, position=32768, graph=False)
+        print(f"[bench] decode 64 seqs @ 32768 done: {small['tok_s']:.0f} tok/s", file=sys.stderr, flush=True)
     prefill = None
-    if not args.no_prefill and args.only is None:
+    if not args.no_prefill:
         prefill = run_prefill(ps, torch)
         print(f"[bench] prefill done: {prefill}", file=sys.stderr, flush=True)
     backward = None
-    if not args.no_backward and args.only is None:
+    if not args.no_backward:
         backward = run_backward(ps, torch)
         print(f"[bench] prefill backward done: {backward['tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
     heavy = None
-    if not args.no_heavy and args.only is None:
+    if not args.no_heavy:
         heavy = run_heavy(ps, torch)
         print(f"[bench] heavy hitters done: {heavy['us_per_layer']:.1f} us/layer", file=sys.stderr, flush=True)
     chunk = None
-    if not args.no_chunk and args.only is None:
+    if not args.no_chunk:
         chunk = run_chunk(ps, torch)
         print(f"[bench] chunk prefill done: {chunk['tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
     sweep = None
-    if not args.no_sweep and args.only is None:
+    if not args.no_sweep:
         sweep = run_sweep(ps, torch, num_seqs=args.num_seqs, layers=args.layers)
         print(f"[bench] position sweep done", file=sys.stderr, flush=True)
     extra = None
-    if not args.no_extra and args.only is None:
+    if not args.no_extra:
         extra = run_decode_extra(ps, torch, layers=args.layers)
         print(f"[bench] other decode workloads done", file=sys.stderr, flush=True)
     full = None
-    if not args.no_full and args.only is None:
+    if not args.no_full:
         full = run_full_attention(ps, torch, args)
         print(f"[bench] full attention done: {full['tok_s']:.0f} tok/s", file=sys.stderr, flush=True)
     achieved = dec["kernel_bytes"] / dec["kernel_s"] / 1e9
@@ -813,9 +857,14 @@ def main():
         "config": {"workload": f"decode-{args.position}-w{args.window}", "num_seqs": args.num_seqs,
                    "layers": args.layers, "position": args.position, "prefix": 100, "window": args.window,
                    "hq": 16, "hkv": 2, "head_dim": 128, "splits": dec["splits"]},
+        "timing": {"protocol": "rings and positions restored from a snapshot before each rep (untimed); 1 warm-up "
+                               "rep discarded; value and ms_per_step are the median of 5 timed reps of `steps` "
+                               "steps, each bracketed by HIP events on the launch stream",
+                   "rep_ms": dec["rep_ms"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(dec["kernel_bytes"]),
                      "kernel": "decode_bf16_kernel (append fused)", "kernel_us": dec["kernel_s"] * 1e6,
+                     "kernel_us_source": "median timed rep / launches in it (launch gaps included)",
                      "kernel_launches_timed": dec["kernel_launches"],
                      "bytes_per_launch": dec["kernel_bytes"],
                      "measured_read_gbs": ceil["hbm_read_gbs"], "frac_of_measured_read": achieved / ceil["hbm_read_gbs"]},
@@ -825,15 +874,31 @@ def main():
                                              "advance) and replayed; value is the eager loop"},
         "cpu_baseline": cpu,
         "cpu_baseline_prefill": cpu_prefill,
-        "prefill": prefill,
-        "prefill_backward": backward,
-        "chunk_prefill": chunk,
-        "heavy_hitters": heavy,
-        "full_attention": full,
     }
+    if small:
+        sb = small["kernel_bytes"] / small["kernel_s"] / 1e9
+        line["decode_32768_64seq"] = {
+            "workload": "decode-32768-w4096-64seq", "num_seqs": 64, "position": 32768, "window": 4096,
+            "layers": args.layers, "tok_s": small["tok_s"], "ms_per_step": small["ms_per_step"],
+            "splits": small["splits"], "kernel_us": small["kernel_s"] * 1e6, "hbm_gbs": sb,
+            "hbm_frac": sb / HBM_PEAK_GBS, "rep_ms": small["rep_ms"]}
     if prefill:
-        for v in prefill.values():
-            v["frac_of_measured_gemm"] = v["tflops"] / ceil["bf16_gemm_tflops"]
+        c4 = prefill["c4-prefill-7b"]
+        line["prefill"] = {"workload": "c4-prefill-7b", "batch": 8, "queries": 8192, "prefix": 100, "window": 2048,
+                           "hq": 28, "hkv": 4, "head_dim": 128, "ms": c4["ms"], "tflops": c4["tflops"],
+                           "useful_tflop": c4["useful_tflop"],
+                           "roofline": {"bound": "mfma", "achieved": c4["tflops"], "peak": BF16_PEAK_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": c4["mfma_frac"], "traffic": None,
+                                        "kernel": "prefill_prep_kernel + prefill_bf16_kernel (whole call)",
+                                        "frac_of_measured_gemm": c4["tflops"] / ceil["bf16_gemm_tflops"]}}
+        fc = prefill.get("c4-prefill-7b-full-causal")
+        if fc:
+            fc["frac_of_measured_gemm"] = fc["tflops"] / ceil["bf16_gemm_tflops"]
+            line["prefill_full_causal"] = dict(workload="c4-prefill-7b-full-causal", **fc)
+    line["prefill_backward"] = backward
+    line["chunk_prefill"] = chunk
+    line["heavy_hitters"] = heavy
+    line["full_attention"] = full
     if extra:
         line["decode_other_workloads"] = extra
     if sweep:
