@@ -22,7 +22,7 @@ __all__ = ["AttnSpec", "CacheSpec", "PSError", "ps_kv_append", "ps_decode_attn",
            "ps_chunk_prefill_attn", "ps_chunk_prefill_workspace_size", "ps_prefill_attn_backward",
            "ps_prefill_backward_workspace_size", "ps_heavy_decode_step", "ps_heavy_workspace_size", "HeavyState",
            "ps_prefill_plan", "ps_decode_workspace_size", "ps_decode_num_splits", "ps_prefill_workspace_size",
-           "ps_prefill_tile_shape", "ps_read_probe", "ps_decode_step", "ps_abi_version", "cache_shapes", "PS_BF16", "PS_F32", "PS_PE_CONTINUE",
+           "ps_prefill_tile_shape", "ps_read_probe", "ps_decode_step", "ps_decode_step_noalloc", "ps_abi_version", "cache_shapes", "PS_BF16", "PS_F32", "PS_PE_CONTINUE",
            "PS_PE_RESET", "PS_PE_RESET_RECOMPUTE"]
 
 _TORCH_DTYPE = {PS_BF16: torch.bfloat16, PS_F32: torch.float32}
@@ -177,6 +177,33 @@ def ps_decode_attn(attn: AttnSpec, cache: CacheSpec, k_cache: torch.Tensor, v_ca
     _lib.check(_lib.load().ps_decode_attn(ctypes.byref(a), ctypes.byref(c), _ptr(k_cache), _ptr(v_cache),
                                           _ptr(block_table), _ptr(prefix_len), _ptr(pos), _ptr(q), _ptr(out),
                                           num_seqs, num_splits, _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def ps_decode_step_noalloc(attn: AttnSpec, cache: CacheSpec, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           prefix_len: torch.Tensor, pos: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                           v_new: torch.Tensor, out: torch.Tensor, *, block_table: Optional[torch.Tensor] = None,
+                           num_splits: int = 0, stream=None) -> torch.Tensor:
+    """ps_decode_step without a workspace: the split partials use the library's
+    static device scratch, so the call allocates nothing (see the header)."""
+    dt = attn.torch_dtype
+    num_seqs = q.shape[0]
+    _need(q, "q", dt, num_seqs * attn.num_q_heads * attn.head_dim)
+    _need(out, "out", dt, q.numel())
+    _need(k_new, "k_new", dt, num_seqs * attn.num_kv_heads * attn.head_dim)
+    _need(v_new, "v_new", dt, k_new.numel())
+    ks, vs = cache_shapes(attn, cache, num_seqs)
+    _need(k_cache, "k_cache", dt, math.prod(ks))
+    _need(v_cache, "v_cache", dt, math.prod(vs))
+    _need(prefix_len, "prefix_len", torch.int32, num_seqs)
+    _need(pos, "pos", torch.int64, num_seqs)
+    if block_table is not None:
+        _need(block_table, "block_table", torch.int32, num_seqs * (cache.slot_capacity // 64))
+    a, c = attn.c(), cache.c()
+    _lib.check(_lib.load().ps_decode_step_noalloc(ctypes.byref(a), ctypes.byref(c), _ptr(k_cache), _ptr(v_cache),
+                                                  _ptr(block_table), _ptr(prefix_len), _ptr(pos), _ptr(q),
+                                                  _ptr(k_new), _ptr(v_new), _ptr(out), num_seqs, num_splits,
+                                                  _stream(stream)))
     return out
 
 

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <utility>
 
@@ -452,6 +453,64 @@ ps_status ps_decode_step(const ps_attn_desc* attn, const ps_cache_desc* cache, v
     return st;
   return decode_call(attn, cache, k_cache, v_cache, block_table, prefix_len, pos, q, out, num_seqs, num_splits,
                      workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+// Device scratch of ps_decode_step_noalloc: the split partials live in this
+// file-scope device array (one copy per GPU, resident until the process ends)
+// instead of a caller workspace.  Host code never passes the array's name to a
+// kernel or a copy (on the host it is only a stand-in); it uses the device
+// address hipGetSymbolAddress returns, looked up once per device with that
+// device current.  Every call on a GPU shares that GPU's copy; the decode
+// kernels overwrite every partial they later read, so nothing needs clearing.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+ps_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "ps_decode_step_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices) return fail(PS_UNSUPPORTED, "device index %d beyond %d", dev, kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return from_hip(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                               "ps_decode_step_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PS_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t ps_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+ps_status ps_decode_step_noalloc(const ps_attn_desc* attn, const ps_cache_desc* cache, void* k_cache, void* v_cache,
+                                 const int32_t* block_table, const int32_t* prefix_len, const int64_t* pos,
+                                 const void* q, const void* k_new, const void* v_new, void* out, int32_t num_seqs,
+                                 int32_t num_splits, hipStream_t stream) {
+  ps_status st = check_attn(attn);
+  if (st != PS_OK) return st;
+  if (!cache || cache->slot_capacity <= 0 || num_seqs < 0 || num_splits < 0)
+    return fail(PS_INVALID_ARGUMENT, "invalid cache descriptor, num_seqs or num_splits");
+  const size_t need = ps_decode_workspace_size(attn, cache, num_seqs, num_splits);
+  if (need > kScratchBytes)
+    return fail(PS_WORKSPACE_TOO_SMALL,
+                "ps_decode_step_noalloc: this call needs %zu scratch bytes, beyond the library's static %zu "
+                "(fewer splits or sequences per call, or ps_decode_step with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_for_current_device(&ws)) != PS_OK) return st;
+  return ps_decode_step(attn, cache, k_cache, v_cache, block_table, prefix_len, pos, q, k_new, v_new, out, num_seqs,
+                        num_splits, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
 size_t ps_heavy_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* cache, int32_t num_seqs,

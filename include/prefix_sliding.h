@@ -205,6 +205,28 @@ ps_status ps_decode_step(const ps_attn_desc* attn, const ps_cache_desc* cache,
                          int32_t num_splits, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* ps_decode_step_noalloc -- ps_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same arguments minus the workspace, the same
+ * rules and results.  The split partials go to a static device array inside
+ * the library (ps_decode_noalloc_scratch_bytes() = 8 MiB per GPU, held until
+ * the process ends); the call allocates nothing.  A call whose partials would
+ * exceed it (ps_decode_workspace_size(...) > 8 MiB: e.g. more than about
+ * 4,000 (sequence, split) pairs of 16 heads at head_dim 128, or
+ * PS_PE_RESET_RECOMPUTE on a large cache) returns PS_WORKSPACE_TOO_SMALL
+ * before anything is enqueued.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (different streams, or host threads)
+ * race and must be serialised by the caller.  The first call on a device
+ * looks the array's device address up (hipGetSymbolAddress). */
+ps_status ps_decode_step_noalloc(const ps_attn_desc* attn, const ps_cache_desc* cache,
+                                 void* k_cache, void* v_cache, const int32_t* block_table,
+                                 const int32_t* prefix_len, const int64_t* pos, const void* q,
+                                 const void* k_new, const void* v_new, void* out, int32_t num_seqs,
+                                 int32_t num_splits, hipStream_t stream);
+
+/* Size of the static scratch array of ps_decode_step_noalloc, in bytes. */
+size_t ps_decode_noalloc_scratch_bytes(void);
+
 /* Split count ps_decode_attn uses for num_splits == 0 (queries the current
  * device; assumes 256 CUs when none is visible).  Returns >= 1, or 0 on
  * invalid arguments. */

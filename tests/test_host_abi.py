@@ -417,3 +417,18 @@ def test_misaligned_element_pointers_are_rejected(lib):
                                     FAKE, FAKE, 1, FAKE, 1 << 30, None) == 1
     assert err("score")
 
+
+def test_noalloc_step_rejects_what_exceeds_its_static_scratch(lib):
+    # ps_decode_step_noalloc keeps the split partials in an 8 MiB static device
+    # array: a call whose partials would not fit is refused before anything runs
+    a, c = _descs()
+    assert lib.ps_decode_noalloc_scratch_bytes() == 8 << 20
+    n, splits = 1024, 8   # 1024 sequences x 16 heads x 8 splits x (128 + 2) floats = 68 MB
+    assert lib.ps_decode_workspace_size(ctypes.byref(a), ctypes.byref(c), n, splits) > 8 << 20
+    st = lib.ps_decode_step_noalloc(ctypes.byref(a), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, n, splits, None)
+    assert st == 3 and b"scratch" in lib.ps_last_error()
+    # the argument checks of ps_decode_step come first
+    bad, _ = _descs(hq=15)
+    assert lib.ps_decode_step_noalloc(ctypes.byref(bad), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, n, splits, None) == 1
