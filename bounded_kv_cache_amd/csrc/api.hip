@@ -851,6 +851,7 @@ ps_status ps_chunk_prefill_attn(const ps_attn_desc* attn, const ps_cache_desc* c
   ap.num_seqs = num_seqs;
   ap.slot_pos = slot_pos;
   ap.rope = a.rope;
+  ap.rope_cs = a.rope_cs;   // the chunk's positions P + t: the query table formed by the prep
   return from_hip(ps::launch_append(ap, stream), "ps_chunk_prefill_attn append launch");
 }
 

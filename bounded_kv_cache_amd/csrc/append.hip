@@ -50,7 +50,13 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     float y1 = x1, y2 = x2;
     if (a.rope.enabled) {
       float c, sn;
-      rope_cos_sin(j, a.rope.inv_freq[i], c, sn);
+      if (a.rope_cs) {
+        const float2 w = reinterpret_cast<const float2*>(a.rope_cs)[((int64_t)s * a.tokens_per_seq + t) * half + i];
+        c = w.x;
+        sn = w.y;
+      } else {
+        rope_cos_sin(j, a.rope.inv_freq[i], c, sn);
+      }
       rotate_pair(x1, x2, c, sn, y1, y2);
     }
     Elem<T>::store(kc + base + k_in_region(slot, i, D), y1);
@@ -118,7 +124,13 @@ __global__ __launch_bounds__(64) void append_block_kernel(AppendArgs a) {
     const int32_t slot = 8 * kb + k;
     for (int32_t i = lane; i < half; i += 64) {
       float c = 1.f, sn = 0.f;
-      if (a.rope.enabled) rope_cos_sin(pos[k], a.rope.inv_freq[i], c, sn);
+      if (a.rope.enabled && a.rope_cs) {   // the caller's table row of this token
+        const float2 w = reinterpret_cast<const float2*>(a.rope_cs)[(tok0 + pos[k]) * half + i];
+        c = w.x;
+        sn = w.y;
+      } else if (a.rope.enabled) {
+        rope_cos_sin(pos[k], a.rope.inv_freq[i], c, sn);
+      }
       for (int32_t h = 0; h < g.hkv; ++h) {
         const int64_t base = region_offset(g, a.block_table, s, h, slot);
         if (base < 0) continue;  // page outside the pool: dropped

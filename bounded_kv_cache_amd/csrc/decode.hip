@@ -315,6 +315,18 @@ __global__ __launch_bounds__(NW * 64, kStats == 2 && NW == kFusedStatsWaves ? 1 
 
   if (c < c_end) load_chunk(c, kA, vA);   // the first chunk is in flight during the query prologue
   // ---- query operand: rotate at pos, fold in scale*log2(e), round to bf16 ----
+  // cos/sin of the query position: each lane forms one rotation pair (pair
+  // lane % (D/2): the angle needs double precision, and the lanes of the
+  // other query heads would form the same values), and every lane fetches the
+  // pairs it rotates from the lane that formed them.
+  float cs_l = 1.f, sn_l = 0.f, csb_l = 1.f, snb_l = 0.f;
+  if (a.rope.enabled) {
+    rope_cos_sin(pos, a.rope.inv_freq[lane % (D / 2)], cs_l, sn_l);
+    if (kReset) {
+      const int64_t lw1 = (int64_t)L + geo.window - 1;
+      rope_cos_sin(pos < lw1 ? pos : lw1, a.rope.inv_freq[lane % (D / 2)], csb_l, snb_l);
+    }
+  }
   {
     const int G = a.group;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)s * a.hq + h * G + (r < G ? r : 0)) * D;
@@ -329,15 +341,12 @@ __global__ __launch_bounds__(NW * 64, kStats == 2 && NW == kFusedStatsWaves ? 1 
         qv[c][2 * e + 1] = (r < G) ? hi_bf16(ww[e]) : 0.f;
       }
     }
-    if (kReset) {
-      const int64_t lw1 = (int64_t)L + geo.window - 1;
-      const int64_t pos_b = pos < lw1 ? pos : lw1;
+    if (kReset) {   // the query at its renumbered position min(p, L + W - 1), for prefix slots
 #pragma unroll
       for (int c = 0; c < NC / 2; ++c) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          float cs = 1.f, sn = 0.f;
-          if (a.rope.enabled) rope_cos_sin(pos_b, a.rope.inv_freq[32 * c + 8 * g + i], cs, sn);
+          const float cs = __shfl(csb_l, 32 * c + 8 * g + i), sn = __shfl(snb_l, 32 * c + 8 * g + i);
           const float x1 = qv[c][i], x2 = qv[c + NC / 2][i];
           qop_b[c][i] = (bf16)((x1 * cs - x2 * sn) * a.scale_log2);
           qop_b[c + NC / 2][i] = (bf16)((x2 * cs + x1 * sn) * a.scale_log2);
@@ -349,8 +358,7 @@ __global__ __launch_bounds__(NW * 64, kStats == 2 && NW == kFusedStatsWaves ? 1 
       for (int c = 0; c < NC / 2; ++c) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          float cs, sn;
-          rope_cos_sin(pos, a.rope.inv_freq[32 * c + 8 * g + i], cs, sn);
+          const float cs = __shfl(cs_l, 32 * c + 8 * g + i), sn = __shfl(sn_l, 32 * c + 8 * g + i);
           const float x1 = qv[c][i], x2 = qv[c + NC / 2][i];
           qv[c][i] = x1 * cs - x2 * sn;
           qv[c + NC / 2][i] = x2 * cs + x1 * sn;
@@ -384,12 +392,11 @@ __global__ __launch_bounds__(NW * 64, kStats == 2 && NW == kFusedStatsWaves ? 1 
         const uint16_t* vn = static_cast<const uint16_t*>(a.v_new) + ((int64_t)s * geo.hkv + h) * D;
         uint16_t* kw = const_cast<uint16_t*>(kc) + base;
         uint16_t* vw = const_cast<uint16_t*>(vc) + base;
-        for (int i = lane; i < D / 2; i += 64) {   // rotate-half pair (i, i + D/2), as the append kernel
+        if (lane < D / 2) {   // rotate-half pair (lane, lane + D/2) at pos: this lane's cos/sin, as the append kernel
+          const int i = lane;
           const float x1 = bf16_to_f32(kn[i]), x2 = bf16_to_f32(kn[i + D / 2]);
-          float cs = 1.f, sn_ = 0.f;
-          if (a.rope.enabled) rope_cos_sin(pos, a.rope.inv_freq[i], cs, sn_);
           float y1, y2;
-          rotate_pair(x1, x2, cs, sn_, y1, y2);
+          rotate_pair(x1, x2, cs_l, sn_l, y1, y2);
           kw[k_in_region(sn, i, D)] = f32_to_bf16_bits(y1);
           kw[k_in_region(sn, i + D / 2, D)] = f32_to_bf16_bits(y2);
           vw[v_in_region(sn, i, D)] = vn[i];

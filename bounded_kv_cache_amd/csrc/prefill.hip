@@ -382,12 +382,10 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const TileRange tr = pf_tile_range(geo, it.qt);
-  const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
-  for (int32_t ci = 0; ci < n_cand; ++ci) {
-    const int32_t kt = ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix);
-    const int kind = pf_classify(geo, it.qt, kt);
-    if (kind == 0) continue;
+  const Walk walk = pf_walk(geo, it.qt);
+  for (int32_t ci = 0; ci < walk.n_cand; ++ci) {
+    const int32_t kt = pf_walk_tile(walk, ci);
+    const int kind = pf_walk_kind(geo, it.qt, walk, ci);
     __syncthreads();
     for (int idx = tid; idx < BN * D; idx += 64) {
       const int j = idx / D, d = idx % D;
@@ -540,24 +538,13 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
     for (int p = 0; p < DMA; ++p) *reinterpret_cast<u32x4*>(dst + (p * 4 + wave) * 512 + lane * 8) = r[p];
   };
 
-  const TileRange tr = pf_tile_range(geo, it.qt);
-  const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
-  auto cand_tile = [&](int32_t ci) { return ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix); };
-  // Every candidate is walked: a candidate with no visible pair (rare: the
-  // prefix and band ranges are exact except at their ends) is treated as a
-  // partly visible tile whose mask hides everything, which keeps the walk free
-  // of data-dependent loops.  Loads past the last candidate repeat it.
-  // prefix candidates: the general classification; band candidates: one
-  // precomputed range of fully visible tiles
-  const FullRange full = pf_band_full_range(geo, it.qt);
-  auto kind_at = [&](int32_t ci) {
-    if (ci < tr.n_prefix) {
-      const int k = pf_classify(geo, it.qt, ci);
-      return k == 0 ? 2 : k;
-    }
-    const int32_t kt = tr.band_lo + (ci - tr.n_prefix);
-    return (kt >= full.lo && kt <= full.hi) ? 1 : 2;
-  };
+  // the walk (ps_sched.h): prefix candidates, then band candidates, each with
+  // at least one visible pair; band kinds come from one precomputed fully
+  // visible range.  Loads past the last candidate repeat it.
+  const Walk walk = pf_walk(geo, it.qt);
+  const int32_t n_cand = walk.n_cand;
+  auto cand_tile = [&](int32_t ci) { return pf_walk_tile(walk, ci); };
+  auto kind_at = [&](int32_t ci) { return pf_walk_kind(geo, it.qt, walk, ci); };
   auto tile_at = [&](int32_t ci) { return cand_tile(ci < n_cand ? ci : n_cand - 1); };
 
   // tiles c0, c0 + 1 of the walk (candidate indices); K(0), V(0), K(1) load
@@ -841,7 +828,7 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
 }
 
 // ---------------------------------------------------------------------------
-// plan export: one workgroup enumerates the same schedule the kernels walk
+// plan export: one workgroup enumerates the walk the attention kernels execute
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 256;
 
@@ -854,9 +841,7 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillGeom 
   const int32_t q0 = tid * per, q1 = q0 + per < n_qt ? q0 + per : n_qt;
   int32_t cnt = 0;
   for (int32_t qt = q0; qt < q1; ++qt) {
-    const TileRange tr = pf_tile_range(geo, qt);
-    for (int32_t kt = 0; kt < tr.n_prefix; ++kt) cnt += pf_classify(geo, qt, kt) != 0;
-    for (int32_t kt = tr.band_lo; kt <= tr.band_hi; ++kt) cnt += pf_classify(geo, qt, kt) != 0;
+    cnt += pf_walk(geo, qt).n_cand;
   }
   part[tid] = cnt;
   __syncthreads();
@@ -872,12 +857,10 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillGeom 
   __syncthreads();
   int32_t o = part[tid];
   for (int32_t qt = q0; qt < q1; ++qt) {
-    const TileRange tr = pf_tile_range(geo, qt);
-    const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
-    for (int32_t ci = 0; ci < n_cand; ++ci) {
-      const int32_t kt = ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix);
-      const int kind = pf_classify(geo, qt, kt);
-      if (!kind) continue;
+    const Walk walk = pf_walk(geo, qt);
+    for (int32_t ci = 0; ci < walk.n_cand; ++ci) {
+      const int32_t kt = pf_walk_tile(walk, ci);
+      const int kind = pf_walk_kind(geo, qt, walk, ci);
       if (o < max_tiles) {
         tiles[3 * (int64_t)o + 0] = qt;
         tiles[3 * (int64_t)o + 1] = kt;

@@ -23,6 +23,10 @@ struct AppendArgs {
   int32_t num_seqs;
   int32_t* slot_pos;
   RopeFreq rope;
+  // optional cos/sin of token t of sequence s at row s * tokens_per_seq + t,
+  // [rows][D/2][2] (the chunk prefill's query table holds exactly these
+  // positions); NULL: formed from the position
+  const float* rope_cs;
 };
 
 struct DecodeArgs {

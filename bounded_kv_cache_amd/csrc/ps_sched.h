@@ -101,19 +101,61 @@ struct TileRange {
 PS_HD inline TileRange pf_tile_range(const PrefillGeom& g, int32_t qt) {
   TileRange r;
   const int32_t nkt = pf_num_ktiles(g);
-  r.n_prefix = pf_min((g.L + g.bn - 1) / g.bn, nkt);
+  const int32_t n_pre = pf_min((g.L + g.bn - 1) / g.bn, nkt);
   r.band_lo = 1;
   r.band_hi = 0;
   const int32_t t0 = qt * g.bm, t1 = pf_min(g.T, t0 + g.bm) - 1;
-  if (t0 > t1 || g.Nk <= g.L) return r;
+  if (t0 > t1) {
+    r.n_prefix = 0;
+    return r;
+  }
   const int32_t u0 = g.Nk - g.T + t0, u1 = g.Nk - g.T + t1;
+  // a prefix tile that starts after the tile's last query holds no visible pair
+  r.n_prefix = pf_min(n_pre, u1 / g.bn + 1);
+  if (g.Nk <= g.L) return r;
   // chunk keys visible to some query of the tile: (u0 - W, u1] intersected with [L, Nk)
   const int32_t lo = pf_max(u0 - g.W + 1 > g.L ? u0 - g.W + 1 : g.L, g.L);
   const int32_t hi = pf_min(u1, g.Nk - 1);
   if (lo > hi) return r;
-  r.band_lo = pf_max(lo / g.bn, r.n_prefix);
+  r.band_lo = pf_max(lo / g.bn, n_pre);
   r.band_hi = hi / g.bn;
   return r;
+}
+
+// The walk of q-tile qt, shared by the attention kernels and the plan export:
+// candidates [0, n_cand) are the prefix k-tiles [0, n_prefix) followed by the
+// band k-tiles band_lo + (ci - n_prefix).  Every candidate holds a visible
+// pair (the prefix range stops at the tile's last query, the band range is
+// exact), so the walk is the plan.
+struct Walk {
+  TileRange tr;
+  FullRange full;
+  int32_t n_cand;
+};
+
+PS_HD inline Walk pf_walk(const PrefillGeom& g, int32_t qt) {
+  Walk w;
+  w.tr = pf_tile_range(g, qt);
+  w.full = pf_band_full_range(g, qt);
+  w.n_cand = w.tr.n_prefix + (w.tr.band_hi >= w.tr.band_lo ? w.tr.band_hi - w.tr.band_lo + 1 : 0);
+  return w;
+}
+
+PS_HD inline int32_t pf_walk_tile(const Walk& w, int32_t ci) {
+  return ci < w.tr.n_prefix ? ci : w.tr.band_lo + (ci - w.tr.n_prefix);
+}
+
+// Kind of candidate ci (1 full, 2 partial): prefix candidates by the general
+// classification, band candidates (chunk keys only) from the fully visible
+// range.  A candidate that held no visible pair would be reported partial, so
+// a kernel masks it whole rather than skipping its mask.
+PS_HD inline int pf_walk_kind(const PrefillGeom& g, int32_t qt, const Walk& w, int32_t ci) {
+  if (ci < w.tr.n_prefix) {
+    const int k = pf_classify(g, qt, ci);
+    return k ? k : 2;
+  }
+  const int32_t kt = w.tr.band_lo + (ci - w.tr.n_prefix);
+  return (kt >= w.full.lo && kt <= w.full.hi) ? 1 : 2;
 }
 
 }  // namespace ps

@@ -370,9 +370,10 @@ size_t ps_chunk_prefill_workspace_size(const ps_attn_desc* attn, const ps_cache_
 /* Tile shape (BM queries x BN keys) ps_prefill_attn uses for this geometry. */
 ps_status ps_prefill_tile_shape(const ps_attn_desc* attn, int32_t* block_m, int32_t* block_n);
 
-/* ps_prefill_plan -- the tile list ps_prefill_attn executes, for checking.
- * Every (q_tile, k_tile) of the BM x BN grid holding at least one visible
- * (query, key) pair, sorted by q_tile then k_tile, as int32 triples
+/* ps_prefill_plan -- the tile list ps_prefill_attn executes, for checking:
+ * the attention kernel's walk itself (the same scheduling functions), which
+ * visits exactly the (q_tile, k_tile) of the BM x BN grid holding at least one
+ * visible (query, key) pair, sorted by q_tile then k_tile, as int32 triples
  * (q_tile, k_tile, kind) with kind 1 = every pair of the full BM x BN tile
  * exists and is visible (no element mask), 2 = partial (masked).  tiles is
  * [max_tiles][3]; *num_tiles receives the total count even when it exceeds

@@ -52,3 +52,26 @@ extern "C" int ps_host_full_range_check(int T, int Nk, int L, int W, long long k
   }
   return checked;
 }
+
+// The attention kernels' walk, candidate by candidate (pf_walk / pf_walk_tile /
+// pf_walk_kind): every candidate with the kind the kernel uses for it.  Equal to
+// the oracle's element-enumerated plan when no candidate is empty and every
+// kind is right.
+extern "C" int ps_host_walk(int T, int Nk, int L, int W, long long kv_start, int bm, int bn, int* tiles,
+                            int max_tiles) {
+  ps::PrefillGeom g{T, Nk, L, W, kv_start, bm, bn};
+  int n = 0;
+  const int nqt = ps::pf_num_qtiles(g);
+  for (int qt = 0; qt < nqt; ++qt) {
+    const ps::Walk w = ps::pf_walk(g, qt);
+    for (int ci = 0; ci < w.n_cand; ++ci) {
+      if (n < max_tiles) {
+        tiles[3 * n] = qt;
+        tiles[3 * n + 1] = ps::pf_walk_tile(w, ci);
+        tiles[3 * n + 2] = ps::pf_walk_kind(g, qt, w, ci);
+      }
+      ++n;
+    }
+  }
+  return n;
+}

@@ -192,6 +192,36 @@ def test_scheduler_matches_oracle_truncated_backprop_shape(sched):
     assert got == oracle.tile_plan(8192, 8292, 100, 2048, 98304, 128, 64)
 
 
+def _host_walk(sched, T, Nk, L, W, start, bm, bn):
+    n = sched.ps_host_walk(T, Nk, L, W, start, bm, bn, None, 0)
+    buf = np.zeros((max(n, 1), 3), dtype=np.int32)
+    sched.ps_host_walk(T, Nk, L, W, start, bm, bn, buf.ctypes.data, n)
+    return [tuple(int(x) for x in r) for r in buf[:n]]
+
+
+def test_kernel_walk_is_the_oracle_plan(sched):
+    # the attention kernels walk exactly the exported plan: every candidate tile
+    # holds a visible pair and gets the oracle's kind (queries reaching far into
+    # a long prefix included, where prefix tiles past the queries must not be walked)
+    sched.ps_host_walk.restype = ctypes.c_int
+    sched.ps_host_walk.argtypes = sched.ps_host_plan.argtypes
+    cases = [(8192, 8292, 100, 2048, 98304, 128, 64), (300, 300, 250, 40, 250, 128, 64),
+             (200, 200, 200, 7, 200, 64, 64), (1000, 1000, 700, 100, 700, 128, 64)]
+    rs = np.random.default_rng(1)
+    for _ in range(300):
+        bm, bn = [(128, 64), (64, 64), (4, 4), (2, 3), (16, 8)][rs.integers(5)]
+        L = int(rs.integers(0, 300))
+        chunk = int(rs.integers(1, 200))
+        nk = L + chunk
+        if rs.random() < 0.5:
+            start, T = L, int(rs.integers(1, nk + 1))
+        else:
+            start, T = L + int(rs.integers(0, 500)), int(rs.integers(1, chunk + 1))
+        cases.append((T, nk, L, int(rs.integers(1, 300)), start, bm, bn))
+    for c in cases:
+        assert _host_walk(sched, *c) == oracle.tile_plan(*c), c
+
+
 def test_chunk_prefill_validation_and_workspace(lib):
     a, c = _descs()
     S, T = 3, 100
