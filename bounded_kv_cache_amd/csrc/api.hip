@@ -393,6 +393,7 @@ ps_status decode_call(const ps_attn_desc* attn, const ps_cache_desc* cache, cons
   a.scale_log2 = attn->softmax_scale * 1.4426950408889634f;
   a.rope = make_rope(attn);
   a.reset_pe = attn->pe_mode == PS_PE_RESET ? 1 : 0;
+  a.wide = (int64_t)num_seqs * attn->num_kv_heads * splits <= device_cu_count() ? 1 : 0;
   a.heavy_count = nullptr;
   a.heavy_score = nullptr;
   a.heavy_slots = 0;

@@ -29,7 +29,11 @@
 #include "ps_internal.h"
 
 // Launch shape of the bf16 kernel: waves per workgroup and the minimum number
-// of resident workgroups per CU the register allocation must allow.
+// of resident workgroups per CU the register allocation must allow.  A launch
+// with no more workgroups than CUs (few sequences: 64 sequences x 2 KV heads x
+// 2 splits fill 256 CUs once) runs eight waves per workgroup instead, one
+// workgroup per CU, so each CU keeps as many loads in flight as two 4-wave
+// workgroups would.
 #ifndef PS_DECODE_WAVES
 #define PS_DECODE_WAVES 4
 #endif
@@ -63,7 +67,7 @@ __device__ inline u32x4 stream_load(const uint16_t* p) {
 // kAppend: the step's token (k_new / v_new at pos) is appended by this kernel
 // (one launch per decode step instead of an append launch and a decode launch).
 template <int D, int NW, bool kReset, int kStats, bool kAppend = false>
-__global__ __launch_bounds__(NW * 64, kStats == 2 && NW == kFusedStatsWaves ? 1 : PS_DECODE_MIN_BLOCKS) void decode_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : PS_DECODE_MIN_BLOCKS) void decode_bf16_kernel(
     DecodeArgs a) {
   constexpr int NC = D / 32;   // QK k-steps (32 dims each)
   constexpr int NDT = D / 16;  // PV d-tiles (16 dims each)
@@ -719,12 +723,16 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     else if (a.heavy_score)
       hipLaunchKernelGGL((decode_bf16_kernel<D, kFusedStatsWaves, false, 2>), grid, dim3(kFusedStatsWaves * 64), 0,
                          stream, a);
+    else if (a.k_new && a.wide)
+      hipLaunchKernelGGL((decode_bf16_kernel<D, 8, false, 0, true>), grid, dim3(8 * 64), 0, stream, a);
     else if (a.k_new)
       hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, 0, true>), grid, dim3(NW * 64), 0, stream, a);
     else if (a.heavy_count)
       hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, 1>), grid, dim3(NW * 64), 0, stream, a);
     else if (a.reset_pe)
       hipLaunchKernelGGL((decode_bf16_kernel<D, NW, true, 0>), grid, dim3(NW * 64), 0, stream, a);
+    else if (a.wide)
+      hipLaunchKernelGGL((decode_bf16_kernel<D, 8, false, 0>), grid, dim3(8 * 64), 0, stream, a);
     else
       hipLaunchKernelGGL((decode_bf16_kernel<D, NW, false, 0>), grid, dim3(NW * 64), 0, stream, a);
   } else {

@@ -49,6 +49,10 @@ struct DecodeArgs {
   float scale_log2;       // softmax_scale * log2(e)
   RopeFreq rope;
   int32_t reset_pe;       // 1: Reset PE scoring (prefix slots use the renumbered query)
+  // 1: the launch has at most one workgroup per compute unit; the plain and
+  // append-fused bf16 kernels then run eight waves per workgroup (twice the
+  // loads in flight per CU)
+  int32_t wide;
   // heavy-hitter mode (NULL / 0 otherwise): visible slots are [0, min(p+1, L+W) + heavy_count)
   const int32_t* heavy_count;  // [num_seqs][hkv]
   int32_t heavy_slots;         // H: heavy slots after the window, L + W + H <= slot_capacity
