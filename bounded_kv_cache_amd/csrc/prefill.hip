@@ -173,18 +173,21 @@ struct Item {
   bool valid;
 };
 __device__ inline Item decode_item(const PrefillArgs& a, int32_t n_qt) {
-  const int64_t total = (int64_t)a.batch * a.hq * n_qt;
-  const int64_t per = (total + 7) / 8;
-  const int64_t lin = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  // the host keeps the item count below 2^31, so 32-bit unsigned arithmetic
+  // is exact (64-bit divisions would cost hundreds of scalar instructions)
+  const uint32_t total = (uint32_t)a.batch * (uint32_t)a.hq * (uint32_t)n_qt;
+  const uint32_t per = (total + 7) / 8;
+  const uint32_t lin = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  const uint32_t group = (uint32_t)a.group, nq = (uint32_t)n_qt, hkv = (uint32_t)a.hkv;
   Item it;
   it.valid = lin < total;
-  const int32_t hg = (int32_t)(lin % a.group);
-  int64_t rest = lin / a.group;
-  it.qt = (int32_t)(rest % n_qt);
-  rest /= n_qt;
-  const int32_t kvh = (int32_t)(rest % a.hkv);
-  it.b = (int32_t)(rest / a.hkv);
-  it.hq = kvh * a.group + hg;
+  const uint32_t hg = lin % group;
+  uint32_t rest = lin / group;
+  it.qt = (int32_t)(rest % nq);
+  rest /= nq;
+  const uint32_t kvh = rest % hkv;
+  it.b = (int32_t)(rest / hkv);
+  it.hq = (int32_t)(kvh * group + hg);
   return it;
 }
 
@@ -538,6 +541,28 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
     for (int p = 0; p < DMA; ++p) *reinterpret_cast<u32x4*>(dst + (p * 4 + wave) * 512 + lane * 8) = r[p];
   };
 
+  // The query row and its cos/sin are loaded first, then the walk is formed
+  // and the first key/value tiles are requested: every load of the prologue is
+  // in flight before the first use, so they share one memory round trip.
+  const int32_t t = it.qt * BM + wave * 32 + col;
+  const bool row_ok = t < a.num_q;
+  const int32_t u = num_k - a.num_q + t;  // key index of this lane's query
+  u32x4 qw[KS], cw[KS / 2][4];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           (((int64_t)it.b * a.num_q + (row_ok ? t : 0)) * a.hq + it.hq) * D;
+    // cos/sin of the query position: one table row per query (uniform
+    // geometry) or per (sequence, query) (chunks continuing a ring); pairs
+    // 16 ks + 8 hf + [0, 8) as 4 x 16 bytes per ks
+    const float* cs = a.rope_cs + ((kPerSeq ? (int64_t)it.b * a.num_q : 0) + (row_ok ? t : 0)) * (D / 2) * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qw[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hf);
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cw[ks][j] = *reinterpret_cast<const u32x4*>(cs + 2 * (16 * ks + 8 * hf) + 4 * j);
+  }
+
   // the walk (ps_sched.h): prefix candidates, then band candidates, each with
   // at least one visible pair; band kinds come from one precomputed fully
   // visible range.  Loads past the last candidate repeat it.
@@ -559,33 +584,22 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
   }
 
   // ---- query operand (B of S^T = K Q^T): query row t, dims 16*ks + 8*hf + e ----
-  const int32_t t = it.qt * BM + wave * 32 + col;
-  const bool row_ok = t < a.num_q;
-  const int32_t u = num_k - a.num_q + t;  // key index of this lane's query
   bf16x8 qop[KS];
   {
     float qv[KS][8];
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           (((int64_t)it.b * a.num_q + (row_ok ? t : 0)) * a.hq + it.hq) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hf);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qv[ks][2 * e] = lo_bf16(ww[e]);
-        qv[ks][2 * e + 1] = hi_bf16(ww[e]);
+        qv[ks][2 * e] = lo_bf16(qw[ks][e]);
+        qv[ks][2 * e + 1] = hi_bf16(qw[ks][e]);
       }
-    }
-    // cos/sin of the query position: one table row per query (uniform
-    // geometry) or per (sequence, query) (chunks continuing a ring)
-    const float* cs = a.rope_cs + ((kPerSeq ? (int64_t)it.b * a.num_q : 0) + (row_ok ? t : 0)) * (D / 2) * 2;
 #pragma unroll
     for (int ks = 0; ks < KS / 2; ++ks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int i = 16 * ks + 8 * hf + e;
-        const float c = cs[2 * i], s = cs[2 * i + 1];
+        const float c = __uint_as_float(cw[ks][e / 2][2 * (e % 2)]);
+        const float s = __uint_as_float(cw[ks][e / 2][2 * (e % 2) + 1]);
         const float x1 = qv[ks][e], x2 = qv[ks + KS / 2][e];
         qv[ks][e] = x1 * c - x2 * s;
         qv[ks + KS / 2][e] = x2 * c + x1 * s;
