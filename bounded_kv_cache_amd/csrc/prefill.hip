@@ -443,13 +443,14 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 // multiplied into O (MFMA), the scores of tile j+1 are computed (MFMA), so each
 // wave always has independent matrix work to issue next to its vector work.
 // K and V^T tiles go global -> LDS directly (global_load_lds_dwordx4, no
-// staging registers) into two-deep rings: at step j the loads of K(j+2) and
-// V(j+1) are in flight.  Inside a tile the 16-byte chunks of a row are
-// XOR-swizzled by row so that the operand reads (16 consecutive rows, one chunk
-// column) fall in distinct LDS banks.  The four buffers are separate LDS
-// objects and the loop is unrolled by two, so every access names its buffer:
-// the compiler can then see that a load in flight into one buffer does not
-// alias reads of another and does not wait for it.
+// staging registers) into a three-deep K ring and a two-deep V^T ring: step j
+// requests K(j+3) and V(j+1) and ends once K(j+2) and V(j+1) have landed, so a
+// K tile has two steps to arrive and a V^T tile one.  Inside a tile the
+// 16-byte chunks of a row are XOR-swizzled by row so that the operand reads
+// (16 consecutive rows, one chunk column) fall in distinct LDS banks.  The
+// loads are issued as inline assembly with explicit waits: the compiler,
+// seeing a direct-to-LDS load in flight, would make the next read of any
+// buffer it may alias wait for every outstanding load.
 template <int CH>
 __device__ inline int chunk_swizzle(int row) {   // CH 16-byte chunks per row (8 or 16)
   return (row / (16 / CH)) & (CH - 1);
@@ -463,9 +464,27 @@ __device__ inline void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// one wave load of 64 x 16 bytes into 1 KB of LDS at `lds` (lane i -> lds + 16 i)
-__device__ inline void load_to_lds(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+// One wave load of 64 x 16 bytes into 1 KB of LDS at byte address `lds`
+// (wave-uniform; lane i -> lds + 16 i), issued as inline assembly so that the
+// compiler neither tracks it nor inserts waits for it: the kernel waits for
+// these loads itself, with explicit vector-memory counts (the loads complete
+// in issue order).  M0, which carries the LDS address, is saved and restored.
+__device__ inline void dma_to_lds(const void* src, uint32_t lds) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+// s_waitcnt operand: at most n vector memory operations outstanding, the LDS and export counters not waited on
+constexpr int vmcnt_only(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+__device__ inline uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
 template <int D, bool kPerSeq>
@@ -476,10 +495,10 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
   constexpr int KCH = D / 8;        // 16-byte chunks per K row
   constexpr int VCH = BN / 8;       // 16-byte chunks per V^T row
   constexpr int DMA = BN * D / 8 / 256;   // 1 KB wave loads per wave per tile (same for K and V^T)
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[BN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[BN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[D * BN];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[D * BN];
+  constexpr int SLOT = BN * D * 2;   // bytes of one K or V^T tile
+  // K ring of three tiles, V^T ring of two (80 KB at D = 128: two workgroups fill a CU's LDS)
+  __shared__ __attribute__((aligned(1024))) uint16_t k_ring[3 * BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_ring[2 * D * BN];
 
   PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, BM, BN};
   const int32_t n_qt = pf_num_qtiles(geo);
@@ -511,34 +530,18 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
                                    ((lane % KCH) ^ chunk_swizzle<KCH>(wave * (64 / KCH) + lane / KCH)) * 8);
   const uint32_t voff = (uint32_t)(lane / VCH) * (uint32_t)nkp +
                         (uint32_t)(((lane % VCH) ^ chunk_swizzle<VCH>(wave * (64 / VCH) + lane / VCH)) * 8);
-  auto load_k = [&](int32_t kt, uint16_t* dst) {
+  // tile kt -> ring slot `slot`: wave load p of this wave fills 1 KB chunk 4p + wave
+  const uint32_t k_lds = lds_address(k_ring) + wave * 1024, v_lds = lds_address(v_ring) + wave * 1024;
+  auto load_k = [&](int32_t kt, int32_t slot) {
     const uint16_t* src = kr + (int64_t)kt * BN * D + koff;
 #pragma unroll
-    for (int p = 0; p < DMA; ++p) load_to_lds(src + p * 4 * (64 / KCH) * D, dst + (p * 4 + wave) * 512);
+    for (int p = 0; p < DMA; ++p) dma_to_lds(src + p * 4 * (64 / KCH) * D, k_lds + slot * SLOT + p * 4096);
   };
-  auto load_v = [&](int32_t kt, uint16_t* dst) {
+  auto load_v = [&](int32_t kt, int32_t slot) {
     const uint16_t* src = vt + (int64_t)kt * BN + voff;
 #pragma unroll
     for (int p = 0; p < DMA; ++p)   // wave load p covers V^T rows (p*4 + wave) * 64/VCH + [0, 64/VCH)
-      load_to_lds(src + (int64_t)((p * 4 + wave) * (64 / VCH)) * nkp, dst + (p * 4 + wave) * 512);
-  };
-  // Inside the loop the tiles are staged through registers instead: a wave's
-  // LDS reads issued after a direct-to-LDS load wait for that load to land,
-  // which would serialise the prefetch with the tile being computed.
-  auto gload_k = [&](int32_t kt, u32x4* r) {
-    const uint16_t* src = kr + (int64_t)kt * BN * D + koff;
-#pragma unroll
-    for (int p = 0; p < DMA; ++p) r[p] = *reinterpret_cast<const u32x4*>(src + p * 4 * (64 / KCH) * D);
-  };
-  auto gload_v = [&](int32_t kt, u32x4* r) {
-    const uint16_t* src = vt + (int64_t)kt * BN + voff;
-#pragma unroll
-    for (int p = 0; p < DMA; ++p)
-      r[p] = *reinterpret_cast<const u32x4*>(src + (int64_t)((p * 4 + wave) * (64 / VCH)) * nkp);
-  };
-  auto lstore = [&](uint16_t* dst, const u32x4* r) {
-#pragma unroll
-    for (int p = 0; p < DMA; ++p) *reinterpret_cast<u32x4*>(dst + (p * 4 + wave) * 512 + lane * 8) = r[p];
+      dma_to_lds(src + (int64_t)((p * 4 + wave) * (64 / VCH)) * nkp, v_lds + slot * SLOT + p * 4096);
   };
 
   // The query row and its cos/sin are loaded first, then the walk is formed
@@ -572,15 +575,12 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
   auto kind_at = [&](int32_t ci) { return pf_walk_kind(geo, it.qt, walk, ci); };
   auto tile_at = [&](int32_t ci) { return cand_tile(ci < n_cand ? ci : n_cand - 1); };
 
-  // tiles c0, c0 + 1 of the walk (candidate indices); K(0), V(0), K(1) load
-  // while the query prologue runs, K(2) is staged in registers one step ahead
-  // of its LDS store
-  u32x4 kst[DMA];
+  // K(0), V(0), K(1) load while the query prologue runs (the prologue waits
+  // for them), K(2) after it (in flight into the first step)
   if (n_cand > 0) {
-    load_k(tile_at(0), k_lds0);
-    load_v(tile_at(0), v_lds0);
-    load_k(tile_at(1), k_lds1);
-    gload_k(tile_at(2), kst);
+    load_k(tile_at(0), 0);
+    load_v(tile_at(0), 0);
+    load_k(tile_at(1), 1);
   }
 
   // ---- query operand (B of S^T = K Q^T): query row t, dims 16*ks + 8*hf + e ----
@@ -722,23 +722,26 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
     }
   };
 
-  __syncthreads();
+  if (n_cand > 0) load_k(tile_at(2), 2);
+  // the query operand is formed (the compiler waited for the query loads);
+  // K(0), V(0), K(1) are complete once at most K(2)'s loads are outstanding
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(DMA));
+  lds_barrier();
   f32x16 sa[2], sb[2];   // scores of tiles c0 / c0 + 1, alternating between steps
   if (n_cand > 0) {
-    qk(k_lds0, sa);
+    qk(k_ring, sa);
     if (kind_at(0) == 2) mask(cand_tile(0), sa);
     rebase(sa, tile_max(sa));
   }
+  lds_barrier();   // every wave's reads of K(0) are done before the first step refills its slot
   int32_t c0 = 0;
-  // one step of the walk: tile c0 (scores in sc, V in vcur) and tile c0 + 1
-  // (K in knext, scores into sn); the staged K(c0 + 2) goes into kfree, V(c0 + 1)
-  // into vnext
-  auto step = [&](uint16_t* kfree, const uint16_t* knext, const uint16_t* vcur, uint16_t* vnext, f32x16* sc,
-                  f32x16* sn) {
-    lstore(kfree, kst);   // K(c0 + 2); K(c0), its previous content, was consumed last step
-    gload_k(tile_at(c0 + 3), kst);
-    u32x4 vst[DMA];
-    gload_v(tile_at(c0 + 1), vst);
+  // one step of the walk: tile c0 (scores in sc, V^T in slot vcur) and tile
+  // c0 + 1 (K in slot knext, scores into sn); V(c0 + 1) is requested into slot
+  // vnext (V(c0 - 1), read last step) and K(c0 + 3) into slot kfree (K(c0), read
+  // last step)
+  auto step = [&](int32_t kfree, int32_t knext, int32_t vcur, int32_t vnext, f32x16* sc, f32x16* sn) {
+    load_v(tile_at(c0 + 1), vnext);
+    load_k(tile_at(c0 + 3), kfree);
 
     // Straight-line sections, each fenced against the scheduler: one MFMA
     // step, the LDS operand reads of the next one, and a share of the vector
@@ -750,18 +753,19 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
     constexpr int EPS = 32 / KS;   // probabilities formed per QK section
     bf16x8 pop[4];
     float ps[2] = {0.f, 0.f};
-    uint32_t ko = k_off, vo = v_off;
+    // (the slot offsets are multiples of 16 KB: the chunk XORs below leave them intact)
+    uint32_t ko = knext * SLOT + k_off, vo = vcur * SLOT + v_off;
     asm volatile("" : "+v"(ko), "+v"(vo));   // keep the per-step XORs from being hoisted into registers
-    bf16x8 k0 = frag(knext, ko);
-    bf16x8 k1 = frag(knext, ko + 64 * D);
+    bf16x8 k0 = frag(k_ring, ko);
+    bf16x8 k1 = frag(k_ring, ko + 64 * D);
     bf16x8 va[MT];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 n0 = k0, n1 = k1;
       if (ks + 1 < KS) {
         const uint32_t c = ko ^ (32 * (ks + 1));
-        n0 = frag(knext, c);
-        n1 = frag(knext, c + 64 * D);
+        n0 = frag(k_ring, c);
+        n1 = frag(k_ring, c + 64 * D);
       }
       sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], ks == 0 ? negref : sn[0], 0, 0, 0);
       sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], ks == 0 ? negref : sn[1], 0, 0, 0);
@@ -782,13 +786,13 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
     l_run += ps[0] + ps[1];
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) va[mt] = frag(vcur, vo + 64 * BN * mt);
+    for (int mt = 0; mt < MT; ++mt) va[mt] = frag(v_ring, vo + 64 * BN * mt);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8 vn[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        vn[mt] = j + 1 < 4 ? frag(vcur, (vo ^ (32 * (j + 1))) + 64 * BN * mt) : va[mt];
+        vn[mt] = j + 1 < 4 ? frag(v_ring, (vo ^ (32 * (j + 1))) + 64 * BN * mt) : va[mt];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mt], pop[j], acc[mt], 0, 0, 0);
@@ -806,7 +810,6 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
       __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("" ::"v"(mx0), "v"(mx1));   // the max is formed in the PV sections above
-    lstore(vnext, vst);   // V of the previous tile, consumed
     if (c0 + 1 < n_cand) {
       if (kind_at(c0 + 1) == 2) {
         mask(cand_tile(c0 + 1), sn);
@@ -815,14 +818,24 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
         rebase(sn, max_xor32(fmaxf(mx0, mx1)));
       }
     }
-    lds_barrier();   // this step's LDS stores are visible and its LDS reads done; K(c0 + 3) stays in flight
+    // V(c0 + 1) and K(c0 + 2) have landed once at most K(c0 + 3)'s loads are
+    // outstanding; the barrier makes every wave's part visible and ends this
+    // step's reads of the slots the next step refills
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(DMA));
+    lds_barrier();
     ++c0;
   };
+  int32_t r3 = 0;   // c0 mod 3: the K slot of tile c0
   while (c0 < n_cand) {
-    step(k_lds0, k_lds1, v_lds0, v_lds1, sa, sb);
+    const int32_t r3n = r3 == 2 ? 0 : r3 + 1;
+    step(r3, r3n, 0, 1, sa, sb);
+    r3 = r3n;
     if (c0 >= n_cand) break;
-    step(k_lds1, k_lds0, v_lds1, v_lds0, sb, sa);
+    const int32_t r3m = r3 == 2 ? 0 : r3 + 1;
+    step(r3, r3m, 1, 0, sb, sa);
+    r3 = r3m;
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // no load into LDS outlives the loop
 
   // ---- epilogue: l across the two halves, normalise, store ----
   l_run = sum_xor32(l_run);
