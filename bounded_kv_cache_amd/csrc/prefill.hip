@@ -468,16 +468,14 @@ __device__ inline void lds_barrier() {
 // (wave-uniform; lane i -> lds + 16 i), issued as inline assembly so that the
 // compiler neither tracks it nor inserts waits for it: the kernel waits for
 // these loads itself, with explicit vector-memory counts (the loads complete
-// in issue order).  M0, which carries the LDS address, is saved and restored.
+// in issue order).  M0 carries the LDS address; nothing else in the kernels
+// that use this sets or reads M0.
 __device__ inline void dma_to_lds(const void* src, uint32_t lds) {
-  uint32_t m0_saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(m0_saved)
+      "global_load_lds_dwordx4 %0, off"
+      :
       : "v"(src), "s"(lds)
       : "memory");
 }
@@ -756,19 +754,26 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
     // (the slot offsets are multiples of 16 KB: the chunk XORs below leave them intact)
     uint32_t ko = knext * SLOT + k_off, vo = vcur * SLOT + v_off;
     asm volatile("" : "+v"(ko), "+v"(vo));   // keep the per-step XORs from being hoisted into registers
-    bf16x8 k0 = frag(k_ring, ko);
-    bf16x8 k1 = frag(k_ring, ko + 64 * D);
+    // K operands two k-steps ahead (ring of three), the first V^T operands
+    // read in the second-to-last QK section
+    bf16x8 kf[3][2];
+    kf[0][0] = frag(k_ring, ko);
+    kf[0][1] = frag(k_ring, ko + 64 * D);
+    kf[1][0] = frag(k_ring, ko ^ 32);
+    kf[1][1] = frag(k_ring, (ko ^ 32) + 64 * D);
     bf16x8 va[MT];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 n0 = k0, n1 = k1;
-      if (ks + 1 < KS) {
-        const uint32_t c = ko ^ (32 * (ks + 1));
-        n0 = frag(k_ring, c);
-        n1 = frag(k_ring, c + 64 * D);
+      if (ks + 2 < KS) {
+        const uint32_t c = ko ^ (32 * (ks + 2));
+        kf[(ks + 2) % 3][0] = frag(k_ring, c);
+        kf[(ks + 2) % 3][1] = frag(k_ring, c + 64 * D);
+      } else if (ks + 2 == KS) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) va[mt] = frag(v_ring, vo + 64 * BN * mt);
       }
-      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], ks == 0 ? negref : sn[0], 0, 0, 0);
-      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], ks == 0 ? negref : sn[1], 0, 0, 0);
+      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % 3][0], qop[ks], ks == 0 ? negref : sn[0], 0, 0, 0);
+      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % 3][1], qop[ks], ks == 0 ? negref : sn[1], 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < EPS; ++e) {
         const int idx = ks * EPS + e, m2 = idx >> 4, i = idx & 15;
@@ -776,17 +781,16 @@ __global__ __launch_bounds__(256, PS_PREFILL_MIN_BLOCKS) void prefill_bf16_kerne
         ps[i & 1] += p;
         pop[2 * m2 + (i >> 3)][i & 7] = (bf16)p;
       }
-      k0 = n0;
-      k1 = n1;
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // the next k-step's operand reads first,
+      if (ks + 2 < KS)   // the operand reads first,
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (ks + 2 == KS)
+        __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // then this k-step's MFMAs,
       __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // then the vector work
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += ps[0] + ps[1];
     float mx0 = -INFINITY, mx1 = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) va[mt] = frag(v_ring, vo + 64 * BN * mt);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8 vn[MT];
