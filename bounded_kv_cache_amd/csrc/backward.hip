@@ -246,16 +246,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   constexpr int BQ = 64;           // queries per step
   constexpr int KS = D / 16;
   constexpr int MT = D / 32;
-  constexpr int RPAD = D + 8;      // row-major query rows in LDS
-  constexpr int TPAD = BQ + 8;     // d-major rows in LDS
-  constexpr int RP = BQ * D / 8 / 256;   // 16-byte pieces per thread per block (row-major)
-  constexpr int TP = D * BQ / 8 / 256;   // (d-major)
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][BQ * RPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t o_lds[2][BQ * RPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[2][D * TPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t ot_lds[2][D * TPAD];
-  __shared__ __attribute__((aligned(16))) float l_lds[2][BQ];
-  __shared__ __attribute__((aligned(16))) float di_lds[2][BQ];
+  constexpr int RCH = D / 8;       // 16-byte chunks per row-major query row
+  constexpr int TCH = BQ / 8;      // 16-byte chunks per d-major row
+  constexpr int DMA = BQ * D / 8 / 256;   // 1 KB wave loads per wave per tile (each of the four)
+  // query block tiles, two buffers each; 16-byte chunks XOR-swizzled by row
+  // (conflict-free operand reads without padding, so whole tiles go global ->
+  // LDS directly)
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][BQ * D];    // Q'' rows
+  __shared__ __attribute__((aligned(1024))) uint16_t o_lds[2][BQ * D];    // dO rows
+  __shared__ __attribute__((aligned(1024))) uint16_t qt_lds[2][D * BQ];   // Q'' d-major
+  __shared__ __attribute__((aligned(1024))) uint16_t ot_lds[2][D * BQ];   // dO d-major
+  __shared__ __attribute__((aligned(1024))) float ld_lds[2][2 * BQ];      // lse2, then Di
 
   const int32_t n_kt = (a.num_k + BK - 1) / BK;
   const int64_t pairs = (int64_t)a.batch * a.hkv;
@@ -297,48 +298,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   const int32_t n_it = n_qb > 0 ? n_qb * a.group : 0;
   PrefillGeom cg{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, BQ, BK};
 
-  u32x4 qreg[RP], oreg[RP], qtreg[TP], otreg[TP];
-  float lreg = 0.f;
-  // block (head h, query block qb) -> registers
-#define PS_BW_GLOAD(H, QB)                                                                           \
-  do {                                                                                              \
-    const int64_t bh_ = (int64_t)b * a.hq + (H);                                                    \
-    const uint16_t* qsb_ = static_cast<const uint16_t*>(a.qs) + (bh_ * a.tqp + (int64_t)(QB) * BQ) * D; \
-    const uint16_t* qtb_ = static_cast<const uint16_t*>(a.qst) + bh_ * D * a.tqp + (int64_t)(QB) * BQ; \
-    const uint16_t* otb_ = static_cast<const uint16_t*>(a.dot) + bh_ * D * a.tqp + (int64_t)(QB) * BQ; \
-    _Pragma("unroll") for (int pc_ = 0; pc_ < RP; ++pc_) {                                          \
-      const int piece_ = tid + 256 * pc_;                                                           \
-      const int r_ = piece_ / (D / 8), c_ = (piece_ % (D / 8)) * 8;                                 \
-      qreg[pc_] = *reinterpret_cast<const u32x4*>(qsb_ + (int64_t)r_ * D + c_);                     \
-      const int32_t tr_ = pf_min((QB) * BQ + r_, a.num_q - 1);                                       \
-      oreg[pc_] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.d_out) +           \
-                                                  (((int64_t)b * a.num_q + tr_) * a.hq + (H)) * D + c_); \
-    }                                                                                               \
-    _Pragma("unroll") for (int pc_ = 0; pc_ < TP; ++pc_) {                                          \
-      const int piece_ = tid + 256 * pc_;                                                           \
-      const int r_ = piece_ / (BQ / 8), c_ = (piece_ % (BQ / 8)) * 8;                               \
-      qtreg[pc_] = *reinterpret_cast<const u32x4*>(qtb_ + (int64_t)r_ * a.tqp + c_);                \
-      otreg[pc_] = *reinterpret_cast<const u32x4*>(otb_ + (int64_t)r_ * a.tqp + c_);                \
-    }                                                                                               \
-    if (tid < 2 * BQ)                                                                               \
-      lreg = (tid < BQ ? a.lse2 : a.di)[bh_ * a.tqp + (int64_t)(QB) * BQ + (tid & (BQ - 1))];        \
-  } while (0)
-#define PS_BW_LSTORE(BUF)                                                                            \
-  do {                                                                                              \
-    _Pragma("unroll") for (int pc_ = 0; pc_ < RP; ++pc_) {                                          \
-      const int piece_ = tid + 256 * pc_;                                                           \
-      const int r_ = piece_ / (D / 8), c_ = (piece_ % (D / 8)) * 8;                                 \
-      *reinterpret_cast<u32x4*>(&q_lds[BUF][r_ * RPAD + c_]) = qreg[pc_];                           \
-      *reinterpret_cast<u32x4*>(&o_lds[BUF][r_ * RPAD + c_]) = oreg[pc_];                           \
-    }                                                                                               \
-    _Pragma("unroll") for (int pc_ = 0; pc_ < TP; ++pc_) {                                          \
-      const int piece_ = tid + 256 * pc_;                                                           \
-      const int r_ = piece_ / (BQ / 8), c_ = (piece_ % (BQ / 8)) * 8;                               \
-      *reinterpret_cast<u32x4*>(&qt_lds[BUF][r_ * TPAD + c_]) = qtreg[pc_];                         \
-      *reinterpret_cast<u32x4*>(&ot_lds[BUF][r_ * TPAD + c_]) = otreg[pc_];                         \
-    }                                                                                               \
-    if (tid < 2 * BQ) (tid < BQ ? l_lds[BUF] : di_lds[BUF])[tid & (BQ - 1)] = lreg;                 \
-  } while (0)
+  // block (head h, query block qb) -> LDS buffer bf, straight from global
+  // memory: wave load p of wave w fills chunks (4p + w) * 64 + lane of each
+  // tile; the swizzle of a chunk's row depends on (w, lane) only
+  const int rrow = wave * (64 / RCH) + lane / RCH;                 // + 4p * 64 / RCH
+  const int rchunk = (lane % RCH) ^ chunk_swizzle<RCH>(rrow);
+  const int trow = wave * (64 / TCH) + lane / TCH;                 // + 4p * 64 / TCH
+  const int tchunk = (lane % TCH) ^ chunk_swizzle<TCH>(trow);
+  auto load_block = [&](int32_t h, int32_t qb, int bf) {
+    const int64_t bh = (int64_t)b * a.hq + h;
+    const uint16_t* qsb = static_cast<const uint16_t*>(a.qs) + (bh * a.tqp + (int64_t)qb * BQ) * D;
+    const uint16_t* qtb = static_cast<const uint16_t*>(a.qst) + bh * D * a.tqp + (int64_t)qb * BQ;
+    const uint16_t* otb = static_cast<const uint16_t*>(a.dot) + bh * D * a.tqp + (int64_t)qb * BQ;
+    const uint32_t w_off = wave * 1024;
+#pragma unroll
+    for (int p = 0; p < DMA; ++p) {
+      const int r = rrow + 4 * p * (64 / RCH);   // query row of the block
+      dma_to_lds(qsb + (int64_t)r * D + rchunk * 8, lds_address(q_lds[bf]) + w_off + p * 4096);
+      const int32_t tr = pf_min(qb * BQ + r, a.num_q - 1);
+      dma_to_lds(static_cast<const uint16_t*>(a.d_out) + (((int64_t)b * a.num_q + tr) * a.hq + h) * D + rchunk * 8,
+                 lds_address(o_lds[bf]) + w_off + p * 4096);
+      const int dr = trow + 4 * p * (64 / TCH);  // dim row of the d-major tiles
+      dma_to_lds(qtb + (int64_t)dr * a.tqp + tchunk * 8, lds_address(qt_lds[bf]) + w_off + p * 4096);
+      dma_to_lds(otb + (int64_t)dr * a.tqp + tchunk * 8, lds_address(ot_lds[bf]) + w_off + p * 4096);
+    }
+    // lse2 and Di of the block's 64 queries: 2 x 256 bytes, lanes 0-31 of wave 0
+    if (wave == 0 && lane < 32) {
+      const float* src = (lane < 16 ? a.lse2 : a.di) + bh * a.tqp + (int64_t)qb * BQ + 4 * (lane & 15);
+      dma_to_lds(src, lds_address(ld_lds[bf]));
+    }
+  };
+  // operand addresses (elements) inside a tile: row-major row r, logical chunk c
+  auto rm_at = [&](int r, int c) { return r * D + ((c ^ chunk_swizzle<RCH>(r)) * 8); };
+  auto dm_at = [&](int r, int c) { return r * BQ + ((c ^ chunk_swizzle<TCH>(r)) * 8); };
 
   f32x16 dk[MT], dv[MT];
 #pragma unroll
@@ -353,10 +345,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   int32_t it = 0;
   int kind = 0;
   while (it < n_it && (kind = pf_classify(cg, qb_lo + it % n_qb, kt)) == 0) ++it;
-  if (it < n_it) {
-    PS_BW_GLOAD(kvh * a.group + it / n_qb, qb_lo + it % n_qb);
-    PS_BW_LSTORE(0);
-  }
+  if (it < n_it) load_block(kvh * a.group + it / n_qb, qb_lo + it % n_qb, 0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   __syncthreads();
   int buf = 0;
   while (it < n_it) {
@@ -366,7 +356,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     int32_t nx = it + 1;
     int nkind = 0;
     while (nx < n_it && (nkind = pf_classify(cg, qb_lo + nx % n_qb, kt)) == 0) ++nx;
-    if (nx < n_it) PS_BW_GLOAD(kvh * a.group + nx / n_qb, qb_lo + nx % n_qb);
+    if (nx < n_it) load_block(kvh * a.group + nx / n_qb, qb_lo + nx % n_qb, buf ^ 1);   // its buffer was read last iteration
     (void)h;
 
     // S = Q'' K'^T and dP = dO V^T (two 32-query M-tiles), then
@@ -380,12 +370,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     f32x16 s[2], dp[2];
     bf16x8 pb[4], sb[4];
     auto products = [&](int m2) {
-      const uint16_t* qrow = &q_lds[buf][(32 * m2 + col) * RPAD + 8 * hf];
-      const uint16_t* orow = &o_lds[buf][(32 * m2 + col) * RPAD + 8 * hf];
+      const int r = 32 * m2 + col;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(orow + 16 * ks);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&q_lds[buf][rm_at(r, 2 * ks + hf)]);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&o_lds[buf][rm_at(r, 2 * ks + hf)]);
         s[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[ks], ks == 0 ? zero : s[m2], 0, 0, 0);
         dp[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vop[ks], ks == 0 ? zero : dp[m2], 0, 0, 0);
       }
@@ -394,8 +383,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int ql = 32 * m2 + 8 * r4 + 4 * hf;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&l_lds[buf][ql]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&di_lds[buf][ql]);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&ld_lds[buf][ql]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&ld_lds[buf][BQ + ql]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
@@ -417,8 +406,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     auto dvdk = [&](int j) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&ot_lds[buf][(32 * mt + col) * TPAD + 16 * j + 8 * hf]);
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qt_lds[buf][(32 * mt + col) * TPAD + 16 * j + 8 * hf]);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&ot_lds[buf][dm_at(32 * mt + col, 2 * j + hf)]);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qt_lds[buf][dm_at(32 * mt + col, 2 * j + hf)]);
         dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pb[j], dv[mt], 0, 0, 0);
         dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb[j], dk[mt], 0, 0, 0);
       }
@@ -450,14 +439,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     dvdk(2);
     dvdk(3);
-    if (nx < n_it) PS_BW_LSTORE(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // the next block has landed (this wave's part)
     __syncthreads();
     buf ^= 1;
     it = nx;
     kind = nkind;
   }
-#undef PS_BW_GLOAD
-#undef PS_BW_LSTORE
 
   // ---- epilogue: register r of tile mt <-> dim 32*mt + 8*(r/4) + 4*hf + r%4 of key kw;
   // dK' = ln2 * acc, rotated back by -position (dims d and d + D/2 pair up: tiles mt, mt + MT/2)
@@ -499,13 +486,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
   constexpr int BM = 128, BN = 64;
   constexpr int KS = D / 16;
   constexpr int MT = D / 32;
-  constexpr int KPAD = D + 8;
-  constexpr int TPAD = BN + 8;
-  constexpr int RP = BN * D / 8 / 256;
-  constexpr int TP = D * BN / 8 / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN * KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t t_lds[2][D * TPAD];
+  constexpr int RCH = D / 8;       // 16-byte chunks per key row
+  constexpr int TCH = BN / 8;      // 16-byte chunks per d-major row
+  constexpr int DMA = BN * D / 8 / 256;   // 1 KB wave loads per wave per tile
+  // key tiles, two buffers each, 16-byte chunks XOR-swizzled by row (loaded
+  // global -> LDS directly)
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][BN * D];   // K' rows
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][BN * D];   // V rows
+  __shared__ __attribute__((aligned(1024))) uint16_t t_lds[2][D * BN];   // K' d-major
 
   PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, BM, BN};
   const int32_t n_qt = pf_num_qtiles(geo);
@@ -529,40 +517,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
   const uint16_t* vr = static_cast<const uint16_t*>(a.vr) + bkv * a.nkp * D;
   const uint16_t* ktr = static_cast<const uint16_t*>(a.krt) + bkv * D * a.nkp;
 
-  // staging: K' and V rows (row-major) and the d-major K' copy, 16-byte pieces
-  auto gload_kv = [&](int32_t kt, u32x4* kreg, u32x4* vreg) {
+  // tile kt -> LDS buffer, straight from global memory: wave load p of wave w
+  // fills chunks (4p + w) * 64 + lane; the swizzle of a chunk's row depends on
+  // (w, lane) only
+  const int rrow = wave * (64 / RCH) + lane / RCH;
+  const int rchunk = (lane % RCH) ^ chunk_swizzle<RCH>(rrow);
+  const int trow_l = wave * (64 / TCH) + lane / TCH;
+  const int tchunk = (lane % TCH) ^ chunk_swizzle<TCH>(trow_l);
+  auto load_kv = [&](int32_t kt, int b_) {
 #pragma unroll
-    for (int pc = 0; pc < RP; ++pc) {
-      const int piece = tid + 256 * pc;
-      const int64_t o = ((int64_t)kt * BN + piece / (D / 8)) * D + (piece % (D / 8)) * 8;
-      kreg[pc] = *reinterpret_cast<const u32x4*>(kr + o);
-      vreg[pc] = *reinterpret_cast<const u32x4*>(vr + o);
+    for (int p = 0; p < DMA; ++p) {
+      const int64_t o = ((int64_t)kt * BN + rrow + 4 * p * (64 / RCH)) * D + rchunk * 8;
+      dma_to_lds(kr + o, lds_address(k_lds[b_]) + wave * 1024 + p * 4096);
+      dma_to_lds(vr + o, lds_address(v_lds[b_]) + wave * 1024 + p * 4096);
     }
   };
-  auto gload_t = [&](int32_t kt, u32x4* treg) {
+  auto load_t = [&](int32_t kt, int b_) {
 #pragma unroll
-    for (int pc = 0; pc < TP; ++pc) {
-      const int piece = tid + 256 * pc;
-      treg[pc] = *reinterpret_cast<const u32x4*>(ktr + (int64_t)(piece / (BN / 8)) * a.nkp + (int64_t)kt * BN +
-                                                  (piece % (BN / 8)) * 8);
-    }
+    for (int p = 0; p < DMA; ++p)
+      dma_to_lds(ktr + (int64_t)(trow_l + 4 * p * (64 / TCH)) * a.nkp + (int64_t)kt * BN + tchunk * 8,
+                 lds_address(t_lds[b_]) + wave * 1024 + p * 4096);
   };
-  auto lstore_kv = [&](int b_, const u32x4* kreg, const u32x4* vreg) {
-#pragma unroll
-    for (int pc = 0; pc < RP; ++pc) {
-      const int piece = tid + 256 * pc;
-      const int o = (piece / (D / 8)) * KPAD + (piece % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&k_lds[b_][o]) = kreg[pc];
-      *reinterpret_cast<u32x4*>(&v_lds[b_][o]) = vreg[pc];
-    }
-  };
-  auto lstore_t = [&](int b_, const u32x4* treg) {
-#pragma unroll
-    for (int pc = 0; pc < TP; ++pc) {
-      const int piece = tid + 256 * pc;
-      *reinterpret_cast<u32x4*>(&t_lds[b_][(piece / (BN / 8)) * TPAD + (piece % (BN / 8)) * 8]) = treg[pc];
-    }
-  };
+  // operand addresses (elements) inside a tile: row-major row r, logical chunk c
+  auto rm_at = [&](int r, int c) { return r * D + ((c ^ chunk_swizzle<RCH>(r)) * 8); };
+  auto dm_at = [&](int r, int c) { return r * BN + ((c ^ chunk_swizzle<TCH>(r)) * 8); };
 
   const TileRange tr = pf_tile_range(geo, qt);
   const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
@@ -577,19 +555,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
   int kind0 = 0, kind1 = 0;
   int32_t c0 = next_live(0, kind0);
   int32_t c1 = c0 < n_cand ? next_live(c0 + 1, kind1) : n_cand;
-  {
-    u32x4 kreg[RP], vreg[RP], treg[TP];
-    if (c0 < n_cand) {
-      gload_kv(cand_tile(c0), kreg, vreg);
-      gload_t(cand_tile(c0), treg);
-      lstore_kv(0, kreg, vreg);
-      lstore_t(0, treg);
-    }
-    if (c1 < n_cand) {
-      gload_kv(cand_tile(c1), kreg, vreg);
-      lstore_kv(1, kreg, vreg);
-    }
+  if (c0 < n_cand) {
+    load_kv(cand_tile(c0), 0);
+    load_t(cand_tile(c0), 0);
   }
+  if (c1 < n_cand) load_kv(cand_tile(c1), 1);
 
   // this lane's query: B operands of S^T = K' Q''^T and dP^T = V dO^T
   const int32_t t = qt * BM + wave * 32 + col;
@@ -648,18 +618,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
   auto sdp = [&](int b_, f32x16* st, f32x16* dpt) {
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
-      const uint16_t* krow = &k_lds[b_][(32 * m2 + col) * KPAD + 8 * hf];
-      const uint16_t* vrow = &v_lds[b_][(32 * m2 + col) * KPAD + 8 * hf];
+      const int r = 32 * m2 + col;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + 16 * ks);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&k_lds[b_][rm_at(r, 2 * ks + hf)]);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&v_lds[b_][rm_at(r, 2 * ks + hf)]);
         st[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[ks], ks == 0 ? neg_lse2 : st[m2], 0, 0, 0);
         dpt[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dop[ks], ks == 0 ? zero : dpt[m2], 0, 0, 0);
       }
     }
   };
 
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // (lse2 / Di and the first tiles)
   __syncthreads();
   f32x16 sa[2], pa[2], sb_[2], pb[2];   // S^T, dP^T of tiles c0 / c1, alternating between steps
   if (c0 < n_cand) {
@@ -670,32 +640,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
   // wave's own matrix and vector work must overlap): the S^T / dP^T products
   // of tile c1 run while tile c0's dS is formed, then dQ^T += K'^T dS^T for
   // tile c0.  K'/V of c1 sit in kv buffer kvb ^ 1, K'^T of c0 in t buffer tb;
-  // the next tiles' data are staged in registers and stored after the LDS
-  // reads of the step.
+  // the next tiles go straight to LDS: K'/V of c2 into kvb (c0's, read last
+  // step) and K'^T of c1 into tb ^ 1 (read the step before).
   int kvb = 0, tb = 0;
   auto step = [&](f32x16* sc, f32x16* pc, f32x16* sn, f32x16* pn) {
     int kind2 = 0;
     const int32_t c2 = c1 < n_cand ? next_live(c1 + 1, kind2) : n_cand;
-    u32x4 kreg[RP], vreg[RP], treg[TP];
-    if (c2 < n_cand) gload_kv(cand_tile(c2), kreg, vreg);
-    if (c1 < n_cand) gload_t(cand_tile(c1), treg);
+    if (c2 < n_cand) load_kv(cand_tile(c2), kvb);
+    if (c1 < n_cand) load_t(cand_tile(c1), tb ^ 1);
 
     // sections: one k-step of the four S^T / dP^T products of tile c1 (its
     // operands read one k-step ahead) and a quarter-eighth of tile c0's dS
     constexpr int EPS = 32 / KS;
     bf16x8 sbv[4];
-    const uint16_t* krow = &k_lds[kvb ^ 1][col * KPAD + 8 * hf];
-    const uint16_t* vrow = &v_lds[kvb ^ 1][col * KPAD + 8 * hf];
-    bf16x8 k0 = *reinterpret_cast<const bf16x8*>(krow), k1 = *reinterpret_cast<const bf16x8*>(krow + 32 * KPAD);
-    bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vrow), v1 = *reinterpret_cast<const bf16x8*>(vrow + 32 * KPAD);
+    const uint16_t* kb = k_lds[kvb ^ 1];
+    const uint16_t* vb = v_lds[kvb ^ 1];
+    auto kfrag = [&](const uint16_t* t_, int r, int ks) { return *reinterpret_cast<const bf16x8*>(&t_[rm_at(r, 2 * ks + hf)]); };
+    bf16x8 k0 = kfrag(kb, col, 0), k1 = kfrag(kb, col + 32, 0);
+    bf16x8 v0 = kfrag(vb, col, 0), v1 = kfrag(vb, col + 32, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 nk0 = k0, nk1 = k1, nv0 = v0, nv1 = v1;
       if (ks + 1 < KS) {
-        nk0 = *reinterpret_cast<const bf16x8*>(krow + 16 * (ks + 1));
-        nk1 = *reinterpret_cast<const bf16x8*>(krow + 32 * KPAD + 16 * (ks + 1));
-        nv0 = *reinterpret_cast<const bf16x8*>(vrow + 16 * (ks + 1));
-        nv1 = *reinterpret_cast<const bf16x8*>(vrow + 32 * KPAD + 16 * (ks + 1));
+        nk0 = kfrag(kb, col, ks + 1);
+        nk1 = kfrag(kb, col + 32, ks + 1);
+        nv0 = kfrag(vb, col, ks + 1);
+        nv1 = kfrag(vb, col + 32, ks + 1);
       }
       sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], ks == 0 ? neg_lse2 : sn[0], 0, 0, 0);
       sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], ks == 0 ? neg_lse2 : sn[1], 0, 0, 0);
@@ -717,16 +687,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
     }
     // dQ''^T += K'^T dS^T for tile c0: k-step j covers keys 16j + 8*(e/4) + 4*hf + e%4
     {
-      const uint16_t* trow = &t_lds[tb][col * TPAD + 8 * hf];
+      const uint16_t* tt = t_lds[tb];
       bf16x8 ta[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) ta[mt] = *reinterpret_cast<const bf16x8*>(trow + 32 * mt * TPAD);
+      for (int mt = 0; mt < MT; ++mt) ta[mt] = *reinterpret_cast<const bf16x8*>(&tt[dm_at(32 * mt + col, hf)]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x8 tn[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          tn[mt] = j + 1 < 4 ? *reinterpret_cast<const bf16x8*>(trow + 32 * mt * TPAD + 16 * (j + 1)) : ta[mt];
+          tn[mt] = j + 1 < 4 ? *reinterpret_cast<const bf16x8*>(&tt[dm_at(32 * mt + col, 2 * (j + 1) + hf)]) : ta[mt];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[mt], sbv[j], acc[mt], 0, 0, 0);
 #pragma unroll
@@ -737,8 +707,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
       }
     }
     if (__builtin_expect(c1 < n_cand && kind1 == 2, 0)) mask(cand_tile(c1), sn);   // partial tiles are few
-    if (c2 < n_cand) lstore_kv(kvb, kreg, vreg);   // K'/V of c0, its previous content, were consumed last step
-    if (c1 < n_cand) lstore_t(tb ^ 1, treg);       // K'^T of the tile before c0, consumed last step
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // this wave's part of the next tiles has landed
     __syncthreads();
     kvb ^= 1;
     tb ^= 1;

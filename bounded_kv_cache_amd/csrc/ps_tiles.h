@@ -56,4 +56,41 @@ __device__ inline void store_vec(T* p, const float* x, int n) {
   }
 }
 
+// 16-byte chunk swizzle of an LDS tile with CH chunks per row (8 or 16): chunk
+// c of row r lives at chunk c ^ chunk_swizzle<CH>(r), so that 16 consecutive
+// rows read at one logical chunk fall in distinct LDS banks
+template <int CH>
+__device__ inline int chunk_swizzle(int row) {   // CH 16-byte chunks per row (8 or 16)
+  return (row / (16 / CH)) & (CH - 1);
+}
+
+// Workgroup barrier that orders LDS only: global loads in flight stay in
+// flight (__syncthreads would wait for them too).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One wave load of 64 x 16 bytes into 1 KB of LDS at byte address `lds`
+// (wave-uniform; lane i -> lds + 16 i), issued as inline assembly so that the
+// compiler neither tracks it nor inserts waits for it: the kernel waits for
+// these loads itself, with explicit vector-memory counts (the loads complete
+// in issue order).  M0 carries the LDS address; nothing else in the kernels
+// that use this sets or reads M0.
+__device__ inline void dma_to_lds(const void* src, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
+}
+// s_waitcnt operand: at most n vector memory operations outstanding, the LDS and export counters not waited on
+constexpr int vmcnt_only(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+__device__ inline uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 }  // namespace ps
