@@ -247,7 +247,7 @@ size_t chunk_ws_bytes(const ps_attn_desc* a, const ps_cache_desc* c, int32_t num
 
 // Backward workspace layout (each piece 256-byte aligned).
 struct BwdLayout {
-  size_t kr, krt, vr, qs, qst, dot, lse2, di, cs_q, cs_k, total;
+  size_t kr, krt, vr, qs, lse2, di, cs_q, cs_k, total;
   int32_t nkp, tqp;
 };
 
@@ -266,8 +266,6 @@ BwdLayout bwd_layout(const ps_attn_desc* a, int32_t batch, int32_t num_q, int32_
   l.krt = o; o += kv;
   l.vr = o; o += kv;
   l.qs = o; o += qv;
-  l.qst = o; o += qv;
-  l.dot = o; o += qv;
   l.lse2 = o; o += rows;
   l.di = o; o += rows;
   l.cs_q = o; o += al((size_t)num_q * d * sizeof(float));
@@ -753,8 +751,6 @@ ps_status ps_prefill_attn_backward(const ps_attn_desc* attn, int32_t window, int
   a.krt = w + l.krt;
   a.vr = w + l.vr;
   a.qs = w + l.qs;
-  a.qst = w + l.qst;
-  a.dot = w + l.dot;
   a.lse2 = reinterpret_cast<float*>(w + l.lse2);
   a.di = reinterpret_cast<float*>(w + l.di);
   a.cs_q = reinterpret_cast<float*>(w + l.cs_q);

@@ -15,16 +15,16 @@
 // Pipeline of one call:
 //   1. key prep: K' row-major and d-major (keys permuted per 16, vt_slot), V
 //      row-major, zero padded to nkp keys; cos/sin of the key positions.
-//   2. query prep: Q'' row-major and d-major (queries permuted per 16), dO
-//      d-major (permuted), lse2 (+inf on padding rows so their P is 0), Di;
-//      cos/sin of the query positions.
+//   2. query prep: Q'' row-major, lse2 (+inf on padding rows so their P is 0),
+//      Di; cos/sin of the query positions.
 //   3. dk/dv kernel: one workgroup per (batch, KV head, 128-key tile), each wave
 //      owning 32 keys whose K' and V stay in registers as MFMA B operands; it
 //      walks the query heads of the group and the 64-query blocks that see the
 //      tile.  S = Q'' K'^T and dP = dO V^T put queries on the M side, so each
 //      lane owns one key and the S / dS registers are directly the B operands of
-//      dV^T += dO^T P and dK^T += Q''^T dS (the d-major copies carry the matching
-//      query permutation).  No atomics: every dk / dv row has one writer.
+//      dV^T += dO^T P and dK^T += Q''^T dS, whose A operands (dO^T, Q''^T in the
+//      matching query order) come from the row-major tiles by transposing LDS
+//      reads.  No atomics: every dk / dv row has one writer.
 //   4. dq kernel: the forward's work decomposition and key-tile schedule:
 //      S^T = K' Q''^T, dP^T = V dO^T, dS^T, then dQ^T += K'^T dS^T.
 // All arithmetic on MFMA is bf16 x bf16 -> fp32; P and dS are rounded to bf16
@@ -148,8 +148,6 @@ __global__ __launch_bounds__(256) void bwd_query_prep_kernel(BackwardArgs a) {
   constexpr int HALF = D / 2;
   constexpr int PQ = HALF / 4;
   constexpr int DQ = D / 4;
-  __shared__ T t_lds[D][TQ + 8];
-  __shared__ T o_lds[D][TQ + 8];
   const int32_t nqt = a.tqp / TQ;
   const int tid = threadIdx.x;
   const int j = tid >> 2, qq = tid & 3;
@@ -157,18 +155,15 @@ __global__ __launch_bounds__(256) void bwd_query_prep_kernel(BackwardArgs a) {
   const T* o = static_cast<const T*>(a.out);
   const T* dout = static_cast<const T*>(a.d_out);
   T* qs = static_cast<T*>(a.qs);
-  T* qst = static_cast<T*>(a.qst);
-  T* dot = static_cast<T*>(a.dot);
   for (int64_t blk = blockIdx.x; blk < (int64_t)a.batch * a.hq * nqt; blk += gridDim.x) {
     const int32_t qt = (int32_t)(blk % nqt);
     const int64_t rest = blk / nqt;
     const int32_t h = (int32_t)(rest % a.hq);
     const int32_t b = (int32_t)(rest / a.hq);
-    __syncthreads();   // the previous block's LDS reads are done
     const int32_t t = qt * TQ + j;
     const bool row_ok = t < a.num_q;
     const int64_t bh = (int64_t)b * a.hq + h;
-    float x1[PQ], x2[PQ], od[DQ];
+    float x1[PQ], x2[PQ];
     float dsum = 0.f;
     if (row_ok) {
       const int64_t src = (((int64_t)b * a.num_q + t) * a.hq + h) * D;
@@ -191,7 +186,7 @@ __global__ __launch_bounds__(256) void bwd_query_prep_kernel(BackwardArgs a) {
         x1[e] = y1 * a.scale_log2;
         x2[e] = y2 * a.scale_log2;
       }
-      float ov[DQ];
+      float od[DQ], ov[DQ];
       load_vec(dout + src + DQ * qq, od, DQ);
       load_vec(o + src + DQ * qq, ov, DQ);
 #pragma unroll
@@ -199,8 +194,6 @@ __global__ __launch_bounds__(256) void bwd_query_prep_kernel(BackwardArgs a) {
     } else {
 #pragma unroll
       for (int e = 0; e < PQ; ++e) x1[e] = x2[e] = 0.f;
-#pragma unroll
-      for (int e = 0; e < DQ; ++e) od[e] = 0.f;
     }
     // the four quarter-rows of a query are four consecutive lanes
     dsum += __shfl_xor(dsum, 1);
@@ -208,26 +201,9 @@ __global__ __launch_bounds__(256) void bwd_query_prep_kernel(BackwardArgs a) {
     T* qrow = qs + (bh * a.tqp + t) * D;
     store_vec(qrow + PQ * qq, x1, PQ);
     store_vec(qrow + HALF + PQ * qq, x2, PQ);
-    const int js = vt_slot(j);
-#pragma unroll
-    for (int e = 0; e < PQ; ++e) {
-      Elem<T>::store(&t_lds[PQ * qq + e][js], x1[e]);
-      Elem<T>::store(&t_lds[HALF + PQ * qq + e][js], x2[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < DQ; ++e) Elem<T>::store(&o_lds[DQ * qq + e][js], od[e]);
     if (qq == 0) {
       a.lse2[bh * a.tqp + t] = row_ok ? a.lse[bh * a.num_q + t] * kLog2e : INFINITY;
       a.di[bh * a.tqp + t] = dsum;
-    }
-    __syncthreads();
-    constexpr int EP = 16 / sizeof(T);
-    for (int idx = tid; idx < D * (TQ / EP); idx += 256) {
-      const int d = idx / (TQ / EP), c = idx % (TQ / EP);
-      *reinterpret_cast<u32x4*>(qst + (bh * D + d) * a.tqp + qt * TQ + c * EP) =
-          *reinterpret_cast<const u32x4*>(&t_lds[d][c * EP]);
-      *reinterpret_cast<u32x4*>(dot + (bh * D + d) * a.tqp + qt * TQ + c * EP) =
-          *reinterpret_cast<const u32x4*>(&o_lds[d][c * EP]);
     }
   }
 }
@@ -247,15 +223,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   constexpr int KS = D / 16;
   constexpr int MT = D / 32;
   constexpr int RCH = D / 8;       // 16-byte chunks per row-major query row
-  constexpr int TCH = BQ / 8;      // 16-byte chunks per d-major row
   constexpr int DMA = BQ * D / 8 / 256;   // 1 KB wave loads per wave per tile (each of the four)
   // query block tiles, two buffers each; 16-byte chunks XOR-swizzled by row
   // (conflict-free operand reads without padding, so whole tiles go global ->
   // LDS directly)
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][BQ * D];    // Q'' rows
   __shared__ __attribute__((aligned(1024))) uint16_t o_lds[2][BQ * D];    // dO rows
-  __shared__ __attribute__((aligned(1024))) uint16_t qt_lds[2][D * BQ];   // Q'' d-major
-  __shared__ __attribute__((aligned(1024))) uint16_t ot_lds[2][D * BQ];   // dO d-major
   __shared__ __attribute__((aligned(1024))) float ld_lds[2][2 * BQ];      // lse2, then Di
 
   const int32_t n_kt = (a.num_k + BK - 1) / BK;
@@ -303,13 +276,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   // tile; the swizzle of a chunk's row depends on (w, lane) only
   const int rrow = wave * (64 / RCH) + lane / RCH;                 // + 4p * 64 / RCH
   const int rchunk = (lane % RCH) ^ chunk_swizzle<RCH>(rrow);
-  const int trow = wave * (64 / TCH) + lane / TCH;                 // + 4p * 64 / TCH
-  const int tchunk = (lane % TCH) ^ chunk_swizzle<TCH>(trow);
   auto load_block = [&](int32_t h, int32_t qb, int bf) {
     const int64_t bh = (int64_t)b * a.hq + h;
     const uint16_t* qsb = static_cast<const uint16_t*>(a.qs) + (bh * a.tqp + (int64_t)qb * BQ) * D;
-    const uint16_t* qtb = static_cast<const uint16_t*>(a.qst) + bh * D * a.tqp + (int64_t)qb * BQ;
-    const uint16_t* otb = static_cast<const uint16_t*>(a.dot) + bh * D * a.tqp + (int64_t)qb * BQ;
     const uint32_t w_off = wave * 1024;
 #pragma unroll
     for (int p = 0; p < DMA; ++p) {
@@ -318,9 +287,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
       const int32_t tr = pf_min(qb * BQ + r, a.num_q - 1);
       dma_to_lds(static_cast<const uint16_t*>(a.d_out) + (((int64_t)b * a.num_q + tr) * a.hq + h) * D + rchunk * 8,
                  lds_address(o_lds[bf]) + w_off + p * 4096);
-      const int dr = trow + 4 * p * (64 / TCH);  // dim row of the d-major tiles
-      dma_to_lds(qtb + (int64_t)dr * a.tqp + tchunk * 8, lds_address(qt_lds[bf]) + w_off + p * 4096);
-      dma_to_lds(otb + (int64_t)dr * a.tqp + tchunk * 8, lds_address(ot_lds[bf]) + w_off + p * 4096);
     }
     // lse2 and Di of the block's 64 queries: 2 x 256 bytes, lanes 0-31 of wave 0
     if (wave == 0 && lane < 32) {
@@ -330,7 +296,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   };
   // operand addresses (elements) inside a tile: row-major row r, logical chunk c
   auto rm_at = [&](int r, int c) { return r * D + ((c ^ chunk_swizzle<RCH>(r)) * 8); };
-  auto dm_at = [&](int r, int c) { return r * BQ + ((c ^ chunk_swizzle<TCH>(r)) * 8); };
 
   f32x16 dk[MT], dv[MT];
 #pragma unroll
@@ -406,8 +371,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     auto dvdk = [&](int j) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&ot_lds[buf][dm_at(32 * mt + col, 2 * j + hf)]);
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qt_lds[buf][dm_at(32 * mt + col, 2 * j + hf)]);
+        // dims 32 mt + m, queries in the k order of P / dS: gathered from the row-major tiles
+        const bf16x8 oa = gather_cols<D>(o_lds[buf], mt, j, lane);
+        const bf16x8 qa = gather_cols<D>(q_lds[buf], mt, j, lane);
         dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pb[j], dv[mt], 0, 0, 0);
         dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb[j], dk[mt], 0, 0, 0);
       }
@@ -431,9 +397,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     dvdk(1);
     softmax_ds(1);
 #pragma unroll
-    for (int i = 0; i < 4 * MT; ++i) {
+    for (int i = 0; i < 4 * MT; ++i) {   // (two transposing reads per operand)
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
     __builtin_amdgcn_sched_barrier(0);

@@ -143,8 +143,6 @@ struct BackwardArgs {
   void* krt;              // [batch][hkv][D][nkp] rotated keys, d-major, keys permuted per 16 (vt_slot)
   void* vr;               // [batch][hkv][nkp][D] values, zero padded
   void* qs;               // [batch][hq][tqp][D] rotated queries * scale * log2(e)
-  void* qst;              // [batch][hq][D][tqp] the same, d-major, queries permuted per 16
-  void* dot;              // [batch][hq][D][tqp] upstream gradient, d-major, queries permuted per 16
   float* lse2;            // [batch][hq][tqp] lse * log2(e); +inf on padding rows
   float* di;              // [batch][hq][tqp] rowsum(d_out * out)
   float* cs_q;            // [num_q][D/2][2] cos/sin of the query positions

@@ -93,4 +93,31 @@ __device__ inline uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane j receives element j % 4 of the 8-byte pieces addressed by lanes
+// 4e + j / 4 of its group, e = 0..3.  So when lane s of a group addresses row
+// r0 + s / 4, columns c0 + 4 (s % 4) .. + 3 of a row-major 16-bit tile, lane j
+// receives column c0 + j of rows r0 .. r0 + 3: a column gather in one read.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ inline s16x4 read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const __attribute__((address_space(3))) void*)p);
+}
+
+// A operand of a 32x32x16 bf16 MFMA taken from a row-major 16-bit tile with D
+// columns (16-byte chunks swizzled by chunk_swizzle<D / 8>): A[m][k] =
+// tile[16 j + k'][32 mt + m], with the k order of an S / S^T accumulator (element
+// e of lane half hf <-> row 16 j + 8 (e / 4) + 4 hf + e % 4).  Two transposing
+// reads: lane group G of 16 covers columns 32 mt + 16 (G % 2) + [0, 16) and
+// rows 16 j + 4 (G / 2) + [0, 4), then the same 8 rows further down.
+template <int D>
+__device__ inline bf16x8 gather_cols(const uint16_t* tile, int mt, int j, int lane) {
+  const int c = 32 * mt + 4 * (lane & 3) + 16 * ((lane >> 4) & 1);   // this lane's 4 columns as a source
+  const int r0 = 16 * j + ((lane & 15) >> 2) + 4 * (lane >> 5), r1 = r0 + 8;
+  const s16x4 lo = read_tr16(&tile[r0 * D + (((c >> 3) ^ chunk_swizzle<D / 8>(r0)) * 8) + (c & 7)]);
+  const s16x4 hi = read_tr16(&tile[r1 * D + (((c >> 3) ^ chunk_swizzle<D / 8>(r1)) * 8) + (c & 7)]);
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+}
+
 }  // namespace ps

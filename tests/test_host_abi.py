@@ -256,7 +256,8 @@ def test_backward_validation_and_workspace(lib):
     B, T, NK = 2, 300, 420
     nkp, tqp = 512, 320
     al = lambda x: (x + 255) // 256 * 256
-    want = (3 * al(B * 2 * nkp * 128 * 2) + 3 * al(B * 16 * tqp * 128 * 2) + 2 * al(B * 16 * tqp * 4)
+    # K' row-major and d-major, V; Q''; lse2 and Di; cos/sin of queries and keys
+    want = (3 * al(B * 2 * nkp * 128 * 2) + al(B * 16 * tqp * 128 * 2) + 2 * al(B * 16 * tqp * 4)
             + al(T * 128 * 4) + al(nkp * 128 * 4))
     need = lib.ps_prefill_backward_workspace_size(ctypes.byref(a), B, T, NK)
     assert need == want
