@@ -512,8 +512,12 @@ def run_backward(ps, torch, reps=5):
     lse = torch.empty((cfg.batch, cfg.hq, cfg.queries), dtype=torch.float32, device="cuda")
     ps.ps_prefill_attn(attn, cfg.window, cfg.prefix, cfg.kv_start, q, k, v, o, lse=lse)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(ps.ps_prefill_backward_workspace_size(attn, cfg.batch, cfg.queries, cfg.nk),
-                     dtype=torch.uint8, device="cuda")
+    # with the dS room the dk/dv pass keeps its dS tiles and dq forms one product instead of three
+    extra = ps.ps_prefill_backward_ds_workspace_size(attn, cfg.window, cfg.prefix, cfg.kv_start, cfg.batch,
+                                                     cfg.queries, cfg.nk)
+    keep_ds = 0 < extra <= torch.cuda.mem_get_info()[0] // 4
+    ws = torch.empty(ps.ps_prefill_backward_workspace_size(attn, cfg.batch, cfg.queries, cfg.nk)
+                     + (extra if keep_ds else 0), dtype=torch.uint8, device="cuda")
 
     def call(n_):
         for _ in range(n_):
@@ -526,7 +530,7 @@ def run_backward(ps, torch, reps=5):
     flops = 10.0 * cfg.dim * pairs * cfg.batch * cfg.hq
     res = {"workload": cfg.name + "-backward", "ms": t * 1e3, "tflops": flops / t / 1e12,
            "useful_tflop": flops / 1e12, "mfma_frac": flops / t / 1e12 / BF16_PEAK_TFLOPS,
-           "executed_products": 7}
+           "executed_products": 5 if keep_ds else 7, "kept_ds": keep_ds, "ds_workspace_bytes": extra if keep_ds else 0}
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return res

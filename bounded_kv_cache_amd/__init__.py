@@ -20,7 +20,7 @@ from ._lib import PS_BF16, PS_F32, PS_PE_CONTINUE, PS_PE_RESET, PS_PE_RESET_RECO
 
 __all__ = ["AttnSpec", "CacheSpec", "PSError", "ps_kv_append", "ps_decode_attn", "ps_prefill_attn",
            "ps_chunk_prefill_attn", "ps_chunk_prefill_workspace_size", "ps_prefill_attn_backward",
-           "ps_prefill_backward_workspace_size", "ps_heavy_decode_step", "ps_heavy_workspace_size", "HeavyState",
+           "ps_prefill_backward_workspace_size", "ps_prefill_backward_ds_workspace_size", "ps_heavy_decode_step", "ps_heavy_workspace_size", "HeavyState",
            "ps_prefill_plan", "ps_decode_workspace_size", "ps_decode_num_splits", "ps_prefill_workspace_size",
            "ps_prefill_tile_shape", "ps_read_probe", "ps_decode_step", "ps_decode_step_noalloc", "ps_abi_version", "cache_shapes", "PS_BF16", "PS_F32", "PS_PE_CONTINUE",
            "PS_PE_RESET", "PS_PE_RESET_RECOMPUTE"]
@@ -323,11 +323,23 @@ def ps_prefill_backward_workspace_size(attn: AttnSpec, batch: int, num_queries: 
     return _lib.load().ps_prefill_backward_workspace_size(ctypes.byref(a), batch, num_queries, num_keys)
 
 
+def ps_prefill_backward_ds_workspace_size(attn: AttnSpec, window: int, prefix_len: int, kv_start: int, batch: int,
+                                          num_queries: int, num_keys: int) -> int:
+    a = attn.c()
+    return _lib.load().ps_prefill_backward_ds_workspace_size(ctypes.byref(a), window, prefix_len, kv_start, batch,
+                                                             num_queries, num_keys)
+
+
 def ps_prefill_attn_backward(attn: AttnSpec, window: int, prefix_len: int, kv_start: int, q: torch.Tensor,
                              k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, d_out: torch.Tensor,
                              lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, *,
-                             workspace: Optional[torch.Tensor] = None, stream=None):
-    """Gradients of ps_prefill_attn: writes dq [B, T, Hq, D], dk and dv [B, Nk, Hkv, D]."""
+                             workspace: Optional[torch.Tensor] = None, keep_ds: Optional[bool] = None,
+                             stream=None):
+    """Gradients of ps_prefill_attn: writes dq [B, T, Hq, D], dk and dv [B, Nk, Hkv, D].
+
+    Without a workspace one is allocated: with the extra dS room (the dq pass then
+    reads the dk/dv pass's dS tiles) when keep_ds is True, or when keep_ds is None and
+    that room is at most a quarter of the free device memory."""
     dt = attn.torch_dtype
     batch, num_q = q.shape[0], q.shape[1]
     num_k = k.shape[1]
@@ -342,7 +354,10 @@ def ps_prefill_attn_backward(attn: AttnSpec, window: int, prefix_len: int, kv_st
     _need(dv, "dv", dt, k.numel())
     need = ps_prefill_backward_workspace_size(attn, batch, num_q, num_k)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        extra = ps_prefill_backward_ds_workspace_size(attn, window, prefix_len, kv_start, batch, num_q, num_k)
+        if keep_ds is None:
+            keep_ds = extra <= torch.cuda.mem_get_info(q.device)[0] // 4
+        workspace = torch.empty(max(need + (extra if keep_ds else 0), 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     a = attn.c()
     _lib.check(_lib.load().ps_prefill_attn_backward(ctypes.byref(a), window, prefix_len, kv_start, _ptr(q), _ptr(k),

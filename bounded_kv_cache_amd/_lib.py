@@ -49,6 +49,7 @@ SIGNATURES = {
     "ps_prefill_attn_backward": (_i32, [_pA, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
                                         _vp, _vp, _vp, _sz, _vp]),
     "ps_prefill_backward_workspace_size": (_sz, [_pA, _i32, _i32, _i32]),
+    "ps_prefill_backward_ds_workspace_size": (_sz, [_pA, _i32, _i32, _i64, _i32, _i32, _i32]),
     "ps_heavy_decode_step": (_i32, [_pA, _pC, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
                                     _i32, _vp, _sz, _vp]),
     "ps_heavy_workspace_size": (_sz, [_pA, _pC, _i32, _i32]),

@@ -274,6 +274,28 @@ BwdLayout bwd_layout(const ps_attn_desc* a, int32_t batch, int32_t num_q, int32_
   return l;
 }
 
+// dS^T tiles the bf16 backward can keep for its dq pass (one 128-key x
+// 64-query bf16 tile per visited pair, ds_slots per 64-query block): bytes and
+// slots; zero for fp32 or an empty call.
+struct DsLayout {
+  size_t bytes;
+  int32_t slots;
+};
+
+DsLayout ds_layout(const ps_attn_desc* a, int32_t window, int32_t prefix_len, int64_t kv_start, int32_t batch,
+                   int32_t num_q, int32_t num_k) {
+  DsLayout d{0, 0};
+  if (a->dtype != PS_BF16 || batch <= 0 || num_q <= 0 || num_k <= 0) return d;
+  const ps::PrefillGeom g{num_q, num_k, prefix_len, window, kv_start, 64, 128};
+  const int32_t nqb = (num_q + 63) / 64;
+  for (int32_t qb = 0; qb < nqb; ++qb) {
+    const int32_t n = ps::pf_walk(g, qb).n_cand;
+    d.slots = n > d.slots ? n : d.slots;
+  }
+  d.bytes = (size_t)batch * a->num_q_heads * nqb * d.slots * (128 * 64 * 2);
+  return d;
+}
+
 }  // namespace
 
 extern "C" {
@@ -700,6 +722,15 @@ size_t ps_prefill_backward_workspace_size(const ps_attn_desc* attn, int32_t batc
   return bwd_layout(attn, batch, num_queries, num_keys).total;
 }
 
+size_t ps_prefill_backward_ds_workspace_size(const ps_attn_desc* attn, int32_t window, int32_t prefix_len,
+                                             int64_t kv_start, int32_t batch, int32_t num_queries,
+                                             int32_t num_keys) {
+  if (check_attn(attn) != PS_OK ||
+      check_prefill_geom(window, prefix_len, kv_start, batch, num_queries, num_keys) != PS_OK)
+    return 0;
+  return ds_layout(attn, window, prefix_len, kv_start, batch, num_queries, num_keys).bytes;
+}
+
 ps_status ps_prefill_attn_backward(const ps_attn_desc* attn, int32_t window, int32_t prefix_len, int64_t kv_start,
                                    const void* q, const void* k, const void* v, const void* out, const void* d_out,
                                    const float* lse, int32_t batch, int32_t num_queries, int32_t num_keys, void* dq,
@@ -723,6 +754,9 @@ ps_status ps_prefill_attn_backward(const ps_attn_desc* attn, int32_t window, int
   const BwdLayout l = bwd_layout(attn, batch, num_queries, num_keys);
   if (!workspace || workspace_bytes < l.total)
     return fail(PS_WORKSPACE_TOO_SMALL, "backward needs %zu workspace bytes, got %zu", l.total, workspace_bytes);
+  // with room for them after the base layout, the dk/dv pass keeps its dS tiles for dq
+  const DsLayout dl = ds_layout(attn, window, prefix_len, kv_start, batch, num_queries, num_keys);
+  const bool keep_ds = dl.bytes > 0 && workspace_bytes - l.total >= dl.bytes;
   char* w = static_cast<char*>(workspace);
   ps::BackwardArgs a{};
   a.dtype = attn->dtype;
@@ -755,6 +789,8 @@ ps_status ps_prefill_attn_backward(const ps_attn_desc* attn, int32_t window, int
   a.di = reinterpret_cast<float*>(w + l.di);
   a.cs_q = reinterpret_cast<float*>(w + l.cs_q);
   a.cs_k = reinterpret_cast<float*>(w + l.cs_k);
+  a.ds = keep_ds ? w + l.total : nullptr;
+  a.ds_slots = keep_ds ? dl.slots : 0;
   a.scale = attn->softmax_scale;
   a.scale_log2 = attn->softmax_scale * 1.4426950408889634f;
   a.rope = make_rope(attn);

@@ -213,10 +213,26 @@ __global__ __launch_bounds__(256) void bwd_query_prep_kernel(BackwardArgs a) {
 //   D[m][n]: lane (n + 32*((m/4)%2)) register 4*(m/8) + m%4
 // so register r of a D tile holds row m = 8*(r/4) + 4*hf + r%4 of column col.
 
+// dS^T tiles the dk/dv kernel can keep for the dq kernel: one [128 keys][64
+// queries] bf16 tile per visited (64-query block qb, 128-key tile kt) pair, at
+// tile index ((b * hq + h) * (tqp / 64) + qb) * ds_slots + slot, where slot is
+// the position of kt in the block's walk (prefix tiles, then band tiles; the
+// walk holds exactly the tiles with a visible pair).  A row holds one key's 64
+// queries in the order of the P / dS registers: position 16 j + 8 hf + e <->
+// query 16 j + 8 (e / 4) + 4 hf + e % 4 (vt_slot).
+constexpr int kDsKeys = 128, kDsQueries = 64;
+__device__ inline int32_t ds_slot(const PrefillGeom& g64x128, int32_t qb, int32_t kt) {
+  const TileRange tr = pf_tile_range(g64x128, qb);
+  return kt < tr.n_prefix ? kt : tr.n_prefix + (kt - tr.band_lo);
+}
+__device__ inline int64_t ds_tile(const BackwardArgs& a, int32_t b, int32_t h, int32_t qb, int32_t slot) {
+  return ((((int64_t)b * a.hq + h) * (a.tqp / kDsQueries) + qb) * a.ds_slots + slot) * (kDsKeys * kDsQueries);
+}
+
 // ---------------------------------------------------------------------------
-// 3. dk / dv (bf16 MFMA)
+// 3. dk / dv (bf16 MFMA); kKeepDs: also store each block's dS^T tile
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool kKeepDs>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   constexpr int BK = 128;          // keys per workgroup, 32 per wave
   constexpr int BQ = 64;           // queries per step
@@ -230,6 +246,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][BQ * D];    // Q'' rows
   __shared__ __attribute__((aligned(1024))) uint16_t o_lds[2][BQ * D];    // dO rows
   __shared__ __attribute__((aligned(1024))) float ld_lds[2][2 * BQ];      // lse2, then Di
+  __shared__ __attribute__((aligned(1024))) uint16_t st_lds[kKeepDs ? 4 * 32 * kDsQueries : 1];   // dS^T staging, per wave
 
   const int32_t n_kt = (a.num_k + BK - 1) / BK;
   const int64_t pairs = (int64_t)a.batch * a.hkv;
@@ -314,6 +331,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   __syncthreads();
   int buf = 0;
+  // dS^T of a block goes through the wave's LDS staging rows (32 keys x 128
+  // bytes, 16-byte chunks XOR-swizzled by row % 8) so that each global store
+  // writes 8 whole rows (1 KB); the stores of a block are issued in the middle
+  // of the next iteration (measured: at its start, ahead of or behind the next
+  // block's loads, they cost 3-10 % more)
+  int64_t keep_at = -1;
+  uint16_t* stg = st_lds + wave * 32 * kDsQueries;
+  auto stage = [&](int r, int c) { return r * kDsQueries + ((c ^ (r & 7)) * 8); };
+  uint16_t* ds = static_cast<uint16_t*>(a.ds) + (32 * wave + lane / 8) * kDsQueries + (lane % 8) * 8;
+  bf16x8 kept[4];
+  auto read_kept = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kept[i] = *reinterpret_cast<const bf16x8*>(&stg[stage(8 * i + lane / 8, lane % 8)]);
+  };
+  auto store_kept = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8*>(ds + keep_at + 8 * i * kDsQueries) = kept[i];
+  };
   while (it < n_it) {
     const int32_t h = kvh * a.group + it / n_qb;
     const int32_t qb = qb_lo + it % n_qb;
@@ -321,8 +356,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     int32_t nx = it + 1;
     int nkind = 0;
     while (nx < n_it && (nkind = pf_classify(cg, qb_lo + nx % n_qb, kt)) == 0) ++nx;
+    if (kKeepDs && keep_at >= 0) read_kept();
     if (nx < n_it) load_block(kvh * a.group + nx / n_qb, qb_lo + nx % n_qb, buf ^ 1);   // its buffer was read last iteration
-    (void)h;
 
     // S = Q'' K'^T and dP = dO V^T (two 32-query M-tiles), then
     // dV^T += dO^T P and dK^T += Q''^T dS over the block's 64 queries.  One
@@ -382,6 +417,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     products(0);
     if (partial) mask(0);
     __builtin_amdgcn_sched_barrier(0);
+    if (kKeepDs && keep_at >= 0) store_kept();   // the previous block's dS^T
+    __builtin_amdgcn_sched_barrier(0);
     products(1);
     softmax_ds(0);
 #pragma unroll
@@ -405,11 +442,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     dvdk(2);
     dvdk(3);
+    if (kKeepDs) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(&stg[stage(col, 2 * j + hf)]) = sb[j];
+      keep_at = ds_tile(a, b, h, qb, ds_slot(cg, qb, kt));
+    }
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // the next block has landed (this wave's part)
     __syncthreads();
     buf ^= 1;
     it = nx;
     kind = nkind;
+  }
+  if (kKeepDs && keep_at >= 0) {
+    read_kept();
+    store_kept();
   }
 
   // ---- epilogue: register r of tile mt <-> dim 32*mt + 8*(r/4) + 4*hf + r%4 of key kw;
@@ -710,6 +756,161 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 4b. dq from the kept dS^T tiles (bf16 MFMA): dQ''^T += K'^T dS^T, one product
+//     instead of three.  One workgroup per (batch, query head, 128-query tile),
+//     walking the 64-key tiles of the forward's schedule.  Per tile the two
+//     64-query halves' dS^T rows (keys of the tile, from the dk/dv kernel's
+//     128-key tile) and the d-major K' tile go global -> LDS directly; a wave's
+//     B operand (32 queries, 8 keys per lane) is gathered from the dS^T rows by
+//     transposing LDS reads.  A half whose 64x128 block held no visible pair
+//     has no tile: its waves skip the tile (its dS is zero).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(BackwardArgs a) {
+  constexpr int BM = 128, BN = 64;
+  constexpr int MT = D / 32;
+  constexpr int TCH = BN / 8;      // 16-byte chunks per d-major K' row
+  constexpr int SCH = BM / 8;      // 16-byte chunks per dS^T row of the tile (two 64-query halves)
+  __shared__ __attribute__((aligned(1024))) uint16_t s_lds[2][BN * BM];   // dS^T: [64 keys][128 queries]
+  __shared__ __attribute__((aligned(1024))) uint16_t t_lds[2][D * BN];    // K' d-major: [D][64 keys]
+
+  PrefillGeom geo{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, BM, BN};
+  PrefillGeom g64{a.num_q, a.num_k, a.prefix_len, a.window, a.kv_start, kDsQueries, kDsKeys};
+  const int32_t n_qt = pf_num_qtiles(geo);
+  // items ordered (batch, KV head, q-tile, head-in-group), each XCD a contiguous run
+  const int64_t total = (int64_t)a.batch * a.hq * n_qt;
+  const int64_t per = (total + 7) / 8;
+  const int64_t lin = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (lin >= total) return;
+  const int32_t hg = (int32_t)(lin % a.group);
+  int64_t rest = lin / a.group;
+  const int32_t qt = (int32_t)(rest % n_qt);
+  rest /= n_qt;
+  const int32_t kvh = (int32_t)(rest % a.hkv);
+  const int32_t b = (int32_t)(rest / a.hkv);
+  const int32_t hq = kvh * a.group + hg;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int64_t bkv = (int64_t)b * a.hkv + kvh;
+  const uint16_t* ktr = static_cast<const uint16_t*>(a.krt) + bkv * D * a.nkp;
+  const uint16_t* dsb = static_cast<const uint16_t*>(a.ds);
+
+  const TileRange tr = pf_tile_range(geo, qt);
+  const int32_t n_cand = tr.n_prefix + (tr.band_hi >= tr.band_lo ? tr.band_hi - tr.band_lo + 1 : 0);
+  auto cand_tile = [&](int32_t ci) { return ci < tr.n_prefix ? ci : tr.band_lo + (ci - tr.n_prefix); };
+  // the kept tile of half qh (query block 2 qt + qh) for 64-key tile kt, or -1
+  auto half_tile = [&](int32_t kt, int qh) -> int64_t {
+    const int32_t qb = 2 * qt + qh;
+    if (qb * kDsQueries >= a.num_q || pf_classify(g64, qb, kt >> 1) == 0) return -1;
+    return ds_tile(a, b, hq, qb, ds_slot(g64, qb, kt >> 1)) + (int64_t)(kt & 1) * BN * kDsQueries;
+  };
+
+  // tile -> LDS buffer: wave load p of wave w fills chunks (4p + w) * 64 + lane;
+  // the swizzle of a chunk's row depends on (w, lane) only
+  const int srow = wave * (64 / SCH) + lane / SCH;                 // + 4p * 64 / SCH: key row
+  const int schunk = (lane % SCH) ^ chunk_swizzle<SCH>(srow);      // logical chunk: half, 8 queries
+  const int trow = wave * (64 / TCH) + lane / TCH;
+  const int tchunk = (lane % TCH) ^ chunk_swizzle<TCH>(trow);
+  auto load_tile = [&](int32_t kt, int b_, int64_t t0, int64_t t1) {
+    // a missing half reads tile 0 of the region (in bounds; its waves skip it)
+    const int64_t src = (schunk < SCH / 2 ? t0 : t1);
+    const int64_t base = src >= 0 ? src : 0;
+#pragma unroll
+    for (int p = 0; p < BN * BM / 8 / 256; ++p)
+      dma_to_lds(dsb + base + (int64_t)(srow + 4 * p * (64 / SCH)) * kDsQueries + (schunk % (SCH / 2)) * 8,
+                 lds_address(s_lds[b_]) + wave * 1024 + p * 4096);
+#pragma unroll
+    for (int p = 0; p < D * BN / 8 / 256; ++p)
+      dma_to_lds(ktr + (int64_t)(trow + 4 * p * (64 / TCH)) * a.nkp + (int64_t)kt * BN + tchunk * 8,
+                 lds_address(t_lds[b_]) + wave * 1024 + p * 4096);
+  };
+  auto dm_at = [&](int r, int c) { return r * BN + ((c ^ chunk_swizzle<TCH>(r)) * 8); };
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+
+  int32_t ci = 0;
+  int64_t h0 = -1, h1 = -1;
+  if (n_cand > 0) {
+    h0 = half_tile(cand_tile(0), 0);
+    h1 = half_tile(cand_tile(0), 1);
+    load_tile(cand_tile(0), 0, h0, h1);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  __syncthreads();
+  int buf = 0;
+  const int qh = wave >> 1;   // this wave's half: queries 32 wave .. + 31 of the tile
+  while (ci < n_cand) {
+    const bool mine = (qh == 0 ? h0 : h1) >= 0;
+    int64_t n0 = -1, n1 = -1;
+    if (ci + 1 < n_cand) {
+      n0 = half_tile(cand_tile(ci + 1), 0);
+      n1 = half_tile(cand_tile(ci + 1), 1);
+      load_tile(cand_tile(ci + 1), buf ^ 1, n0, n1);   // its buffer was read last step
+    }
+    if (mine) {
+      // k-step j covers keys 16 j + 8 (e / 4) + 4 hf + e % 4: the d-major K' rows
+      // (keys permuted per 16) and the gathered dS^T columns agree on that order
+      const uint16_t* tt = t_lds[buf];
+      const uint16_t* st = s_lds[buf];
+      bf16x8 ta[MT], sbv = gather_cols<BM>(st, wave, 0, lane);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) ta[mt] = *reinterpret_cast<const bf16x8*>(&tt[dm_at(32 * mt + col, hf)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 tn[MT], sn = sbv;
+        if (j + 1 < 4) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            tn[mt] = *reinterpret_cast<const bf16x8*>(&tt[dm_at(32 * mt + col, 2 * (j + 1) + hf)]);
+          sn = gather_cols<BM>(st, wave, j + 1, lane);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[mt], sbv, acc[mt], 0, 0, 0);
+        if (j + 1 < 4) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) ta[mt] = tn[mt];
+          sbv = sn;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // this wave's part of the next tiles has landed
+    __syncthreads();
+    buf ^= 1;
+    h0 = n0;
+    h1 = n1;
+    ++ci;
+  }
+
+  // dQ' = scale * acc, rotated back by -position; column col of the accumulator
+  // is tile column 32 wave + col, i.e. query vt_slot(32 wave + col) of the tile
+  const int32_t t = qt * BM + vt_slot(32 * wave + col);
+  if (t >= a.num_q) return;
+  uint16_t* dqrow = static_cast<uint16_t*>(a.dq) + (((int64_t)b * a.num_q + t) * a.hq + hq) * D;
+  const float* cs = a.cs_q + (int64_t)t * D;
+#pragma unroll
+  for (int mt = 0; mt < MT / 2; ++mt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * mt + 8 * r4 + 4 * hf;
+      float g1[4], g2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float c = cs[2 * (d + e)], sn = cs[2 * (d + e) + 1];
+        const float x1 = acc[mt][4 * r4 + e] * a.scale, x2 = acc[mt + MT / 2][4 * r4 + e] * a.scale;
+        g1[e] = x1 * c + x2 * sn;
+        g2[e] = x2 * c - x1 * sn;
+      }
+      *reinterpret_cast<uint2*>(dqrow + d) = uint2{pack_bf16x2(g1[0], g1[1]), pack_bf16x2(g1[2], g1[3])};
+      *reinterpret_cast<uint2*>(dqrow + d + D / 2) = uint2{pack_bf16x2(g2[0], g2[1]), pack_bf16x2(g2[2], g2[3])};
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 debug path: one thread per query row (dq) / key row (dk, dv)
 // ---------------------------------------------------------------------------
 template <int D>
@@ -812,10 +1013,17 @@ hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (sizeof(T) == 2) {
     const int64_t kv_items = (int64_t)a.batch * a.hkv * ((a.num_k + 127) / 128);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((uint32_t)kv_items), dim3(256), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t q_items = (int64_t)a.batch * a.hq * ((a.num_q + 127) / 128);
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((uint32_t)(((q_items + 7) / 8) * 8)), dim3(256), 0, stream, a);
+    const dim3 q_grid((uint32_t)(((q_items + 7) / 8) * 8));
+    if (a.ds) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((uint32_t)kv_items), dim3(256), 0, stream, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL((bwd_dq_ds_kernel<D>), q_grid, dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((uint32_t)kv_items), dim3(256), 0, stream, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL((bwd_dq_kernel<D>), q_grid, dim3(256), 0, stream, a);
+    }
   } else {
     const int64_t kv_rows = (int64_t)a.batch * a.hkv * a.num_k;
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), dim3((uint32_t)((kv_rows + 63) / 64)), dim3(64), 0, stream, a);

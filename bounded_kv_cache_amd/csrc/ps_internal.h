@@ -147,6 +147,9 @@ struct BackwardArgs {
   float* di;              // [batch][hq][tqp] rowsum(d_out * out)
   float* cs_q;            // [num_q][D/2][2] cos/sin of the query positions
   float* cs_k;            // [nkp][D/2][2] cos/sin of the key positions
+  void* ds;               // optional dS^T tiles kept by the dk/dv kernel for the dq kernel (null: dq recomputes
+                          // S and dP): [batch][hq][tqp/64][ds_slots][128 keys][64 queries]
+  int32_t ds_slots;       // tiles per 64-query block: the longest walk of 128-key tiles of a block
   float scale;            // softmax scale
   float scale_log2;       // scale * log2(e)
   RopeFreq rope;

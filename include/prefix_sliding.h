@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 8
+#define PS_ABI_VERSION 9
 
 typedef enum {
   PS_OK = 0,
@@ -318,7 +318,13 @@ size_t ps_heavy_workspace_size(const ps_attn_desc* attn, const ps_cache_desc* ca
  *   lse  : the forward's LSE [batch][Hq][num_queries] (required).
  *   dq   : [batch][num_queries][Hq][D]; dk, dv : [batch][num_keys][Hkv][D];
  *          dtype of attn; fully overwritten (keys no query sees get zeros).
- *   workspace : >= ps_prefill_backward_workspace_size(...) bytes.
+ *   workspace : >= ps_prefill_backward_workspace_size(...) bytes.  In bf16,
+ *          when it also holds ps_prefill_backward_ds_workspace_size(...)
+ *          more bytes, the dk/dv pass keeps its dS tiles there and the dq
+ *          pass reads them instead of forming S and dP again (same
+ *          arithmetic, one product instead of three); otherwise dq
+ *          recomputes them.  The two paths may differ in the last bit of dq
+ *          (fp32 sums in another order); dk and dv are the same.
  * Deterministic: every output row has exactly one writer (no atomics). */
 ps_status ps_prefill_attn_backward(const ps_attn_desc* attn, int32_t window, int32_t prefix_len,
                                    int64_t kv_start, const void* q, const void* k, const void* v,
@@ -329,6 +335,17 @@ ps_status ps_prefill_attn_backward(const ps_attn_desc* attn, int32_t window, int
 
 size_t ps_prefill_backward_workspace_size(const ps_attn_desc* attn, int32_t batch,
                                           int32_t num_queries, int32_t num_keys);
+
+/* Extra workspace bytes (beyond ps_prefill_backward_workspace_size's) with
+ * which the bf16 backward keeps its dS tiles for the dq pass: one 128-key x
+ * 64-query bf16 tile (16 KB) per query head, 64-query block and 128-key tile
+ * of the block's walk, i.e. batch * Hq * ceil(num_queries / 64) * slots *
+ * 16384 bytes, slots the longest walk (the pinned-key tiles, then the window
+ * band: about (W + 64) / 128 + 2 tiles when the prefix fits one tile).  0 for
+ * fp32 or invalid arguments (the dq pass then recomputes). */
+size_t ps_prefill_backward_ds_workspace_size(const ps_attn_desc* attn, int32_t window,
+                                             int32_t prefix_len, int64_t kv_start, int32_t batch,
+                                             int32_t num_queries, int32_t num_keys);
 
 /* ps_chunk_prefill_attn -- a chunk of new tokens continues cached traces:
  * attention of the chunk's queries over each sequence's ring plus the chunk

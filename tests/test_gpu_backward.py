@@ -64,7 +64,7 @@ def _structural_zero_rows(do, L, W, ks, nk):
     return ~live_q, vis, live_q
 
 
-def _run(ps, dtype, hq, hkv, d, L, W, ks, T, chunk, batch=1, seed=0, loss_rows=None):
+def _run(ps, dtype, hq, hkv, d, L, W, ks, T, chunk, batch=1, seed=0, loss_rows=None, keep_ds=None):
     dt_name = "bf16" if dtype == "bf16" else "f32"
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16 if dtype == "bf16" else ps.PS_F32, 10000.0, 1 / math.sqrt(d))
@@ -91,7 +91,8 @@ def _run(ps, dtype, hq, hkv, d, L, W, ks, T, chunk, batch=1, seed=0, loss_rows=N
     dv = torch.full((batch, nk, hkv, d), float("nan"), dtype=tdt, device="cuda")
     ps.ps_prefill_attn_backward(attn, W, L, ks, to_dev(q, tdt), to_dev(k, tdt), to_dev(v, tdt),
                                 to_dev(np.stack(outs), tdt), to_dev(do, tdt),
-                                torch.from_numpy(np.ascontiguousarray(np.stack(lses))).cuda(), dq, dk, dv)
+                                torch.from_numpy(np.ascontiguousarray(np.stack(lses))).cuda(), dq, dk, dv,
+                                keep_ds=keep_ds)
     torch.cuda.synchronize()
     got = [x.float().cpu().numpy() for x in (dq, dk, dv)]
     worst = {}
@@ -127,12 +128,44 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("keep_ds", [True, False], ids=["kept_ds", "recomputed_ds"])
 @pytest.mark.parametrize("case", range(len(CASES)))
-def test_backward_bf16_matches_oracle(ps, case):
+def test_backward_bf16_matches_oracle(ps, case, keep_ds):
+    # kept_ds: the dk/dv pass stores its dS tiles and the dq pass reads them;
+    # recomputed_ds: the dq pass forms S and dP again (workspace without the dS room)
     hq, hkv, d, L, W, ks, T, chunk, batch = CASES[case]
-    print(f"backward bf16 case {case}: Hq={hq} Hkv={hkv} D={d} L={L} W={W} kv_start={ks} T={T} chunk={chunk}",
-          flush=True)
-    _run(ps, "bf16", hq, hkv, d, L, W, ks, T, chunk, batch, seed=case)
+    print(f"backward bf16 case {case} keep_ds={keep_ds}: Hq={hq} Hkv={hkv} D={d} L={L} W={W} kv_start={ks} "
+          f"T={T} chunk={chunk}", flush=True)
+    _run(ps, "bf16", hq, hkv, d, L, W, ks, T, chunk, batch, seed=case, keep_ds=keep_ds)
+
+
+@pytest.mark.parametrize("case", [0, 3, 4])
+def test_backward_kept_ds_agrees_with_recomputed(ps, case):
+    # the two dq paths share the dk/dv pass: dk and dv are bitwise equal; dq may
+    # differ where an fp32 sum in another order rounds a dS element differently
+    hq, hkv, d, L, W, ks, T, chunk, batch = CASES[case]
+    print(f"backward kept vs recomputed dS, case {case}", flush=True)
+    attn = ps.AttnSpec(hq, hkv, d, ps.PS_BF16, 10000.0, 1 / math.sqrt(d))
+    nk = L + chunk
+    g = torch.Generator(device="cuda").manual_seed(40 + case)
+    q = torch.randn((batch, T, hq, d), generator=g, device="cuda").bfloat16()
+    k = torch.randn((batch, nk, hkv, d), generator=g, device="cuda").bfloat16()
+    v = torch.randn((batch, nk, hkv, d), generator=g, device="cuda").bfloat16()
+    do = torch.randn_like(q)
+    out = torch.empty_like(q)
+    lse = torch.empty((batch, hq, T), dtype=torch.float32, device="cuda")
+    ps.ps_prefill_attn(attn, W, L, ks, q, k, v, out, lse=lse)
+    res = []
+    for keep in (True, False):
+        grads = [torch.empty_like(x) for x in (q, k, v)]
+        ps.ps_prefill_attn_backward(attn, W, L, ks, q, k, v, out, do, lse, *grads, keep_ds=keep)
+        res.append([x.float() for x in grads])
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][1], res[1][1]) and torch.equal(res[0][2], res[1][2])
+    dq_k, dq_r = res[0][0], res[1][0]
+    diff = float((dq_k - dq_r).norm() / dq_r.norm())
+    print("dq relative (Frobenius) difference between the paths:", diff, flush=True)
+    assert diff <= 2e-3, diff
 
 
 @pytest.mark.parametrize("case", [0, 1, 4])
