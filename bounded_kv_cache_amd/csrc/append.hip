@@ -7,12 +7,15 @@
 // "位置编码：Reset PE 还是 Continue PE？" (Continue PE: the rotated key is
 // cached and never rotated again).
 #include "ps_internal.h"
+#include "ps_tiles.h"
 
 namespace ps {
 namespace {
 
 // calls appending at least this many tokens per sequence take the block path
 constexpr int32_t kBulkAppendTokens = 16;
+// LDS bytes of the block path's V stage: the 8 tokens' V rows of every KV head
+constexpr size_t kAppendStage = 8192;
 
 // One wavefront per (sequence, token).  Each lane rotates rotate-half pairs
 // (i, i + D/2) of one KV head; V is copied into the 8-slot d-major blocks.
@@ -117,33 +120,71 @@ __global__ __launch_bounds__(64) void append_block_kernel(AppendArgs a) {
   T* __restrict__ kc = static_cast<T*>(a.k_cache);
   T* __restrict__ vc = static_cast<T*>(a.v_cache);
   const int64_t tok0 = (int64_t)s * a.tokens_per_seq - start;   // token row of position j: tok0 + j
-  // K: rotate each kept token at its position (cos/sin shared by the KV heads)
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  // K: rotate each kept token at its position (cos/sin shared by the KV heads);
+  // a lane takes 16-byte runs of both halves of a row: E rotation pairs
+  constexpr int E = 16 / sizeof(T);
+  const int32_t runs = half / E;   // runs per half row
+  for (int32_t task = lane; task < 8 * g.hkv * runs; task += 64) {
+    const int k = task / (g.hkv * runs);
+    const int32_t h = (task / runs) % g.hkv, i0 = (task % runs) * E;
     if (pos[k] < 0) continue;
     const int32_t slot = 8 * kb + k;
-    for (int32_t i = lane; i < half; i += 64) {
+    const int64_t base = region_offset(g, a.block_table, s, h, slot);
+    if (base < 0) continue;  // page outside the pool: dropped
+    const T* row = kn + ((tok0 + pos[k]) * g.hkv + h) * D;
+    float x1[E], x2[E], y1[E], y2[E];
+    load_vec(row + i0, x1, E);
+    load_vec(row + half + i0, x2, E);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
       float c = 1.f, sn = 0.f;
       if (a.rope.enabled && a.rope_cs) {   // the caller's table row of this token
-        const float2 w = reinterpret_cast<const float2*>(a.rope_cs)[(tok0 + pos[k]) * half + i];
+        const float2 w = reinterpret_cast<const float2*>(a.rope_cs)[(tok0 + pos[k]) * half + i0 + e];
         c = w.x;
         sn = w.y;
       } else if (a.rope.enabled) {
-        rope_cos_sin(pos[k], a.rope.inv_freq[i], c, sn);
+        rope_cos_sin(pos[k], a.rope.inv_freq[i0 + e], c, sn);
       }
-      for (int32_t h = 0; h < g.hkv; ++h) {
-        const int64_t base = region_offset(g, a.block_table, s, h, slot);
-        if (base < 0) continue;  // page outside the pool: dropped
-        const T* row = kn + ((tok0 + pos[k]) * g.hkv + h) * D;
-        const float x1 = Elem<T>::load(row + i), x2 = Elem<T>::load(row + i + half);
-        float y1, y2;
-        rotate_pair(x1, x2, c, sn, y1, y2);
-        Elem<T>::store(kc + base + k_in_region(slot, i, D), y1);
-        Elem<T>::store(kc + base + k_in_region(slot, i + half, D), y2);
+      rotate_pair(x1[e], x2[e], c, sn, y1[e], y2[e]);
+    }
+    store_vec(kc + base + k_in_region(slot, i0, D), y1, E);
+    store_vec(kc + base + k_in_region(slot, half + i0, D), y2, E);
+  }
+  // V: per (KV head, dim) the block's 8 slots are 8 contiguous elements.  With
+  // all 8 slots written and the rows fitting the LDS stage, the 8 tokens' rows
+  // come in with 16-byte loads and each (head, dim) column is read back from
+  // LDS; otherwise column by column from global memory.
+  __shared__ T vstage[kAppendStage / sizeof(T)];
+  if (written == 8 && (size_t)8 * g.hkv * D * sizeof(T) <= kAppendStage) {
+    const int32_t row_runs = g.hkv * D / E;
+    for (int32_t task = lane; task < 8 * row_runs; task += 64) {
+      const int k = task / row_runs, r = task % row_runs;
+      *reinterpret_cast<u32x4*>(&vstage[(k * row_runs + r) * E]) =
+          *reinterpret_cast<const u32x4*>(vn + (tok0 + pos[k]) * g.hkv * D + r * E);
+    }
+    // (one wave: its LDS accesses complete in program order)
+    for (int32_t hd = lane; hd < g.hkv * D; hd += 64) {
+      const int32_t h = hd / D, d = hd % D;
+      const int64_t base = region_offset(g, a.block_table, s, h, 8 * kb);
+      if (base < 0) continue;
+      T* dst = vc + base + v_in_region(8 * kb, d, D);   // slot 8 kb + k at dst[k]
+      T val[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) val[k] = vstage[k * g.hkv * D + hd];
+      if constexpr (sizeof(T) == 2) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)__builtin_bit_cast(uint16_t, val[2 * e]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, val[2 * e + 1]) << 16);
+        *reinterpret_cast<u32x4*>(dst) = w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dst[k] = val[k];
       }
     }
+    return;
   }
-  // V: per (KV head, dim) the block's 8 slots are 8 contiguous elements
   for (int32_t hd = lane; hd < g.hkv * D; hd += 64) {
     const int32_t h = hd / D, d = hd % D;
     const int64_t base = region_offset(g, a.block_table, s, h, 8 * kb);
