@@ -202,14 +202,18 @@ def _host_walk(sched, T, Nk, L, W, start, bm, bn):
 def test_kernel_walk_is_the_oracle_plan(sched):
     # the attention kernels walk exactly the exported plan: every candidate tile
     # holds a visible pair and gets the oracle's kind (queries reaching far into
-    # a long prefix included, where prefix tiles past the queries must not be walked)
+    # a long prefix included, where prefix tiles past the queries must not be walked).
+    # (64, 128) is the backward's dS tiling: a kept dS tile sits at its key tile's
+    # position in the 64-query block's walk, so the walk must be exactly the tiles
+    # with a visible pair there too
     sched.ps_host_walk.restype = ctypes.c_int
     sched.ps_host_walk.argtypes = sched.ps_host_plan.argtypes
     cases = [(8192, 8292, 100, 2048, 98304, 128, 64), (300, 300, 250, 40, 250, 128, 64),
-             (200, 200, 200, 7, 200, 64, 64), (1000, 1000, 700, 100, 700, 128, 64)]
+             (200, 200, 200, 7, 200, 64, 64), (1000, 1000, 700, 100, 700, 128, 64),
+             (8192, 8292, 100, 2048, 98304, 64, 128), (1000, 1000, 700, 100, 700, 64, 128)]
     rs = np.random.default_rng(1)
     for _ in range(300):
-        bm, bn = [(128, 64), (64, 64), (4, 4), (2, 3), (16, 8)][rs.integers(5)]
+        bm, bn = [(128, 64), (64, 64), (4, 4), (2, 3), (16, 8), (64, 128)][rs.integers(6)]
         L = int(rs.integers(0, 300))
         chunk = int(rs.integers(1, 200))
         nk = L + chunk
