@@ -24,9 +24,11 @@
 //      lane owns one key and the S / dS registers are directly the B operands of
 //      dV^T += dO^T P and dK^T += Q''^T dS, whose A operands (dO^T, Q''^T in the
 //      matching query order) come from the row-major tiles by transposing LDS
-//      reads.  No atomics: every dk / dv row has one writer.
-//   4. dq kernel: the forward's work decomposition and key-tile schedule:
-//      S^T = K' Q''^T, dP^T = V dO^T, dS^T, then dQ^T += K'^T dS^T.
+//      reads.  No atomics: every dk / dv row has one writer.  With room in the
+//      workspace it also stores each block's dS^T tile for step 4.
+//   4. dq kernel, on the forward's key-tile schedule: from the kept dS^T tiles,
+//      dQ^T += K'^T dS^T (one product); without them it forms S^T = K' Q''^T,
+//      dP^T = V dO^T and dS^T again first.
 // All arithmetic on MFMA is bf16 x bf16 -> fp32; P and dS are rounded to bf16
 // as MFMA operands.  The fp32 kernels at the end are the debug path (plain
 // loops, one thread per query or key row).
