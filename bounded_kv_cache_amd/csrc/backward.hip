@@ -341,7 +341,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   int64_t keep_at = -1;
   uint16_t* stg = st_lds + wave * 32 * kDsQueries;
   auto stage = [&](int r, int c) { return r * kDsQueries + ((c ^ (r & 7)) * 8); };
-  uint16_t* ds = static_cast<uint16_t*>(a.ds) + (32 * wave + lane / 8) * kDsQueries + (lane % 8) * 8;
+  uint16_t* ds = kKeepDs ? static_cast<uint16_t*>(a.ds) + (32 * wave + lane / 8) * kDsQueries + (lane % 8) * 8 : nullptr;
   bf16x8 kept[4];
   auto read_kept = [&]() {
 #pragma unroll
