@@ -467,3 +467,29 @@ def test_noalloc_step_rejects_what_exceeds_its_static_scratch(lib):
     bad, _ = _descs(hq=15)
     assert lib.ps_decode_step_noalloc(ctypes.byref(bad), ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
                                       FAKE, FAKE, n, splits, None) == 1
+
+
+def test_backward_ds_workspace_is_the_longest_block_walk(lib, sched):
+    # the kept-dS room: one 128-key x 64-query bf16 tile (16 KB) per query head,
+    # 64-query block and slot, the slots being the longest walk of 128-key tiles
+    # over a 64-query block (the host build of the same scheduling functions)
+    sched.ps_host_walk.restype = ctypes.c_int
+    sched.ps_host_walk.argtypes = sched.ps_host_plan.argtypes
+    f = lib.ps_prefill_backward_ds_workspace_size
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32]
+    for hq, hkv, B, T, nk, L, W, ks in [(28, 4, 8, 8192, 8292, 100, 2048, 98304), (16, 2, 2, 300, 420, 20, 64, 500),
+                                        (8, 2, 1, 257, 257, 0, 1 << 30, 0), (16, 2, 1, 190, 337, 37, 130, 37)]:
+        a, _ = _descs(hq=hq, hkv=hkv)
+        walk = _host_walk(sched, T, nk, L, W, ks, 64, 128)
+        per_block = {}
+        for qb, _kt, _kind in walk:
+            per_block[qb] = per_block.get(qb, 0) + 1
+        slots = max(per_block.values())
+        nqb = (T + 63) // 64
+        assert f(ctypes.byref(a), W, L, ks, B, T, nk) == B * hq * nqb * slots * 16384, (T, nk, L, W)
+    a32, _ = _descs(dtype=1)
+    assert f(ctypes.byref(a32), 64, 20, 500, 2, 300, 420) == 0          # fp32: the dq pass recomputes
+    a, _ = _descs()
+    assert f(ctypes.byref(a), 0, 20, 500, 2, 300, 420) == 0             # invalid window
