@@ -649,7 +649,7 @@ def run_cpu_baseline(args):
     import concurrent.futures
     import multiprocessing
     host = len(os.sched_getaffinity(0))
-    cores = min(host, 16)   # a GPU machine's CPU share is 16 cores, whatever the host shows
+    cores = min(host, 16)   # at most 16 worker processes, one per core of the host share that serves one GPU
     reps = 2
     jobs = [(i, args.position, 100, args.window, reps) for i in range(cores)]
     ctx = multiprocessing.get_context("spawn")
